@@ -1,0 +1,255 @@
+/*
+ * mla.h — C ABI of the INT2 rotated-latent MLA decode library (libmla.so,
+ * AMD Instinct MI355X / gfx950).
+ *
+ * What the library computes comes from three pages:
+ *  [OSCAR-MLA]  OSCAR issue #10 "MLA model support (GLM-5.1 / DeepSeek-style)",
+ *               maintainer reply, part "How the rotation adapts to the latent":
+ *               one rotation per MLA layer fitted on the shared latent c_kv
+ *               (eigh of c_kv^T c_kv over calibration tokens, eigenvectors by
+ *               ascending eigenvalue), clip thresholds fitted on the rotated
+ *               latent, the cache holds the rotated INT2 latent, and the
+ *               kv_b_proj up-projection runs on the dequantised latent.
+ *  [SHARD-MLA]  shard PR #5 "GLM-5.2 speculative drafting ... + opt-in
+ *               MLA-latent KV cache", TL;DR item 2: DeepSeek "absorb" — cache
+ *               the latent plus one shared rope key, attend in latent space.
+ *  [LLMH-SIZE]  llm-helper PR #64 "hf: size GLM-5.3-Flash's KV cache from its
+ *               latent layers only", PR description: a latent layer stores
+ *               kv_lora_rank + qk_rope_head_dim (+ index_head_dim) per token.
+ *
+ * Conventions for every call
+ *  - Pointers marked "device" are device memory of the current HIP device;
+ *    "host" pointers are ordinary host memory.  The caller owns every buffer.
+ *    append and decode allocate no device memory.
+ *  - bf16 and fp16 values travel as uint16_t bit patterns.
+ *  - Arguments are checked on the host before anything is launched; on
+ *    failure the call returns a non-zero status, writes nothing and
+ *    mla_last_error() describes the problem.
+ *  - Calls marked "asynchronous" enqueue work on `stream` (a hipStream_t;
+ *    NULL = the legacy default stream) and return; a device-side fault shows
+ *    up as MLA_ERR_HIP on a later call or at the caller's synchronisation.
+ *  - No C++ exception crosses this interface.  Calls are not re-entrant on
+ *    one stream from several host threads.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,  /* bad pointer, size, shape or dims */
+  MLA_ERR_UNSUPPORTED = 2,  /* valid, but no kernel for this shape */
+  MLA_ERR_WORKSPACE = 3,    /* workspace too small */
+  MLA_ERR_NUMERIC = 4,      /* non-finite input or solver failure */
+  MLA_ERR_HIP = 5           /* a HIP runtime call failed */
+} mla_status;
+
+typedef enum mla_dtype { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype;
+
+/* Shapes of one MLA layer.  Requirements checked by every call:
+ * kv_lora_rank (r) > 0, r % group_size == 0, r % 16 == 0, group_size in
+ * {16, 32}; 0 < qk_rope_head_dim (d_r) <= 256 and even; qk_nope_head_dim
+ * (d_n), v_head_dim (d_v) in 1..1024; num_heads (H) >= 1;
+ * index_head_dim (d_idx) >= 0 (0 = no indexer key). */
+typedef struct mla_dims {
+  int32_t kv_lora_rank;
+  int32_t qk_rope_head_dim;
+  int32_t qk_nope_head_dim;
+  int32_t v_head_dim;
+  int32_t num_heads;
+  int32_t group_size;
+  int32_t index_head_dim;
+} mla_dims;
+
+/* The INT2 latent cache: structure-of-arrays over token slots
+ * [LLMH-SIZE: per token, the latent plus the rotary key (plus the indexer
+ * key)].  Slot s holds
+ *   codes[s*r/4 .. +r/4)        2-bit codes; channel 4k+i at bits 2i..2i+1 of
+ *                               byte k (channels of the rotated latent)
+ *   scale_zero[s*(r/G)*2 ..]    per group g: [2g] = scale, [2g+1] = zero, fp16
+ *   k_rope[s*d_r ..]            shared rope key, bf16, stored unquantised
+ *   idx_key[s*d_idx ..]         indexer key, bf16 (NULL when d_idx == 0)
+ * i.e. r/4 + 4r/G + 2d_r (+ 2d_idx) bytes per token, no padding.
+ * Dequantised value: z_hat = zero + scale * code.  All pointers device. */
+typedef struct mla_cache {
+  uint8_t *codes;
+  uint16_t *scale_zero;
+  uint16_t *k_rope;
+  uint16_t *idx_key;
+  int64_t capacity; /* number of slots */
+} mla_cache;
+
+/* ------------------------------------------------------------------------
+ * mla_calibrate_rotation — per-layer latent rotation  [OSCAR-MLA]
+ *
+ * Sigma = c^T c / n_cal over the calibration latents (fp64, no centring),
+ * symmetric eigendecomposition in fp64, eigenvectors ordered by ascending
+ * eigenvalue, each eigenvector's largest-magnitude entry made positive (ties:
+ * lowest row).  The covariance is formed on the GPU; the r x r fp64
+ * eigensolver (Householder tridiagonalisation + implicit symmetric QR) runs
+ * on the host inside the library.
+ *   c_cal    device [n_cal][r], dtype bf16 or fp32, row-major
+ *   R_out    device [r][r] fp32 row-major: R_out[i*r + j] = component i of
+ *            the eigenvector of the j-th smallest eigenvalue
+ *   eig_out  host [r] fp64 eigenvalues of Sigma, ascending (may be NULL)
+ * Synchronous: returns after R_out is written.
+ * Errors: INVALID_ARG (n_cal < 1, NULL pointers, dims), NUMERIC (non-finite
+ * covariance or no convergence), HIP.
+ * ---------------------------------------------------------------------- */
+mla_status mla_calibrate_rotation(const mla_dims *dims, const void *c_cal,
+                                  mla_dtype dtype, int64_t n_cal, float *R_out,
+                                  double *eig_out, void *stream);
+
+/* ------------------------------------------------------------------------
+ * mla_prepare_rotation — the rotation as applied: R_apply = bf16(R)
+ *
+ * Writes R_apply_t[j*r + i] = bf16_round_nearest_even(R[i*r + j]) (the
+ * transpose, so row j holds eigenvector j).  Every consumer (append, clip
+ * fit, weight folding) uses this one matrix.
+ *   R          device [r][r] fp32 (as written by mla_calibrate_rotation)
+ *   R_apply_t  device [r][r] bf16
+ * Asynchronous.
+ * ---------------------------------------------------------------------- */
+mla_status mla_prepare_rotation(const mla_dims *dims, const float *R,
+                                uint16_t *R_apply_t, void *stream);
+
+/* ------------------------------------------------------------------------
+ * mla_fit_clip — per-group clip ratios on the rotated latent  [OSCAR-MLA]
+ *
+ * For each group g and each ratio a in alpha_grid: rotate every calibration
+ * latent with R_apply (z = c R_apply, rounded to fp32), quantise group g with
+ * thresholds mid -+ a*half of each token's group range (the append
+ * quantiser), and sum (z - z_hat)^2 over tokens and channels in fp64.
+ * alpha_out[g] = the ratio with the smallest sum; exact ties -> larger ratio.
+ *   c_cal       device [n_cal][r] bf16 or fp32
+ *   R_apply_t   device [r][r] bf16 (mla_prepare_rotation)
+ *   alpha_grid  host [n_grid] fp32, each in (0, 1]; 1 <= n_grid <= 64
+ *   alpha_out   device [r/G] fp32
+ *   sse_out     host [r/G][n_grid] fp64 (may be NULL)
+ * Synchronous.
+ * ---------------------------------------------------------------------- */
+mla_status mla_fit_clip(const mla_dims *dims, const void *c_cal,
+                        mla_dtype dtype, int64_t n_cal,
+                        const uint16_t *R_apply_t, const float *alpha_grid,
+                        int32_t n_grid, float *alpha_out, double *sse_out,
+                        void *stream);
+
+/* ------------------------------------------------------------------------
+ * mla_fold_absorb_weights — fold the un-rotation into kv_b_proj
+ *
+ * The cache holds z = c R_apply; attention needs c_hat = R_apply z_hat
+ * [OSCAR-MLA: up-projection on the dequantised latent].  Folding
+ * W~[h] = W[h] R_apply once per layer lets decode work on z_hat directly:
+ *   w_uk_f[h][a][j] = sum_i w_uk[h][a][i] R_apply[i][j]   (fp32 sum -> fp16)
+ *   w_uv_f[h][v][j] = sum_i w_uv[h][v][i] R_apply[i][j]
+ *   w_uk   device [H][d_n][r] bf16 (the K half of kv_b_proj per head)
+ *   w_uv   device [H][d_v][r] bf16 (the V half)
+ *   w_uk_f device [H][d_n][r] fp16;  w_uv_f device [H][d_v][r] fp16
+ * Asynchronous.
+ * ---------------------------------------------------------------------- */
+mla_status mla_fold_absorb_weights(const mla_dims *dims, const uint16_t *w_uk,
+                                   const uint16_t *w_uv,
+                                   const uint16_t *R_apply_t, uint16_t *w_uk_f,
+                                   uint16_t *w_uv_f, void *stream);
+
+/* ------------------------------------------------------------------------
+ * mla_append_quant — quantise-on-append  [OSCAR-MLA; SHARD-MLA]
+ *
+ * For each token i < n with 0 <= slot_mapping[i] < capacity (other slots are
+ * skipped): z = latent[i] R_apply (fp32 accumulation), then per group of G
+ * channels, in fp32 without fused multiply-add:
+ *   mid = 0.5(mx+mn); half = 0.5(mx-mn); lo = mid - a*half; hi = mid + a*half
+ *   scale = fp16((hi-lo)/3); zero = fp16(lo)
+ *   code = min(3, max(0, rint((z - zero)/scale)))   (0 when scale == 0)
+ * and write codes, (scale, zero), k_rope[i] and idx_key[i] to the slot.
+ *   latent        device [n][r] bf16 or fp32
+ *   k_rope        device [n][d_r] bf16
+ *   idx_key       device [n][d_idx] bf16 (NULL iff d_idx == 0)
+ *   slot_mapping  device [n] int64
+ *   R_apply_t     device [r][r] bf16;  alpha  device [r/G] fp32
+ *   cache         host struct of device pointers
+ * Slots that repeat within one call race.  Asynchronous.
+ * ---------------------------------------------------------------------- */
+mla_status mla_append_quant(const mla_dims *dims, const void *latent,
+                            mla_dtype dtype, const uint16_t *k_rope,
+                            const uint16_t *idx_key,
+                            const int64_t *slot_mapping, int64_t n,
+                            const uint16_t *R_apply_t, const float *alpha,
+                            const mla_cache *cache, void *stream);
+
+/* Bytes of workspace mla_decode_absorbed needs for `batch` sequences of `tq`
+ * queries on the current device (0 for invalid arguments). */
+size_t mla_decode_workspace_size(const mla_dims *dims, int32_t batch,
+                                 int32_t tq);
+
+/* ------------------------------------------------------------------------
+ * mla_decode_absorbed — absorbed MLA decode over the INT2 cache
+ * [SHARD-MLA absorb form; OSCAR-MLA up-projection on z_hat]
+ *
+ * For sequence b, query t, head h, with L = seq_len[b] cache slots
+ * seq_base[b] .. seq_base[b]+L-1 (the tq queries are the last tq positions):
+ *   q~ = w_uk_f[h]^T q_nope[b,t,h]
+ *   s_tau = softmax_scale (q~ . z_hat_tau + q_rope[b,t,h] . k_rope_tau)
+ *   p = softmax over visible tau (causal != 0: tau <= L - tq + t; else all L)
+ *   out[b,t,h] = w_uv_f[h] sum_tau p_tau z_hat_tau
+ *   lse[b,t,h] = log sum_tau exp(s_tau)   (natural log)
+ * Work is split over token chunks (split-K) and merged by log-sum-exp.  A
+ * row with no visible token gets out = 0 and lse = -inf.
+ *   q_nope [B][tq][H][d_n] bf16; q_rope [B][tq][H][d_r] bf16   (device)
+ *   w_uk_f [H][d_n][r] fp16; w_uv_f [H][d_v][r] fp16   (device, folded)
+ *   seq_base [B] int64; seq_len [B] int32   (device)
+ *   workspace  device, >= mla_decode_workspace_size(dims, batch, tq) bytes
+ *   out [B][tq][H][d_v] fp32 (device); lse [B][tq][H] fp32 (device or NULL)
+ * Requirements: 1 <= tq <= 64; batch >= 0 (0 = nothing to do); the caller
+ * keeps seq_base[b] + seq_len[b] <= capacity (not checkable on the host).
+ * Asynchronous; no host synchronisation.
+ * ---------------------------------------------------------------------- */
+mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope,
+                               const uint16_t *q_rope, const uint16_t *w_uk_f,
+                               const uint16_t *w_uv_f, const mla_cache *cache,
+                               const int64_t *seq_base, const int32_t *seq_len,
+                               int32_t batch, int32_t tq, int32_t causal,
+                               float softmax_scale, void *workspace,
+                               size_t workspace_bytes, float *out, float *lse,
+                               void *stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics
+ * ---------------------------------------------------------------------- */
+
+/* Message for the last failed call on this host thread ("" if none). */
+const char *mla_last_error(void);
+const char *mla_status_string(mla_status status);
+int32_t mla_abi_version(void);
+
+/* Decode kernel selection, for tests and measurement: 0 = automatic (MFMA
+ * split-K when H*tq >= 16 and the shape has an MFMA kernel, else the
+ * vector-ALU split-K kernel), 1 = always the vector-ALU kernel, 2 = always
+ * MFMA (MLA_ERR_UNSUPPORTED where no MFMA kernel fits).  Process-wide. */
+mla_status mla_set_decode_variant(int32_t variant);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around
+ * every kernel the library enqueues while enabled.  Names: "append_quant",
+ * "decode_plan", "absorb_q", "splitk_decode", "combine_upproj",
+ * "fold_weights", "prepare_rotation", "covariance", "clip_fit".
+ * mla_timing_query waits for the recorded events and returns the summed
+ * milliseconds and launch count since the last reset.  Process-wide; not
+ * for use while another thread launches. */
+mla_status mla_timing_enable(int32_t enable);
+mla_status mla_timing_reset(void);
+mla_status mla_timing_query(const char *kernel, double *total_ms,
+                            int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,333 @@
+// Quantise-on-append: rotate each incoming latent token by R_apply, clip and
+// INT2-quantise it group by group, pack 2-bit codes with fp16 scale/zero,
+// and copy the bf16 rope key (and indexer key) into its cache slot.
+//
+// [OSCAR issue #10, maintainer reply, "How the rotation adapts to the
+// latent"]: the cache holds the rotated, INT2-quantised latent; low-variance
+// eigen-directions (the first channels of z, ascending order) share groups.
+// [llm-helper PR #64, PR description]: a latent layer stores the latent, the
+// rotary key and (GLM-5.3-Flash) the indexer key per token.
+//
+// Two kernels, chosen by input dtype and shape (never by token count, so one
+// layer always quantises the same way):
+//  * append_mfma_kernel: bf16 latents, r in {128, 256, 384, 512}.  The
+//    rotation z^T = R_apply^T c^T is a bf16 MFMA GEMM (32x32x16, fp32
+//    accumulate) with channels as the M dimension: each lane then holds 16
+//    channels of one token, so a 32-channel group is two lanes (one cross-lane
+//    exchange for min/max) and the 2-bit codes of 4 consecutive channels form
+//    one byte in-lane.  The R_apply^T slice (128 channels x r) stays in LDS;
+//    latents stream from HBM straight into MFMA B operands.
+//  * append_valu_kernel: any other shape and fp32 latents; the dot products
+//    run in fp64 (exact products, fp64 sum) and are rounded once to fp32.
+#include "kernels.hpp"
+
+namespace mla {
+namespace {
+
+// Copy one token's bf16 side key (width values) with the widest aligned moves.
+__device__ __forceinline__ void copy_key(uint16_t *__restrict__ dst, const uint16_t *__restrict__ src,
+                                         int width, int lane, int nlanes) {
+  if ((width & 7) == 0) {
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+    for (int e = lane; e < width / 8; e += nlanes) d4[e] = s4[e];
+  } else {
+    const uint32_t *s1 = reinterpret_cast<const uint32_t *>(src);
+    uint32_t *d1 = reinterpret_cast<uint32_t *>(dst);
+    for (int e = lane; e < width / 2; e += nlanes) d1[e] = s1[e];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ double latent_f64(const T *p, int64_t i);
+template <>
+__device__ __forceinline__ double latent_f64<float>(const float *p, int64_t i) {
+  return static_cast<double>(p[i]);
+}
+template <>
+__device__ __forceinline__ double latent_f64<uint16_t>(const uint16_t *p, int64_t i) {
+  return static_cast<double>(bf16_to_f32(p[i]));
+}
+
+struct AppendParams {
+  const void *latent;
+  const uint16_t *k_rope;
+  const uint16_t *idx_key;
+  const int64_t *slots;
+  int64_t n;
+  const uint16_t *Rt;
+  const float *alpha;
+  mla_cache cache;
+  float *z_out;
+  int r, G, d_r, d_idx;
+};
+
+// One block per token, one thread per output channel (blockDim == r <= 1024).
+template <typename T>
+__global__ __launch_bounds__(1024) void append_valu_kernel(AppendParams p) {
+  extern __shared__ double cs[];
+  const int64_t tok = blockIdx.x;
+  const int j = threadIdx.x;
+  const int r = p.r;
+  const T *lat = static_cast<const T *>(p.latent);
+  int64_t slot = -1;
+  if (p.z_out == nullptr) {
+    slot = p.slots[tok];
+    if (slot < 0 || slot >= p.cache.capacity) return;  // uniform per block
+  }
+  for (int i = j; i < r; i += blockDim.x) cs[i] = latent_f64<T>(lat, tok * r + i);
+  __syncthreads();
+  const uint16_t *row = p.Rt + static_cast<int64_t>(j) * r;
+  double acc = 0.0;
+  for (int i = 0; i < r; i += 8) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(row + i);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc = fma(cs[i + 2 * k], static_cast<double>(bf16_to_f32(static_cast<uint16_t>(ww[k] & 0xffffu))), acc);
+      acc = fma(cs[i + 2 * k + 1], static_cast<double>(bf16_to_f32(static_cast<uint16_t>(ww[k] >> 16))), acc);
+    }
+  }
+  const float z = static_cast<float>(acc);  // one rounding, to nearest even
+  if (p.z_out != nullptr) {
+    p.z_out[tok * r + j] = z;
+    return;
+  }
+  const int G = p.G;
+  float mx = z, mn = z;
+  for (int off = G / 2; off > 0; off >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+    mn = fminf(mn, __shfl_xor(mn, off));
+  }
+  const QuantParams q = quant_params(mx, mn, p.alpha[j / G]);
+  const uint32_t code = quant_code(z, q);
+  const uint32_t c1 = __shfl_down(code, 1), c2 = __shfl_down(code, 2), c3 = __shfl_down(code, 3);
+  if ((j & 3) == 0)
+    p.cache.codes[slot * (r / 4) + j / 4] = static_cast<uint8_t>(code | (c1 << 2) | (c2 << 4) | (c3 << 6));
+  if (j % G == 0) {
+    const uint32_t sz = static_cast<uint32_t>(f16_bits(q.scale)) | (static_cast<uint32_t>(f16_bits(q.zero)) << 16);
+    reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (r / G) + j / G] = sz;
+  }
+  copy_key(p.cache.k_rope + slot * p.d_r, p.k_rope + tok * p.d_r, p.d_r, j, blockDim.x);
+  if (p.d_idx > 0)
+    copy_key(p.cache.idx_key + slot * p.d_idx, p.idx_key + tok * p.d_idx, p.d_idx, j, blockDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path
+// ---------------------------------------------------------------------------
+constexpr int kSlice = 128;       // channels per block (4 M-tiles of 32)
+constexpr int kTokPerWave = 64;   // 2 N-tiles of 32 tokens
+constexpr int kTokPerBlock = 256; // 4 waves
+
+template <int R>
+constexpr int lds_stride() { return R + 8; }  // +16 B per row: rows rotate banks
+
+template <int R, int G, int NACC>
+__global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t rt_s[];
+  constexpr int KS = R / 16;
+  constexpr int NSLICE = R / kSlice;
+  constexpr int LS = lds_stride<R>();
+  const int cs = blockIdx.x % NSLICE;
+  const int tb = blockIdx.x / NSLICE;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, hf = l >> 5, l32 = l & 31;
+
+  // stage R_apply^T rows [cs*128, +128) into LDS (16-byte chunks)
+  {
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.Rt + static_cast<int64_t>(cs) * kSlice * R);
+    constexpr int CPR = R / 8;  // chunks per row
+    for (int e = tid; e < kSlice * CPR; e += 256) {
+      const int row = e / CPR, c = e % CPR;
+      *reinterpret_cast<uint4 *>(rt_s + row * LS + c * 8) = src[row * CPR + c];
+    }
+  }
+  const uint16_t *lat = static_cast<const uint16_t *>(p.latent);
+  int64_t tok[2];
+  bool valid[2];
+  const bf16x8 *brow[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    tok[nt] = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave + nt * 32 + l32;
+    valid[nt] = tok[nt] < p.n;
+    brow[nt] = reinterpret_cast<const bf16x8 *>(lat + (valid[nt] ? tok[nt] : 0) * R);
+  }
+  __syncthreads();
+
+  f32x16 acc[NACC][4][2];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[a][mt][nt] = f32x16{};
+
+  const bf16x8 zero8 = {};
+  bf16x8 bcur[2], bnext[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) bcur[nt] = valid[nt] ? brow[nt][hf] : zero8;
+#pragma unroll 2
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) bnext[nt] = valid[nt] ? brow[nt][2 * (ks + 1) + hf] : zero8;
+    }
+    bf16x8 a[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      a[mt] = *reinterpret_cast<const bf16x8 *>(rt_s + (mt * 32 + l32) * LS + ks * 16 + hf * 8);
+    const int par = ks % NACC;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        acc[par][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], bcur[nt], acc[par][mt][nt], 0, 0, 0);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) bcur[nt] = bnext[nt];
+  }
+
+  // epilogue: lane holds channels 32mt + 8q + 4hf + s (v = 4q + s) of token tok[nt]
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const bool ok = valid[nt];
+    int64_t slot = -1;
+    if (ok && p.z_out == nullptr) slot = p.slots[tok[nt]];
+    const bool write = ok && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 z = acc[0][mt][nt];
+#pragma unroll
+      for (int a = 1; a < NACC; ++a) z += acc[a][mt][nt];
+      const int ch0 = cs * kSlice + mt * 32;  // first channel of this M-tile
+      if (p.z_out != nullptr) {
+        if (write) {
+          float *dst = p.z_out + tok[nt] * R + ch0 + 4 * hf;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4 *>(dst + 8 * q) = f32x4{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+        }
+        continue;
+      }
+      // group statistics (exchange with the partner lane l ^ 32, same token)
+      constexpr int NGT = 32 / G;  // groups per M-tile: 1 (G=32) or 2 (G=16)
+      constexpr int VPG = 16 / NGT;  // values per lane per group
+      QuantParams qp[NGT];
+#pragma unroll
+      for (int g = 0; g < NGT; ++g) {
+        float mx = z[g * VPG], mn = z[g * VPG];
+#pragma unroll
+        for (int v = 1; v < VPG; ++v) {
+          mx = fmaxf(mx, z[g * VPG + v]);
+          mn = fminf(mn, z[g * VPG + v]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mn = fminf(mn, __shfl_xor(mn, 32));
+        qp[g] = quant_params(mx, mn, p.alpha[ch0 / G + g]);
+      }
+      uint32_t dword = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t byte = 0;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) byte |= quant_code(z[4 * q + s], qp[(4 * q) / VPG]) << (2 * s);
+        dword |= byte << (8 * q);
+      }
+      // lane hf=0 holds bytes 0,2,4,6 of the tile's 8 code bytes, hf=1 holds 1,3,5,7
+      const uint32_t partner = __shfl_xor(dword, 32);
+      const uint32_t packed = __builtin_amdgcn_perm(partner, dword, hf ? 0x03070206u : 0x05010400u);
+      if (write) {
+        reinterpret_cast<uint32_t *>(p.cache.codes + slot * (R / 4) + ch0 / 4)[hf] = packed;
+        if (NGT == 1) {
+          if (hf == 0) {
+            const uint32_t sz = static_cast<uint32_t>(f16_bits(qp[0].scale)) |
+                                (static_cast<uint32_t>(f16_bits(qp[0].zero)) << 16);
+            reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G] = sz;
+          }
+        } else {
+          const QuantParams &qh = qp[hf & (NGT - 1)];
+          const uint32_t sz = static_cast<uint32_t>(f16_bits(qh.scale)) |
+                              (static_cast<uint32_t>(f16_bits(qh.zero)) << 16);
+          reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G + hf] = sz;
+        }
+      }
+    }
+    // side keys: the first channel slice copies them, one wave per token row
+    if (cs == 0 && p.z_out == nullptr) {
+      // each lane of the wave handles tokens of its own 64-token range in turn
+      for (int t = 0; t < 32; ++t) {
+        const int64_t tk = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave + nt * 32 + t;
+        if (tk >= p.n) break;
+        const int64_t sl = p.slots[tk];
+        if (sl < 0 || sl >= p.cache.capacity) continue;
+        copy_key(p.cache.k_rope + sl * p.d_r, p.k_rope + tk * p.d_r, p.d_r, l, 64);
+        if (p.d_idx > 0) copy_key(p.cache.idx_key + sl * p.d_idx, p.idx_key + tk * p.d_idx, p.d_idx, l, 64);
+      }
+    }
+  }
+}
+
+template <int R, int G>
+hipError_t launch_mfma_rg(const AppendParams &p, hipStream_t s) {
+  constexpr int NACC = 2;
+  const size_t lds = static_cast<size_t>(kSlice) * lds_stride<R>() * sizeof(uint16_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&append_mfma_kernel<R, G, NACC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t blocks = ((p.n + kTokPerBlock - 1) / kTokPerBlock) * (R / kSlice);
+  append_mfma_kernel<R, G, NACC><<<static_cast<unsigned>(blocks), 256, lds, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_mfma_r(const AppendParams &p, hipStream_t s) {
+  return p.G == 32 ? launch_mfma_rg<R, 32>(p, s) : launch_mfma_rg<R, 16>(p, s);
+}
+
+}  // namespace
+
+bool append_uses_mfma(const mla_dims &d, mla_dtype dt) {
+  const int r = d.kv_lora_rank;
+  return dt == MLA_DTYPE_BF16 && (r == 128 || r == 256 || r == 384 || r == 512);
+}
+
+hipError_t launch_append(const mla_dims &d, const void *latent, mla_dtype dt, const uint16_t *k_rope,
+                         const uint16_t *idx_key, const int64_t *slots, int64_t n, const uint16_t *Rt,
+                         const float *alpha, const mla_cache &cache, float *z_out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  TimedLaunch tl("append_quant", s);
+  AppendParams p;
+  p.latent = latent;
+  p.k_rope = k_rope;
+  p.idx_key = idx_key;
+  p.slots = slots;
+  p.n = n;
+  p.Rt = Rt;
+  p.alpha = alpha;
+  p.cache = cache;
+  p.z_out = z_out;
+  p.r = d.kv_lora_rank;
+  p.G = d.group_size;
+  p.d_r = d.qk_rope_head_dim;
+  p.d_idx = d.index_head_dim;
+  if (append_uses_mfma(d, dt)) {
+    switch (p.r) {
+      case 128: return launch_mfma_r<128>(p, s);
+      case 256: return launch_mfma_r<256>(p, s);
+      case 384: return launch_mfma_r<384>(p, s);
+      default: return launch_mfma_r<512>(p, s);
+    }
+  }
+  const size_t lds = static_cast<size_t>(p.r) * sizeof(double);
+  if (dt == MLA_DTYPE_FP32)
+    append_valu_kernel<float><<<static_cast<unsigned>(n), p.r, lds, s>>>(p);
+  else
+    append_valu_kernel<uint16_t><<<static_cast<unsigned>(n), p.r, lds, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

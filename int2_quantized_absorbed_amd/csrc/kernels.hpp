@@ -1,0 +1,69 @@
+// Kernel launchers shared between the translation units of libmla.
+// Every launcher enqueues on `stream`, checks nothing it can assume from the
+// caller (api.hip validates first) and returns the launch error.
+#pragma once
+
+#include "common.hpp"
+
+namespace mla {
+
+// One split-K work item: tokens [t0, t1) of sequence b.
+struct WorkItem {
+  int32_t b, t0, t1, pad;
+};
+
+// ---- calibration (calib.hip) ----
+hipError_t launch_covariance(const void *c, mla_dtype dt, int64_t n, int r,
+                             double *sigma, hipStream_t s);
+hipError_t launch_prepare_rotation(const float *R, int r, uint16_t *Rt,
+                                   hipStream_t s);
+hipError_t launch_group_sse(const float *z, int64_t n, int r, int G,
+                            const float *grid, int n_grid, double *sse,
+                            float *alpha_out, hipStream_t s);
+hipError_t launch_fold(const uint16_t *w, int rows, int r, const uint16_t *Rt,
+                       uint16_t *wf, hipStream_t s);
+
+// ---- append (append.hip) ----
+// z_out != nullptr: write the fp32 rotated latent [n][r] instead of the cache
+// (same arithmetic as the cache path; used by the clip fit).
+bool append_uses_mfma(const mla_dims &d, mla_dtype dt);
+hipError_t launch_append(const mla_dims &d, const void *latent, mla_dtype dt,
+                         const uint16_t *k_rope, const uint16_t *idx_key,
+                         const int64_t *slots, int64_t n, const uint16_t *Rt,
+                         const float *alpha, const mla_cache &cache,
+                         float *z_out, hipStream_t s);
+
+// ---- decode (decode.hip, decode_mfma.hip) ----
+struct DecodeArgs {
+  mla_dims d;
+  const uint16_t *q_nope, *q_rope, *w_uk_f, *w_uv_f;
+  mla_cache cache;
+  const int64_t *seq_base;
+  const int32_t *seq_len;
+  int32_t B, Tq, causal;
+  float scale_log2;  // softmax_scale * log2(e)
+  float *out, *lse;
+  // workspace carve-up
+  WorkItem *items;
+  int32_t *item_begin;  // [B + 1]
+  int32_t *meta;        // [0] = n_items, [1] = chunk tokens
+  void *qbuf;           // absorbed queries
+  float *part_o;        // [max_items][M][r]
+  float *part_ml;       // [max_items][M][2]  (m in log2 units, l)
+  int32_t max_items;
+  int32_t target_items;
+  int32_t tile;
+};
+
+hipError_t launch_plan(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_absorb_f32(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_combine_upproj(const DecodeArgs &a, hipStream_t s);
+
+// MFMA split-K path (r = 512, d_r = 64): supported() says whether it applies.
+bool mfma_decode_supported(const mla_dims &d, int rows);
+int mfma_row_block();
+hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace mla

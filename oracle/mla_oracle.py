@@ -141,26 +141,21 @@ def rotate(c, r_apply) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-def quantize_groups(z32, alpha, group):
-    """Clip + INT2-quantise rotated latents group by group, in IEEE fp32.
+def group_params(z32, alpha, group):
+    """Per-(token, group) clip thresholds and fp16 side information, fp32.
 
     z32:   [n, r] float32 rotated latents.
     alpha: [r/G] clip ratios, one per group (Reading: the fitted clip
            threshold is a ratio of each token's group half-range around its
            mid-point; alpha = 1 is plain asymmetric min-max INT2).
-    Returns codes [n, r] uint8 in 0..3, scale_h and zero_h [n, r/G] float16,
-    and u [n, r] float32 (the pre-rounding code value, for boundary bands).
-
     Per (token, group), in this order, each step rounded to fp32:
       mx, mn = max, min of the group
       mid = 0.5 * (mx + mn);  half = 0.5 * (mx - mn)
       lo = mid - (alpha * half);  hi = mid + (alpha * half)
       scale32 = (hi - lo) / 3
       scale_h = fp16(scale32);  zero_h = fp16(lo)
-      u = (z - zero_h) / scale_h   (u = 0 when scale_h == 0)
-      code = min(3, max(0, rint(u)))   rint: ties to even
-    Reading: the stored fp16 scale and zero are the ones used to quantise, so
-    the stored side information and the codes agree.
+    Returns scale_h, zero_h (float16 [n, r/G]) and scale32, lo (float32, the
+    values before the fp16 rounding).
     """
     z32 = np.asarray(z32, dtype=F32)
     n, r = z32.shape
@@ -177,17 +172,42 @@ def quantize_groups(z32, alpha, group):
     lo = mid - ah
     hi = mid + ah
     scale32 = (hi - lo) / F32(3.0)
-    scale_h = fp16_round(scale32)
-    zero_h = fp16_round(lo)
-    s = scale_h.astype(F32)[:, :, None]
-    z0 = zero_h.astype(F32)[:, :, None]
+    return fp16_round(scale32), fp16_round(lo), scale32, lo
+
+
+def codes_from_params(z32, scale_h, zero_h, group):
+    """INT2 codes of each channel from its group's fp16 scale and zero, fp32.
+
+      u = (z - zero_h) / scale_h   (u = 0 when scale_h == 0)
+      code = min(3, max(0, rint(u)))   rint: ties to even; NaN -> 0
+    Reading: the stored fp16 scale and zero are the ones used to quantise, so
+    the stored side information and the codes agree.
+    Returns codes [n, r] uint8 and u [n, r] float32.
+    """
+    z32 = np.asarray(z32, dtype=F32)
+    n, r = z32.shape
+    ng = r // group
+    zg = z32.reshape(n, ng, group)
+    s = np.asarray(scale_h).astype(F32)[:, :, None]
+    z0 = np.asarray(zero_h).astype(F32)[:, :, None]
     with np.errstate(divide="ignore", invalid="ignore"):
         u = (zg - z0) / s
     u = np.where(s == 0, F32(0.0), u).astype(F32)
     code = np.clip(np.rint(u), F32(0.0), F32(3.0))
     code = np.where(np.isnan(code), F32(0.0), code)
-    return (code.astype(np.uint8).reshape(n, r), scale_h, zero_h,
-            u.reshape(n, r))
+    return code.astype(np.uint8).reshape(n, r), u.reshape(n, r)
+
+
+def quantize_groups(z32, alpha, group):
+    """Clip + INT2-quantise rotated latents group by group, in IEEE fp32.
+
+    ``group_params`` then ``codes_from_params``.  Returns codes [n, r] uint8
+    in 0..3, scale_h and zero_h [n, r/G] float16, and u [n, r] float32 (the
+    pre-rounding code value, for boundary bands).
+    """
+    scale_h, zero_h, _, _ = group_params(z32, alpha, group)
+    codes, u = codes_from_params(z32, scale_h, zero_h, group)
+    return codes, scale_h, zero_h, u
 
 
 def pack_codes(codes) -> np.ndarray:
@@ -223,13 +243,16 @@ def quantize_cache(c, r_apply, alpha, group):
     """Append path for a block of tokens: rotate, clip, quantise, pack.
 
     Returns a dict with packed codes [n, r/4] uint8, scale_zero [n, r/G, 2]
-    float16 (scale first), unpacked codes, u and the fp32 rotated latent.
+    float16 (scale first), unpacked codes, u, the fp32 rotated latent and the
+    pre-rounding scale32 and lo.
     """
     z32 = rotate(c, r_apply)
-    codes, scale_h, zero_h, u = quantize_groups(z32, alpha, group)
+    scale_h, zero_h, scale32, lo = group_params(z32, alpha, group)
+    codes, u = codes_from_params(z32, scale_h, zero_h, group)
     sz = np.stack([scale_h, zero_h], axis=-1)
     return dict(packed=pack_codes(codes), scale_zero=sz, codes=codes, u=u,
-                z32=z32, scale_h=scale_h, zero_h=zero_h)
+                z32=z32, scale_h=scale_h, zero_h=zero_h, scale32=scale32,
+                lo=lo)
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute launched).
+
+The library must load, export every function include/mla.h declares, and
+reject invalid arguments on the host before touching a device.
+"""
+import ctypes
+
+import pytest
+
+import int2_quantized_absorbed_amd as M
+from int2_quantized_absorbed_amd import binding as Bd
+
+DS = M.Dims(512, 64, 128, 128, 128, 32, 0)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.lib()
+    names = M.header_functions()
+    assert "mla_decode_absorbed" in names and "mla_append_quant" in names
+    assert "mla_calibrate_rotation" in names and "mla_fit_clip" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert M.mla_abi_version() == 1
+
+
+def test_status_strings():
+    for st in range(6):
+        assert isinstance(M.mla_status_string(st), str)
+    assert M.mla_status_string(0) == "ok"
+
+
+def _dims(**kw):
+    base = dict(kv_lora_rank=512, qk_rope_head_dim=64, qk_nope_head_dim=128, v_head_dim=128,
+                num_heads=128, group_size=32, index_head_dim=0)
+    base.update(kw)
+    return Bd.mla_dims(*base.values())
+
+
+BAD_DIMS = [
+    dict(kv_lora_rank=0), dict(kv_lora_rank=100), dict(group_size=8), dict(group_size=64),
+    dict(kv_lora_rank=48, group_size=32), dict(qk_rope_head_dim=0), dict(qk_rope_head_dim=3),
+    dict(num_heads=0), dict(index_head_dim=-2), dict(v_head_dim=0),
+]
+
+
+@pytest.mark.parametrize("bad", BAD_DIMS)
+def test_invalid_dims_rejected_everywhere(bad):
+    lib = M.lib()
+    d = _dims(**bad)
+    P = ctypes.c_void_p(16)
+    cache = Bd.mla_cache(16, 16, 16, 0, 10)
+    assert lib.mla_prepare_rotation(ctypes.byref(d), P, P, None) == Bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_quant(ctypes.byref(d), P, 0, P, None, P, 4, P, P, ctypes.byref(cache), None) \
+        == Bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_workspace_size(ctypes.byref(d), 1, 1) == 0
+    assert lib.mla_decode_absorbed(ctypes.byref(d), P, P, P, P, ctypes.byref(cache), P, P, 1, 1, 1, 0.1, P,
+                                   1 << 30, P, P, None) == Bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_calibrate_rotation(ctypes.byref(d), P, 0, 10, P, None, None) == Bd.MLA_ERR_INVALID_ARG
+    assert M.mla_last_error() != ""
+
+
+def test_null_dims():
+    lib = M.lib()
+    assert lib.mla_prepare_rotation(None, None, None, None) == Bd.MLA_ERR_INVALID_ARG
+    assert "NULL" in M.mla_last_error()
+
+
+def test_decode_argument_checks():
+    lib = M.lib()
+    d = _dims()
+    P = ctypes.c_void_p(256)
+    cache = Bd.mla_cache(256, 256, 256, 0, 1000)
+    call = lambda **kw: lib.mla_decode_absorbed(
+        ctypes.byref(d), kw.get("qn", P), P, P, P, ctypes.byref(cache), P, P, kw.get("B", 2), kw.get("tq", 1),
+        kw.get("causal", 1), kw.get("scale", 0.07), kw.get("ws", P), kw.get("wsb", 1 << 40), P, P, None)
+    assert call(tq=0) == Bd.MLA_ERR_INVALID_ARG
+    assert call(tq=65) == Bd.MLA_ERR_INVALID_ARG
+    assert call(causal=2) == Bd.MLA_ERR_INVALID_ARG
+    assert call(B=-1) == Bd.MLA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == Bd.MLA_ERR_INVALID_ARG
+    assert call(qn=ctypes.c_void_p(0)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(qn=ctypes.c_void_p(258)) == Bd.MLA_ERR_INVALID_ARG       # misaligned
+    assert call(wsb=16) == Bd.MLA_ERR_WORKSPACE
+    assert "workspace" in M.mla_last_error()
+    assert call(B=0) == Bd.MLA_OK                                         # nothing to do
+    d2 = _dims(kv_lora_rank=1024)
+    assert lib.mla_decode_absorbed(ctypes.byref(d2), P, P, P, P, ctypes.byref(cache), P, P, 2, 1, 1, 0.07, P,
+                                   1 << 40, P, P, None) == Bd.MLA_ERR_UNSUPPORTED
+
+
+def test_append_argument_checks():
+    lib = M.lib()
+    d = _dims()
+    P = ctypes.c_void_p(256)
+    cache = Bd.mla_cache(256, 256, 256, 0, 1000)
+    call = lambda **kw: lib.mla_append_quant(
+        ctypes.byref(kw.get("d", d)), P, kw.get("dt", 0), P, kw.get("idx", None), P, kw.get("n", 8), P, P,
+        ctypes.byref(kw.get("cache", cache)), None)
+    assert call(n=0) == Bd.MLA_OK
+    assert call(n=-1) == Bd.MLA_ERR_INVALID_ARG
+    assert call(dt=7) == Bd.MLA_ERR_INVALID_ARG
+    assert call(idx=P) == Bd.MLA_ERR_INVALID_ARG          # idx key without index_head_dim
+    d_idx = _dims(index_head_dim=64)
+    assert call(d=d_idx) == Bd.MLA_ERR_INVALID_ARG        # index_head_dim without idx key
+    assert call(cache=Bd.mla_cache(0, 256, 256, 0, 10)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(cache=Bd.mla_cache(256, 256, 256, 0, -1)) == Bd.MLA_ERR_INVALID_ARG
+
+
+def test_calibration_argument_checks():
+    lib = M.lib()
+    d = _dims()
+    P = ctypes.c_void_p(256)
+    assert lib.mla_calibrate_rotation(ctypes.byref(d), P, 0, 0, P, None, None) == Bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_calibrate_rotation(ctypes.byref(d), P, 5, 10, P, None, None) == Bd.MLA_ERR_INVALID_ARG
+    grid = (ctypes.c_float * 2)(1.0, 1.5)
+    assert lib.mla_fit_clip(ctypes.byref(d), P, 0, 10, P, grid, 2, P, None, None) == Bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_fit_clip(ctypes.byref(d), P, 0, 10, P, grid, 0, P, None, None) == Bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_set_decode_variant(3) == Bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_set_decode_variant(0) == Bd.MLA_OK
+
+
+def test_workspace_size_is_monotone():
+    s1 = M.mla_decode_workspace_size(DS, 8, 1)
+    s2 = M.mla_decode_workspace_size(DS, 16, 1)
+    s3 = M.mla_decode_workspace_size(DS, 8, 8)
+    assert 0 < s1 < s2 and s1 < s3
+    assert M.mla_decode_workspace_size(DS, 8, 0) == 0

@@ -1,0 +1,261 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle, on the
+same seeded inputs, at sizes the oracle finishes in seconds (several tiles
+plus ragged tails).  Tolerances are the ones stated in tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import int2_quantized_absorbed_amd as M
+from oracle import mla_oracle as O
+from workloads import synth as S
+from tests import gpu_cases as C
+from tests.parity import LSE_TOL, OUT_RTOL, compare_append, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    torch.cuda.set_device(0)
+    M.mla_set_decode_variant(0)
+    yield
+    torch.cuda.synchronize()
+    M.mla_set_decode_variant(0)
+
+
+# ---------------------------------------------------------------------------
+# calibration
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wid", [0, 1])
+def test_calibrate_rotation(wid):
+    w = S.WORKLOADS[wid]
+    C.say(f"calibrate_rotation workload {wid}")
+    st = S.streams(wid)
+    model = S.latent_model(w, st)
+    c = S.calib_latents(w, st, model)
+    R_o, lam_o, _ = O.calibrate_rotation(c)
+    R_g, lam_g = M.mla_calibrate_rotation(C.dims_of(w), C.latent_tensor(c, w.latent_dtype))
+    R_g = R_g.cpu().numpy()
+    np.testing.assert_allclose(lam_g, lam_o, rtol=1e-9, atol=1e-14)
+    assert np.max(np.abs(R_g - R_o)) <= 2e-6
+    R64 = R_g.astype(np.float64)
+    assert np.max(np.abs(R64.T @ R64 - np.eye(w.kv_lora_rank))) <= 1e-6
+
+
+def test_prepare_rotation_bit_exact():
+    w = S.WORKLOADS[1]
+    rng = np.random.default_rng(3)
+    R = rng.standard_normal((w.kv_lora_rank, w.kv_lora_rank)).astype(np.float32)
+    Rt = M.mla_prepare_rotation(C.dims_of(w), C.t_f32(R)).float().cpu().numpy()
+    want = O.rotation_apply(R).T
+    assert np.array_equal(Rt.view(np.uint32), np.ascontiguousarray(want).view(np.uint32))
+
+
+@pytest.mark.parametrize("wid", [0, 1])
+def test_fit_clip(wid):
+    w = S.WORKLOADS[wid]
+    C.say(f"fit_clip workload {wid}")
+    layer = C.Layer(w)
+    grid = list(O.DEFAULT_ALPHA_GRID)
+    a_o, sse_o = O.fit_clip(layer.c_cal, layer.R, w.group_size, grid)
+    a_g, sse_g = M.mla_fit_clip(layer.dims, C.latent_tensor(layer.c_cal, w.latent_dtype), layer.Rt_d, grid)
+    a_g = a_g.cpu().numpy()
+    np.testing.assert_allclose(sse_g, sse_o, rtol=1e-5, atol=1e-12)
+    for g in range(len(a_o)):
+        if a_g[g] != a_o[g]:
+            best = np.sort(sse_o[g])[:2]
+            assert (best[1] - best[0]) <= 1e-6 * best[0], (g, a_g[g], a_o[g], best)
+
+
+def test_fold_weights():
+    w = S.WORKLOADS[1].with_(num_heads=8)
+    layer = C.Layer(w)
+    for got, wt in ((layer.w_uk_f, layer.w_uk), (layer.w_uv_f, layer.w_uv)):
+        ref = O.fold_weights(wt, layer.R_apply)
+        g = got.float().cpu().numpy().astype(np.float64)
+        # fp32 accumulation then one fp16 rounding: the accumulation error can
+        # move a value across an fp16 rounding midpoint, so allow one fp16 ulp
+        tol = np.abs(np.spacing(ref.astype(np.float16))).astype(np.float64) * 1.0 + 1e-6 * np.abs(ref) + 1e-8
+        assert np.all(np.abs(g - ref) <= tol)
+
+
+# ---------------------------------------------------------------------------
+# quantise-on-append
+# ---------------------------------------------------------------------------
+
+APPEND_CASES = [
+    ("w0-fp32-valu", 0, dict(), 517),
+    ("w1-bf16-mfma", 1, dict(), 1000),
+    ("w1-bf16-mfma-g16", 1, dict(group_size=16), 333),
+    ("w4-bf16-idx", 4, dict(), 300),
+    ("w1-r256", 1, dict(kv_lora_rank=256), 129),
+    ("w1-r96-valu", 1, dict(kv_lora_rank=96), 70),
+]
+
+
+@pytest.mark.parametrize("name,wid,over,n", APPEND_CASES)
+def test_append_quant(name, wid, over, n):
+    w = S.WORKLOADS[wid].with_(**over)
+    C.say(f"append_quant {name} n={n}")
+    layer = C.Layer(w)
+    rng = np.random.default_rng(7)
+    c = layer.model.sample(rng, n)
+    kr = S.rope_keys(rng, n, w.qk_rope_head_dim)
+    idx = S.rope_keys(rng, n, w.index_head_dim) if w.index_head_dim else None
+    cap = n + 50
+    slots = rng.permutation(cap)[:n].astype(np.int64)
+    slots[::37] = -1                                   # skipped tokens
+    slots[5] = cap + 3                                  # out of range: skipped
+    cache = M.Cache(layer.dims, cap, C.DEV)
+    cache.codes.fill_(0xAB)
+    M.mla_append_quant(layer.dims, C.latent_tensor(c, w.latent_dtype), C.t_bf16(kr),
+                       C.t_bf16(idx) if idx is not None else None, torch.from_numpy(slots).to(C.DEV),
+                       layer.Rt_d, layer.alpha_d, cache)
+    torch.cuda.synchronize()
+    ref = O.quantize_cache(c, layer.R_apply, layer.alpha, w.group_size)
+    ok = (slots >= 0) & (slots < cap)
+    sl = slots[ok]
+    packed = cache.codes.cpu().numpy()[sl]
+    sz = cache.scale_zero.cpu().numpy()[sl]
+    sub = {k: v[ok] for k, v in ref.items()}
+    stats = compare_append(packed, sz, sub, w.group_size)
+    C.say(name, stats)
+    assert stats["violations"] == 0 and stats["sz_violations"] == 0, stats
+    assert np.array_equal(cache.k_rope.float().cpu().numpy()[sl], kr[ok])
+    if idx is not None:
+        assert np.array_equal(cache.idx_key.float().cpu().numpy()[sl], idx[ok])
+    untouched = np.setdiff1d(np.arange(cap), sl)
+    assert np.all(cache.codes.cpu().numpy()[untouched] == 0xAB)
+
+
+def test_append_empty_is_noop():
+    w = S.WORKLOADS[1]
+    layer = C.Layer(w.with_(num_heads=2))
+    cache = M.Cache(layer.dims, 4, C.DEV)
+    M.mla_append_quant(layer.dims, torch.empty((0, 512), dtype=torch.bfloat16, device=C.DEV),
+                       torch.empty((0, 64), dtype=torch.bfloat16, device=C.DEV), None,
+                       torch.empty((0,), dtype=torch.int64, device=C.DEV), layer.Rt_d, layer.alpha_d, cache)
+    torch.cuda.synchronize()
+    assert int(cache.codes.sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# decode over a random cache (decode checked on its own)
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = [
+    # name, workload, overrides, lens, tq, causal, variant
+    ("w0-valu", 0, dict(), [256], 1, True, 0),
+    ("w0-ragged", 0, dict(), [1, 17, 300, 64], 1, True, 0),
+    ("w1-small-auto", 1, dict(), [37, 100, 257], 1, True, 0),
+    ("w1-small-valu", 1, dict(), [37, 100, 257], 1, True, 1),
+    ("w3-tq8-causal", 3, dict(), [40, 9, 129], 8, True, 0),
+    ("w3-tq8-causal-valu", 3, dict(), [40, 9, 129], 8, True, 1),
+    ("w3-tq4-full", 3, dict(num_heads=16), [33, 70], 4, False, 0),
+    ("w4-h64", 4, dict(), [200, 513], 1, True, 0),
+    ("w1-h16", 1, dict(num_heads=16), [300, 31], 1, True, 0),
+    ("w1-g16", 1, dict(group_size=16, num_heads=32), [129], 1, True, 0),
+]
+
+
+def _run_decode(layer, case, tq, causal, scale):
+    d = layer.dims
+    cache = C.upload_cache(d, case)
+    out, lse = M.mla_decode_absorbed(d, C.t_bf16(case["qn"]), C.t_bf16(case["qr"]), layer.w_uk_f,
+                                     layer.w_uv_f, cache, torch.from_numpy(case["base"]).to(C.DEV),
+                                     torch.from_numpy(case["lens"]).to(C.DEV), tq, causal, scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,wid,over,lens,tq,causal,variant", DECODE_CASES)
+def test_decode_random_cache(name, wid, over, lens, tq, causal, variant):
+    w = S.WORKLOADS[wid].with_(**over)
+    C.say(f"decode {name} lens={lens} tq={tq} causal={causal} variant={variant}")
+    layer = C.Layer(w)
+    case = C.random_decode_case(w, lens, tq, seed=11)
+    scale = O.default_softmax_scale(w.qk_nope_head_dim, w.qk_rope_head_dim)
+    M.mla_set_decode_variant(variant)
+    out, lse = _run_decode(layer, case, tq, causal, scale)
+    ref = C.oracle_decode(layer, case, tq, causal, scale)
+    worst, worst_lse = 0.0, 0.0
+    for b, (o_ref, l_ref) in ref.items():
+        fin = np.isfinite(l_ref)
+        assert np.array_equal(np.isfinite(lse[b]), fin), name
+        if (~fin).any():
+            assert np.all(out[b][~fin] == 0)
+        if fin.any():
+            err = row_rel_err(out[b][fin], o_ref[fin])
+            worst = max(worst, float(err.max()))
+            lerr = np.abs(lse[b][fin] - l_ref[fin]) / np.maximum(1, np.abs(l_ref[fin]))
+            worst_lse = max(worst_lse, float(lerr.max()))
+    C.say(name, "worst row rel err", worst, "worst lse err", worst_lse)
+    assert worst <= OUT_RTOL
+    assert worst_lse <= LSE_TOL
+
+
+def test_decode_edge_lengths():
+    """Sequences shorter than the draft window and empty sequences."""
+    w = S.WORKLOADS[3].with_(num_heads=16)
+    layer = C.Layer(w)
+    case = C.random_decode_case(w, [3, 0, 8, 1], 8, seed=5)
+    scale = O.default_softmax_scale(w.qk_nope_head_dim, w.qk_rope_head_dim)
+    out, lse = _run_decode(layer, case, 8, True, scale)
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+    ref = C.oracle_decode(layer, case, 8, True, scale, seqs=[0, 2, 3])
+    for b, (o_ref, l_ref) in ref.items():
+        fin = np.isfinite(l_ref)
+        assert np.array_equal(np.isfinite(lse[b]), fin)
+        assert np.all(out[b][~fin] == 0)
+        if fin.any():
+            assert row_rel_err(out[b][fin], o_ref[fin]).max() <= OUT_RTOL
+
+
+# ---------------------------------------------------------------------------
+# the whole chain on workload 0 (calibrate -> fit -> fold -> append -> decode)
+# ---------------------------------------------------------------------------
+
+def test_end_to_end_workload0():
+    w = S.WORKLOADS[0]
+    C.say("end-to-end workload 0")
+    st = S.streams(0)
+    model = S.latent_model(w, st)
+    c_cal = S.calib_latents(w, st, model)
+    d = C.dims_of(w)
+    # oracle chain
+    R_o, _, _ = O.calibrate_rotation(c_cal)
+    a_o, _ = O.fit_clip(c_cal, R_o, w.group_size)
+    Ra = O.rotation_apply(R_o)
+    w_uk, w_uv = S.weights(w, st)
+    L = w.context
+    lat = model.sample(st["cache"], L)
+    kr = S.rope_keys(st["cache"], L, w.qk_rope_head_dim)
+    qn, qr = S.queries(w, st)
+    ref_q = O.quantize_cache(lat, Ra, a_o, w.group_size)
+    zh = O.dequantize(ref_q["codes"], ref_q["scale_h"], ref_q["zero_h"], w.group_size)
+    scale = O.default_softmax_scale(w.qk_nope_head_dim, w.qk_rope_head_dim)
+    o_ref, l_ref = O.absorbed_attention(qn[0], qr[0], w_uk, w_uv, zh, kr, Ra, scale)
+    # HIP chain
+    cal_d = C.latent_tensor(c_cal, w.latent_dtype)
+    R_g, _ = M.mla_calibrate_rotation(d, cal_d)
+    Rt = M.mla_prepare_rotation(d, R_g)
+    a_g, _ = M.mla_fit_clip(d, cal_d, Rt, list(O.DEFAULT_ALPHA_GRID))
+    uk_f, uv_f = M.mla_fold_absorb_weights(d, C.t_bf16(w_uk), C.t_bf16(w_uv), Rt)
+    cache = M.Cache(d, L, C.DEV)
+    M.mla_append_quant(d, C.latent_tensor(lat, w.latent_dtype), C.t_bf16(kr), None,
+                       torch.arange(L, dtype=torch.int64, device=C.DEV), Rt, a_g, cache)
+    out, lse = M.mla_decode_absorbed(d, C.t_bf16(qn), C.t_bf16(qr), uk_f, uv_f, cache,
+                                     torch.zeros(1, dtype=torch.int64, device=C.DEV),
+                                     torch.full((1,), L, dtype=torch.int32, device=C.DEV), 1, True, scale)
+    torch.cuda.synchronize()
+    a_g_h = a_g.cpu().numpy()
+    _, sse_o = O.fit_clip(c_cal, R_o, w.group_size)
+    for g in np.nonzero(a_g_h != a_o)[0]:      # only near-ties may differ
+        best = np.sort(sse_o[g])[:2]
+        assert best[1] - best[0] <= 1e-6 * best[0]
+    err = row_rel_err(out.cpu().numpy()[0], o_ref)
+    C.say("end-to-end worst row rel err", err.max())
+    assert err.max() <= OUT_RTOL
+    assert np.all(np.abs(lse.cpu().numpy()[0] - l_ref) <= LSE_TOL * np.maximum(1, np.abs(l_ref)))
