@@ -157,6 +157,9 @@ DECODE_CASES = [
     ("w4-h64", 4, dict(), [200, 513], 1, True, 0),
     ("w1-h16", 1, dict(num_heads=16), [300, 31], 1, True, 0),
     ("w1-g16", 1, dict(group_size=16, num_heads=32), [129], 1, True, 0),
+    ("w1-mfma-forced", 1, dict(), [1, 33, 64, 95], 1, True, 2),
+    ("w1-h8-mfma-padrows", 1, dict(num_heads=8), [500], 1, True, 2),
+    ("w2-ragged-long", 2, dict(), [2049, 1500, 31, 4000], 1, True, 0),
 ]
 
 
