@@ -148,11 +148,13 @@ mla_status mla_fit_clip(const mla_dims *dims, const void *c_cal,
  * The cache holds z = c R_apply; attention needs c_hat = R_apply z_hat
  * [OSCAR-MLA: up-projection on the dequantised latent].  Folding
  * W~[h] = W[h] R_apply once per layer lets decode work on z_hat directly:
- *   w_uk_f[h][a][j] = sum_i w_uk[h][a][i] R_apply[i][j]   (fp32 sum -> fp16)
+ *   w_uk_f[h][j][a] = sum_i w_uk[h][a][i] R_apply[i][j]   (fp32 sum -> fp16)
  *   w_uv_f[h][v][j] = sum_i w_uv[h][v][i] R_apply[i][j]
+ * (the K-side fold is stored transposed per head, latent channel-major, so
+ * the absorb kernel reads contiguous runs of the nope dimension)
  *   w_uk   device [H][d_n][r] bf16 (the K half of kv_b_proj per head)
  *   w_uv   device [H][d_v][r] bf16 (the V half)
- *   w_uk_f device [H][d_n][r] fp16;  w_uv_f device [H][d_v][r] fp16
+ *   w_uk_f device [H][r][d_n] fp16;  w_uv_f device [H][d_v][r] fp16
  * Asynchronous.
  * ---------------------------------------------------------------------- */
 mla_status mla_fold_absorb_weights(const mla_dims *dims, const uint16_t *w_uk,
@@ -196,7 +198,7 @@ size_t mla_decode_workspace_size(const mla_dims *dims, int32_t batch,
  *
  * For sequence b, query t, head h, with L = seq_len[b] cache slots
  * seq_base[b] .. seq_base[b]+L-1 (the tq queries are the last tq positions):
- *   q~ = w_uk_f[h]^T q_nope[b,t,h]
+ *   q~[j] = sum_a w_uk_f[h][j][a] q_nope[b,t,h][a]
  *   s_tau = softmax_scale (q~ . z_hat_tau + q_rope[b,t,h] . k_rope_tau)
  *   p = softmax over visible tau (causal != 0: tau <= L - tq + t; else all L)
  *   out[b,t,h] = w_uv_f[h] sum_tau p_tau z_hat_tau
@@ -204,12 +206,13 @@ size_t mla_decode_workspace_size(const mla_dims *dims, int32_t batch,
  * Work is split over token chunks (split-K) and merged by log-sum-exp.  A
  * row with no visible token gets out = 0 and lse = -inf.
  *   q_nope [B][tq][H][d_n] bf16; q_rope [B][tq][H][d_r] bf16   (device)
- *   w_uk_f [H][d_n][r] fp16; w_uv_f [H][d_v][r] fp16   (device, folded)
+ *   w_uk_f [H][r][d_n] fp16; w_uv_f [H][d_v][r] fp16   (device, folded)
  *   seq_base [B] int64; seq_len [B] int32   (device)
  *   workspace  device, >= mla_decode_workspace_size(dims, batch, tq) bytes
  *   out [B][tq][H][d_v] fp32 (device); lse [B][tq][H] fp32 (device or NULL)
- * Requirements: 1 <= tq <= 64; batch >= 0 (0 = nothing to do); the caller
- * keeps seq_base[b] + seq_len[b] <= capacity (not checkable on the host).
+ * Requirements: 1 <= tq <= 64; batch >= 0 (0 = nothing to do);
+ * kv_lora_rank <= 512 (UNSUPPORTED otherwise); the caller keeps
+ * seq_base[b] + seq_len[b] <= capacity (not checkable on the host).
  * Asynchronous; no host synchronisation.
  * ---------------------------------------------------------------------- */
 mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope,
@@ -238,7 +241,7 @@ mla_status mla_set_decode_variant(int32_t variant);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around
  * every kernel the library enqueues while enabled.  Names: "append_quant",
- * "decode_plan", "absorb_q", "splitk_decode", "combine_upproj",
+ * "decode_plan", "absorb_q", "splitk_decode", "combine", "up_proj",
  * "fold_weights", "prepare_rotation", "covariance", "clip_fit".
  * mla_timing_query waits for the recorded events and returns the summed
  * milliseconds and launch count since the last reset.  Process-wide; not

@@ -220,12 +220,12 @@ def mla_fit_clip(dims: Dims, c_cal: torch.Tensor, R_apply_t: torch.Tensor, grid)
 
 
 def mla_fold_absorb_weights(dims: Dims, w_uk: torch.Tensor, w_uv: torch.Tensor, R_apply_t: torch.Tensor):
-    """Returns (w_uk_f [H, d_n, r] fp16, w_uv_f [H, d_v, r] fp16)."""
+    """Returns (w_uk_f [H, r, d_n] fp16 (transposed per head), w_uv_f [H, d_v, r] fp16)."""
     H, r = dims.num_heads, dims.kv_lora_rank
     _need(w_uk, "w_uk", torch.bfloat16, (H, dims.qk_nope_head_dim, r))
     _need(w_uv, "w_uv", torch.bfloat16, (H, dims.v_head_dim, r))
     _need(R_apply_t, "R_apply_t", torch.bfloat16, (r, r))
-    uk = torch.empty(w_uk.shape, dtype=torch.float16, device=w_uk.device)
+    uk = torch.empty((H, r, dims.qk_nope_head_dim), dtype=torch.float16, device=w_uk.device)
     uv = torch.empty(w_uv.shape, dtype=torch.float16, device=w_uv.device)
     d = dims.c()
     st = lib().mla_fold_absorb_weights(ctypes.byref(d), _ptr(w_uk), _ptr(w_uv), _ptr(R_apply_t), _ptr(uk),
@@ -266,7 +266,7 @@ def mla_decode_absorbed(dims: Dims, q_nope, q_rope, w_uk_f, w_uv_f, cache: Cache
     dev = q_nope.device
     _need(q_nope, "q_nope", torch.bfloat16, (B, tq, H, dims.qk_nope_head_dim))
     _need(q_rope, "q_rope", torch.bfloat16, (B, tq, H, dims.qk_rope_head_dim))
-    _need(w_uk_f, "w_uk_f", torch.float16, (H, dims.qk_nope_head_dim, r))
+    _need(w_uk_f, "w_uk_f", torch.float16, (H, r, dims.qk_nope_head_dim))
     _need(w_uv_f, "w_uv_f", torch.float16, (H, dims.v_head_dim, r))
     _need(seq_base, "seq_base", torch.int64, (B,))
     _need(seq_len, "seq_len", torch.int32, (B,))

@@ -138,7 +138,7 @@ int g_decode_variant = 0;
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
-  size_t items = 0, item_begin = 0, meta = 0, qbuf = 0, part_o = 0, part_ml = 0, total = 0;
+  size_t items = 0, item_begin = 0, meta = 0, qbuf = 0, oz = 0, part_o = 0, part_ml = 0, total = 0;
   int max_items = 0;
 };
 
@@ -168,6 +168,8 @@ WsLayout layout(const mla_dims &d, int B, int Tq) {
   const int rbm = (M + mfma_row_block() - 1) / mfma_row_block();
   const size_t q16 = static_cast<size_t>(B) * rbm * mfma_row_block() * K * sizeof(uint16_t);
   off = align256(off + std::max(q32, q16));
+  w.oz = off;
+  off = align256(off + static_cast<size_t>(B) * M * r * sizeof(float));
   w.part_o = off;
   off = align256(off + static_cast<size_t>(w.max_items) * M * r * sizeof(float));
   w.part_ml = off;
@@ -346,8 +348,8 @@ mla_status mla_fold_absorb_weights(const mla_dims *dims, const uint16_t *w_uk, c
     return fail(MLA_ERR_INVALID_ARG, "mla_fold_absorb_weights: NULL device pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int r = dims->kv_lora_rank, H = dims->num_heads;
-  hipError_t e = launch_fold(w_uk, H * dims->qk_nope_head_dim, r, R_apply_t, w_uk_f, s);
-  if (e == hipSuccess) e = launch_fold(w_uv, H * dims->v_head_dim, r, R_apply_t, w_uv_f, s);
+  hipError_t e = launch_fold(w_uk, H * dims->qk_nope_head_dim, r, R_apply_t, w_uk_f, dims->qk_nope_head_dim, s);
+  if (e == hipSuccess) e = launch_fold(w_uv, H * dims->v_head_dim, r, R_apply_t, w_uv_f, 0, s);
   if (e != hipSuccess) return hip_fail(e, "mla_fold_absorb_weights");
   clear_error();
   return MLA_OK;
@@ -430,6 +432,8 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
   } else if (g_decode_variant == 0) {
     use_mfma = M >= 16 && mfma_decode_supported(*dims, M);
   }
+  if (use_mfma && !mfma_absorb_supported(*dims))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_absorbed: qk_nope_head_dim must be a multiple of 16 for the MFMA path");
   const WsLayout w = layout(*dims, batch, tq);
   if (workspace_bytes < w.total)
     return fail(MLA_ERR_WORKSPACE, "mla_decode_absorbed: workspace needs " + std::to_string(w.total) + " bytes");
@@ -453,6 +457,7 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
   a.item_begin = reinterpret_cast<int32_t *>(ws + w.item_begin);
   a.meta = reinterpret_cast<int32_t *>(ws + w.meta);
   a.qbuf = ws + w.qbuf;
+  a.oz = reinterpret_cast<float *>(ws + w.oz);
   a.part_o = reinterpret_cast<float *>(ws + w.part_o);
   a.part_ml = reinterpret_cast<float *>(ws + w.part_ml);
   a.max_items = w.max_items;
@@ -462,7 +467,8 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
   hipError_t e = launch_plan(a, s);
   if (e == hipSuccess) e = use_mfma ? launch_absorb_mfma_layout(a, s) : launch_absorb_f32(a, s);
   if (e == hipSuccess) e = use_mfma ? launch_splitk_mfma(a, s) : launch_splitk_valu(a, s);
-  if (e == hipSuccess) e = launch_combine_upproj(a, s);
+  if (e == hipSuccess) e = launch_combine(a, s);
+  if (e == hipSuccess) e = launch_upproj(a, s);
   if (e != hipSuccess) return hip_fail(e, "mla_decode_absorbed");
   clear_error();
   return MLA_OK;

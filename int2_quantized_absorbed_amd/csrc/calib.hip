@@ -135,11 +135,12 @@ __global__ void clip_argmin_kernel(const double *__restrict__ sse, const float *
   alpha[g] = best_a;
 }
 
-// wf[row][j] = fp16(sum_i w[row][i] * R_apply[i][j]) = fp16(sum_i w[row][i] Rt[j][i])
-// 64x64 output tile per block, fp32 accumulation.
+// W~[row][j] = fp16(sum_i w[row][i] * R_apply[i][j]) = fp16(sum_i w[row][i] Rt[j][i])
+// 64x64 output tile per block, fp32 accumulation.  inner > 0 stores each
+// head's block transposed: row = h*inner + a goes to wf[(h*r + j)*inner + a].
 __global__ __launch_bounds__(256) void fold_kernel(const uint16_t *__restrict__ w, int rows,
                                                    int r, const uint16_t *__restrict__ Rt,
-                                                   uint16_t *__restrict__ wf) {
+                                                   uint16_t *__restrict__ wf, int inner) {
   constexpr int TK = 32;
   __shared__ float as[TK][65];
   __shared__ float bs[TK][65];
@@ -167,7 +168,11 @@ __global__ __launch_bounds__(256) void fold_kernel(const uint16_t *__restrict__ 
   for (int i = 0; i < 4; ++i)
     for (int j = 0; j < 4; ++j) {
       const int row = row0 + ty * 4 + i, col = col0 + tx * 4 + j;
-      if (row < rows && col < r) wf[static_cast<int64_t>(row) * r + col] = f16_bits(f32_to_f16(acc[i][j]));
+      if (row < rows && col < r) {
+        const int64_t dst = inner > 0 ? (static_cast<int64_t>(row / inner) * r + col) * inner + row % inner
+                                      : static_cast<int64_t>(row) * r + col;
+        wf[dst] = f16_bits(f32_to_f16(acc[i][j]));
+      }
     }
 }
 
@@ -203,10 +208,10 @@ hipError_t launch_group_sse(const float *z, int64_t n, int r, int G, const float
 }
 
 hipError_t launch_fold(const uint16_t *w, int rows, int r, const uint16_t *Rt, uint16_t *wf,
-                       hipStream_t s) {
+                       int inner, hipStream_t s) {
   TimedLaunch tl("fold_weights", s);
   dim3 grid((r + 63) / 64, (rows + 63) / 64);
-  fold_kernel<<<grid, 256, 0, s>>>(w, rows, r, Rt, wf);
+  fold_kernel<<<grid, 256, 0, s>>>(w, rows, r, Rt, wf, inner);
   return hipGetLastError();
 }
 

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void absorb_f32_kernel(DecodeArgs a) {
   extern __shared__ float qs_dyn[];  // [RC][dn + 1]
   const int QP = dn + 1;
   float *qbuf = static_cast<float *>(a.qbuf);
-  const uint16_t *w = a.w_uk_f + static_cast<int64_t>(h) * dn * r;
+  const uint16_t *w = a.w_uk_f + static_cast<int64_t>(h) * r * dn;  // [r][d_n] of head h
   for (int q0 = 0; q0 < nrows; q0 += RC) {
     const int nr = min(RC, nrows - q0);
     __syncthreads();
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void absorb_f32_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < RC; ++i) acc[i] = 0.0f;
       for (int k = 0; k < dn; ++k) {
-        const float wv = static_cast<float>(bits_f16(w[static_cast<int64_t>(k) * r + j]));
+        const float wv = static_cast<float>(bits_f16(w[static_cast<int64_t>(j) * dn + k]));
 #pragma unroll
         for (int i = 0; i < RC; ++i) acc[i] = fmaf(wv, qs_dyn[i * QP + k], acc[i]);
       }
@@ -251,66 +251,95 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
   }
 }
 
-// Log-sum-exp merge of the split-K partials, then out = W~_UV[h] o_z.
-// One block per head; rows (b, t) in chunks of 16.
-__global__ __launch_bounds__(256) void combine_upproj_kernel(DecodeArgs a) {
-  constexpr int CH = 16;
-  const int h = blockIdx.x;
-  const int H = a.d.num_heads, r = a.d.kv_lora_rank, dv = a.d.v_head_dim;
+// Log-sum-exp merge of the split-K partials of one query row (b, t, h):
+// m = max_i m_i, o_z = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i,
+// lse = ln 2 * (m + log2 sum_i 2^(m_i - m) l_i).  One block per row.
+__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+  const int H = a.d.num_heads, r = a.d.kv_lora_rank;
   const int M = H * a.Tq;
+  const int row = blockIdx.x;               // (b*Tq + t)*H + h
+  const int q = row / H, h = row % H;
+  const int b = q / a.Tq, t = q % a.Tq, m = t * H + h;
+  const int ib = a.item_begin[b], ie = a.item_begin[b + 1];
+  float mx = -INFINITY;
+  for (int i = ib; i < ie; ++i) mx = fmaxf(mx, a.part_ml[(static_cast<int64_t>(i) * M + m) * 2]);
+  float den = 0.0f;
+  if (mx != -INFINITY)
+    for (int i = ib; i < ie; ++i) {
+      const float mi = a.part_ml[(static_cast<int64_t>(i) * M + m) * 2];
+      if (mi != -INFINITY) den += exp2f(mi - mx) * a.part_ml[(static_cast<int64_t>(i) * M + m) * 2 + 1];
+    }
+  if (threadIdx.x == 0 && a.lse != nullptr) a.lse[row] = (den > 0.0f) ? (mx + log2f(den)) * kLn2 : -INFINITY;
+  const float inv = (den > 0.0f) ? 1.0f / den : 0.0f;
+  float *dst = a.oz + static_cast<int64_t>(row) * r;
+  for (int j = 4 * threadIdx.x; j < r; j += 4 * blockDim.x) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (den > 0.0f)
+      for (int i = ib; i < ie; ++i) {
+        const float mi = a.part_ml[(static_cast<int64_t>(i) * M + m) * 2];
+        if (mi == -INFINITY) continue;
+        const float wgt = exp2f(mi - mx);
+        acc += wgt * *reinterpret_cast<const f32x4 *>(a.part_o + (static_cast<int64_t>(i) * M + m) * r + j);
+      }
+    *reinterpret_cast<f32x4 *>(dst + j) = acc * inv;
+  }
+}
+
+// out[b,t,h,:] = W~_UV[h] o_z[b,t,h,:] on MFMA (32x32x16 f16, fp32 acc).
+// o_z is split as hi + lo (two fp16 parts) so the product keeps ~fp32
+// precision of o_z; W~_UV is fp16.  Block = (head, 32 query rows); wave w
+// produces output columns [32w, 32w + 32) of each 128-wide slice.
+__global__ __launch_bounds__(256) void upproj_mfma_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, rt = blockIdx.y;
+  const int H = a.d.num_heads, r = a.d.kv_lora_rank, dv = a.d.v_head_dim;
   const int nrows = a.B * a.Tq;
-  __shared__ float oz[CH][513];
-  __shared__ float mmax_s[CH], den_s[CH];
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  for (int q0 = 0; q0 < nrows; q0 += CH) {
-    const int nr = min(CH, nrows - q0);
-    __syncthreads();
-    if (tid < nr) {
-      const int q = q0 + tid, b = q / a.Tq, t = q % a.Tq, m = t * H + h;
-      const int ib = a.item_begin[b], ie = a.item_begin[b + 1];
-      float mx = -INFINITY;
-      for (int i = ib; i < ie; ++i) mx = fmaxf(mx, a.part_ml[(static_cast<int64_t>(i) * M + m) * 2]);
-      float den = 0.0f;
-      if (mx != -INFINITY)
-        for (int i = ib; i < ie; ++i) {
-          const float mi = a.part_ml[(static_cast<int64_t>(i) * M + m) * 2];
-          if (mi != -INFINITY) den += exp2f(mi - mx) * a.part_ml[(static_cast<int64_t>(i) * M + m) * 2 + 1];
-        }
-      mmax_s[tid] = mx;
-      den_s[tid] = den;
-      if (a.lse != nullptr)
-        a.lse[static_cast<int64_t>(q) * H + h] = (den > 0.0f) ? (mx + log2f(den)) * kLn2 : -INFINITY;
-    }
-    __syncthreads();
-    for (int e = tid; e < nr * r; e += 256) {
-      const int i = e / r, j = e % r;
-      const int q = q0 + i, b = q / a.Tq, t = q % a.Tq, m = t * H + h;
-      const int ib = a.item_begin[b], ie = a.item_begin[b + 1];
-      const float mx = mmax_s[i], den = den_s[i];
-      float num = 0.0f;
-      if (den > 0.0f) {
-        for (int it = ib; it < ie; ++it) {
-          const float mi = a.part_ml[(static_cast<int64_t>(it) * M + m) * 2];
-          if (mi != -INFINITY) num += exp2f(mi - mx) * a.part_o[(static_cast<int64_t>(it) * M + m) * r + j];
-        }
-        num /= den;
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, hf = l >> 5, l32 = l & 31;
+  const int q = rt * 32 + l32;              // A-operand row of this lane
+  const bool q_ok = q < nrows;
+  const float *arow = a.oz + (static_cast<int64_t>(q_ok ? q : 0) * H + h) * r;
+  for (int v0 = 32 * w; v0 < dv; v0 += 128) {
+    const uint16_t *brow = a.w_uv_f + (static_cast<int64_t>(h) * dv + v0 + l32) * r;
+    f32x16 acc = {};
+    for (int k0 = 0; k0 < r; k0 += 16) {
+      f16x8 ahi, alo;
+      const f32x4 x0 = q_ok ? *reinterpret_cast<const f32x4 *>(arow + k0 + 8 * hf) : f32x4{};
+      const f32x4 x1 = q_ok ? *reinterpret_cast<const f32x4 *>(arow + k0 + 8 * hf + 4) : f32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16 h0 = static_cast<f16>(x0[e]), h1 = static_cast<f16>(x1[e]);
+        ahi[e] = h0;
+        ahi[e + 4] = h1;
+        alo[e] = static_cast<f16>(x0[e] - static_cast<float>(h0));
+        alo[e + 4] = static_cast<f16>(x1[e] - static_cast<float>(h1));
       }
-      oz[i][j] = num;
+      const f16x8 bw = *reinterpret_cast<const f16x8 *>(brow + k0 + 8 * hf);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bw, acc, 0, 0, 0);
     }
-    __syncthreads();
-    for (int v = wv; v < dv; v += 4) {
-      const uint16_t *wrow = a.w_uv_f + (static_cast<int64_t>(h) * dv + v) * r;
-      float wl[8];
-      int nw = 0;
-      for (int j = lane; j < r && nw < 8; j += 64) wl[nw++] = static_cast<float>(bits_f16(wrow[j]));
-      for (int i = 0; i < nr; ++i) {
-        float s = 0.0f;
-        int k = 0;
-        for (int j = lane; j < r && k < 8; j += 64) s = fmaf(wl[k++], oz[i][j], s);
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-        if (lane == 0) a.out[(static_cast<int64_t>(q0 + i) * H + h) * dv + v] = s;
-      }
+    // C layout: lane holds column v0 + l32, rows 8(v/4) + 4hf + v%4
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int qq = rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+      if (qq < nrows) a.out[(static_cast<int64_t>(qq) * H + h) * dv + v0 + l32] = acc[v];
     }
+  }
+}
+
+// Vector-ALU up-projection for v_head_dim not a multiple of 32: one wave per
+// (head, output column), lanes split the latent channels.
+__global__ __launch_bounds__(256) void upproj_valu_kernel(DecodeArgs a) {
+  const int H = a.d.num_heads, r = a.d.kv_lora_rank, dv = a.d.v_head_dim;
+  const int nrows = a.B * a.Tq;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (gw >= H * dv) return;
+  const int h = gw / dv, v = gw % dv;
+  const uint16_t *wrow = a.w_uv_f + (static_cast<int64_t>(h) * dv + v) * r;
+  for (int q = 0; q < nrows; ++q) {
+    const float *oz = a.oz + (static_cast<int64_t>(q) * H + h) * r;
+    float s = 0.0f;
+    for (int j = lane; j < r; j += 64) s = fmaf(static_cast<float>(bits_f16(wrow[j])), oz[j], s);
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) a.out[(static_cast<int64_t>(q) * H + h) * dv + v] = s;
   }
 }
 
@@ -350,9 +379,22 @@ hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine_upproj(const DecodeArgs &a, hipStream_t s) {
-  TimedLaunch tl("combine_upproj", s);
-  combine_upproj_kernel<<<a.d.num_heads, 256, 0, s>>>(a);
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
+  TimedLaunch tl("combine", s);
+  const int rows = a.B * a.Tq * a.d.num_heads;
+  combine_kernel<<<rows, 128, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_upproj(const DecodeArgs &a, hipStream_t s) {
+  TimedLaunch tl("up_proj", s);
+  if (a.d.v_head_dim % 32 == 0) {
+    const int nrows = a.B * a.Tq;
+    upproj_mfma_kernel<<<dim3(a.d.num_heads, (nrows + 31) / 32), 256, 0, s>>>(a);
+  } else {
+    const int waves = a.d.num_heads * a.d.v_head_dim;
+    upproj_valu_kernel<<<(waves + 3) / 4, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -36,7 +36,6 @@ constexpr int ROWS = 64;        // query rows per workgroup
 constexpr int TT = 32;          // tokens per tile
 constexpr int KB = 9;           // K-blocks of 16 per wave: 8 latent + 1 rope
 constexpr int ZSTRIDE = 144;    // halves per token row of the Z tile (128 + pad)
-constexpr int PSTRIDE = 80;     // halves per token row of P^T (64 + pad)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -48,21 +47,17 @@ __device__ __forceinline__ f16x4 ds_read_tr16(const f16 *p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
-// 16-lane all-reduce via DPP (xor 1, xor 2, half-row mirror, row mirror),
-// then the two 16-lane rows of each 32-lane half are combined with a swap.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
+// all-reduce over the 4 lanes of a quad (DPP quad permutations)
 template <bool kMax>
-__device__ __forceinline__ float reduce32(float x) {
+__device__ __forceinline__ float reduce4(float x) {
   auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
-  x = op(x, dpp_mov<0xB1>(x));     // quad_perm [1,0,3,2]
-  x = op(x, dpp_mov<0x4E>(x));     // quad_perm [2,3,0,1]
-  x = op(x, dpp_mov<0x141>(x));    // row_half_mirror
-  x = op(x, dpp_mov<0x140>(x));    // row_mirror
-  x = op(x, __shfl_xor(x, 16));
+  x = op(x, dpp_mov<0xB1>(x));  // quad_perm [1,0,3,2]
+  x = op(x, dpp_mov<0x4E>(x));  // quad_perm [2,3,0,1]
   return x;
 }
 
@@ -74,12 +69,36 @@ __device__ __forceinline__ int slot_channel(int hf, int kb, int e) {
   return 64 * hf + 16 * (kb >> 1) + 4 * (kb & 1) + (e >> 1) + 8 * (e & 1);
 }
 
+constexpr int SPSTRIDE = 68;    // floats per accumulator slot row (2 x 32 lanes + pad)
+constexpr int PRSTRIDE = 40;    // halves per row of P (32 tokens + pad)
+
 struct __align__(16) Smem {
-  float sp[4][32][64];              // partial scores, [wave][acc slot][lane]
-  f16 z[4][TT * ZSTRIDE];           // dequantised latent tile per wave
-  f16 pt[TT * PSTRIDE];             // P^T [token][row]
+  float sp[4][32][SPSTRIDE];        // partial scores [wave][acc slot][lane (+4 for hf=1)]
+  f16 z[4][TT * ZSTRIDE];           // dequantised latent tile per wave, [token][slot]
+  f16 p[ROWS * PRSTRIDE];           // P [row][token]
   float alpha[ROWS];
 };
+
+struct RawTile {
+  uint4 codes;
+  uint4 sz;     // 2 (G = 32) or 4 (G = 16) scale/zero words
+  uint4 rope;
+};
+
+template <int G>
+__device__ __forceinline__ RawTile load_tile(const DecodeArgs &a, int64_t slot, int w, int hf) {
+  RawTile t;
+  const uint32_t *codes32 = reinterpret_cast<const uint32_t *>(a.cache.codes);
+  t.codes = *reinterpret_cast<const uint4 *>(codes32 + slot * (R / 16) + w * 8 + hf * 4);
+  if (G == 32) {
+    const uint2 s2 = *reinterpret_cast<const uint2 *>(a.cache.scale_zero + (slot * (R / G) + (4 * w + 2 * hf)) * 2);
+    t.sz = uint4{s2.x, s2.y, 0u, 0u};
+  } else {
+    t.sz = *reinterpret_cast<const uint4 *>(a.cache.scale_zero + (slot * (R / G) + (8 * w + 4 * hf)) * 2);
+  }
+  t.rope = *reinterpret_cast<const uint4 *>(a.cache.k_rope + slot * DR + 16 * w + 8 * hf);
+  return t;
+}
 
 template <int G>
 __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int rb_count, int n_logical) {
@@ -112,27 +131,14 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
       for (int kb = 0; kb < KB; ++kb) aq[mt][kb] = qp[(mt * KB + kb) * 64 + l];
   }
 
-  // ---- softmax rows owned by this wave: acc slots rho = 8w .. 8w+7 ----
-  // slot rho -> (mt = rho/16, v = rho%16) -> row 32mt + 8(v/4) + 4hf + v%4
-  int srow[8], svis[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rho = 8 * w + i, mt = rho >> 4, v = rho & 15;
-    srow[i] = 32 * mt + 8 * (v >> 2) + 4 * hf + (v & 3);
-    const int m = rb * ROWS + srow[i];
-    if (m < M) {
-      const int t = m / H;
-      svis[i] = a.causal ? (L - a.Tq + t + 1) : L;
-    } else {
-      svis[i] = -1;  // padding row: never visible
-    }
-  }
-  float m_run[8], l_run[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.0f;
-  }
+  // ---- softmax ownership: lane -> (accumulator slot, lane half, 8 tokens) ----
+  // slot rho = 8w + (l >> 3) maps to row 32(rho/16) + 8((rho%16)/4) + 4*shf + rho%4
+  const int s_rho = 8 * w + (l >> 3), s_hf = (l >> 2) & 1, s_k8 = l & 3;
+  const int s_row = 32 * (s_rho >> 4) + 8 * ((s_rho & 15) >> 2) + 4 * s_hf + (s_rho & 3);
+  const int s_m = rb * ROWS + s_row;
+  int s_vis = -1;  // padding rows are never visible
+  if (s_m < M) s_vis = a.causal ? (L - a.Tq + s_m / H + 1) : L;
+  float m_run = -INFINITY, l_run = 0.0f;
 
   f32x16 o[2][4];
 #pragma unroll
@@ -140,40 +146,25 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x16{};
 
-  const uint32_t *codes32 = reinterpret_cast<const uint32_t *>(a.cache.codes);
-  const uint16_t *sz16 = a.cache.scale_zero;
-  const uint16_t *rope = a.cache.k_rope;
-  constexpr int NG = R / G;                 // groups per token
-  constexpr int GPL = 64 / G;               // groups per lane (2 or 4)
   const f16x2 k1024 = {static_cast<f16>(-1024.0f), static_cast<f16>(-1024.0f)};
+  const int g16 = l >> 4, s16 = l & 15;
+  f16 *zt_w = sm.z[w] + l32 * ZSTRIDE + 64 * hf;
 
+  RawTile cur = load_tile<G>(a, base + min(it.t0 + l32, it.t1 - 1), w, hf);
   for (int t0 = it.t0; t0 < it.t1; t0 += TT) {
-    // ---- 1. load + dequantise this lane's token into score B operands ----
-    const int tau = t0 + l32;
-    const bool tok_ok = tau < it.t1;
-    const int64_t slot = base + (tok_ok ? tau : it.t0);
-    const uint4 cw = *reinterpret_cast<const uint4 *>(codes32 + slot * (R / 16) + w * 8 + hf * 4);
-    uint32_t szw[GPL];
-    if (GPL == 2) {
-      const uint2 s2 = *reinterpret_cast<const uint2 *>(sz16 + (slot * NG + (4 * w + 2 * hf)) * 2);
-      szw[0] = s2.x;
-      szw[1] = s2.y;
-    } else {
-      const uint4 s4 = *reinterpret_cast<const uint4 *>(sz16 + (slot * NG + (8 * w + 4 * hf)) * 2);
-      szw[0] = s4.x;
-      szw[1] = s4.y;
-      szw[2 % GPL] = s4.z;
-      szw[3 % GPL] = s4.w;
-    }
-    const uint4 rw = *reinterpret_cast<const uint4 *>(rope + slot * DR + 16 * w + 8 * hf);
+    // ---- 0. prefetch the next tile (clamped in-bounds; unused past the end) ----
+    const int tn = t0 + TT;
+    RawTile nxt = cur;
+    if (tn < it.t1) nxt = load_tile<G>(a, base + min(tn + l32, it.t1 - 1), w, hf);
 
+    // ---- 1. dequantise this lane's token into the score B operands ----
     f16x8 bz[KB];
-    const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+    const uint32_t cws[4] = {cur.codes.x, cur.codes.y, cur.codes.z, cur.codes.w};
+    const uint32_t szw[4] = {cur.sz.x, cur.sz.y, cur.sz.z, cur.sz.w};
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
       const int q = kb >> 1;                       // dword: channels 16q..16q+15
-      const int gi = (G == 32) ? (q >> 1) : q;     // group within the lane
-      const uint32_t sz = szw[gi];
+      const uint32_t sz = szw[(G == 32) ? (q >> 1) : q];
       const f16x2 sc = __builtin_bit_cast(f16x2, (sz & 0xffffu) * 0x10001u);
       const f16x2 zr = __builtin_bit_cast(f16x2, (sz >> 16) * 0x10001u);
       f16x8 v;
@@ -188,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
       bz[kb] = v;
     }
     {
-      const uint32_t rws[4] = {rw.x, rw.y, rw.z, rw.w};
+      const uint32_t rws[4] = {cur.rope.x, cur.rope.y, cur.rope.z, cur.rope.w};
       f16x8 v;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -207,40 +198,60 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
 
     // latent tile to LDS (wave-private), row = token, slots 64hf + 8kb + e
-    f16 *zt = sm.z[w] + l32 * ZSTRIDE + 64 * hf;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = bz[kb];
-    // partial scores to LDS, slot-major and lane-contiguous
+    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt_w + 8 * kb) = bz[kb];
+    // partial scores to LDS: slot-major, lanes contiguous per half
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sm.sp[w][mt * 16 + v][l] = sacc[mt][v];
+      for (int v = 0; v < 16; ++v) sm.sp[w][mt * 16 + v][l + 4 * hf] = sacc[mt][v];
     __syncthreads();
 
-    // ---- 3. reduce partials + online softmax for this wave's 16 rows ----
-    bool any_rescale = false;
+    // ---- 3. reduce partials + online softmax: one row x 8 tokens per lane ----
+    float s[8];
+    {
+      const int off = 32 * s_hf + 4 * s_hf + 8 * s_k8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rho = 8 * w + i;
-      float s = sm.sp[0][rho][l] + sm.sp[1][rho][l] + sm.sp[2][rho][l] + sm.sp[3][rho][l];
-      if (!(tok_ok && tau < svis[i])) s = -INFINITY;
-      const float tmax = reduce32<true>(s);
-      float m_use = m_run[i];
-      float alpha = 1.0f;
-      if (tmax > m_use + kRescaleThreshold) {  // also true for the first visible tile
-        alpha = (m_use == -INFINITY) ? 0.0f : exp2f(m_use - tmax);
-        m_use = tmax;
-        any_rescale = true;
+      for (int e = 0; e < 8; e += 4) {
+        f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[0][s_rho][off + e]);
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[ww][s_rho][off + e]);
+        s[e] = acc4[0];
+        s[e + 1] = acc4[1];
+        s[e + 2] = acc4[2];
+        s[e + 3] = acc4[3];
       }
-      const float p = (s == -INFINITY) ? 0.0f : exp2f(s - m_use);
-      const float psum = reduce32<false>(p);
-      l_run[i] = l_run[i] * alpha + psum;
-      m_run[i] = m_use;
-      sm.pt[l32 * PSTRIDE + srow[i]] = static_cast<f16>(p);
-      if (l32 == 0) sm.alpha[srow[i]] = alpha;
     }
+    const int tau0 = t0 + 8 * s_k8;
+    const int lim = min(it.t1, s_vis);  // tokens < lim are visible to this row
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (tau0 + e >= lim) s[e] = -INFINITY;
+      tmax = fmaxf(tmax, s[e]);
+    }
+    tmax = reduce4<true>(tmax);
+    float alpha = 1.0f;
+    bool rescaled = false;
+    if (tmax > m_run + kRescaleThreshold) {  // also true for the first visible tile
+      alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - tmax);
+      m_run = tmax;
+      rescaled = true;
+    }
+    float psum = 0.0f;
+    f16x8 pv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = (s[e] == -INFINITY) ? 0.0f : exp2f(s[e] - m_run);
+      psum += p;
+      pv[e] = static_cast<f16>(p);
+    }
+    psum = reduce4<false>(psum);
+    l_run = l_run * alpha + psum;
+    *reinterpret_cast<f16x8 *>(sm.p + s_row * PRSTRIDE + 8 * s_k8) = pv;
+    if (s_k8 == 0) sm.alpha[s_row] = alpha;
     // barrier that also tells every wave whether any row moved its max
-    const int rescale = __syncthreads_or(any_rescale ? 1 : 0);
+    const int rescale = __syncthreads_or(rescaled ? 1 : 0);
 
     // ---- 4. O = alpha * O + P Z ----
     if (rescale) {
@@ -253,20 +264,15 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
           for (int nt = 0; nt < 4; ++nt) o[mt][nt][v] *= al;
         }
     }
-    const int g = l >> 4, s16 = l & 15;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      // source-lane addresses for the transposing loads: 4 tokens x 16 columns
-      const int krow = 16 * ks + 8 * (g >> 1) + (s16 >> 2);
-      const int col = 16 * (g & 1) + 4 * (s16 & 3);
       f16x8 pa[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const f16 *p0 = sm.pt + krow * PSTRIDE + 32 * mt + col;
-        const f16x4 lo = ds_read_tr16(p0);
-        const f16x4 hi = ds_read_tr16(p0 + 4 * PSTRIDE);
-        pa[mt] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      for (int mt = 0; mt < 2; ++mt)
+        pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
+      // transposing loads: source lane reads 4 slots of token krow
+      const int krow = 16 * ks + 8 * (g16 >> 1) + (s16 >> 2);
+      const int col = 16 * (g16 & 1) + 4 * (s16 & 3);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const f16 *z0 = sm.z[w] + krow * ZSTRIDE + 32 * nt + col;
@@ -278,6 +284,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
           o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[mt], zb, o[mt][nt], 0, 0, 0);
       }
     }
+    cur = nxt;
   }
 
   // ---- write the partial (O, m, l) of this work item ----
@@ -293,82 +300,89 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
         if (m < M) a.part_o[(static_cast<int64_t>(item) * M + m) * R + ch] = o[mt][nt][v];
       }
   }
-  if (l32 == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = rb * ROWS + srow[i];
-      if (m < M) {
-        a.part_ml[(static_cast<int64_t>(item) * M + m) * 2 + 0] = m_run[i];
-        a.part_ml[(static_cast<int64_t>(item) * M + m) * 2 + 1] = l_run[i];
-      }
-    }
+  if (s_k8 == 0 && s_m < M) {
+    a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 0] = m_run;
+    a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 1] = l_run;
   }
 }
 
-// q~ = W~_UK[h]^T q_nope and q_rope, both times scale*log2(e), written in fp16
-// straight into the per-lane operand order of splitk_mfma_kernel:
-// [b][row block][wave][mt][kb][lane][8], zero for padding rows.
+// q~ = W~_UK[h]^T q_nope on MFMA (32x32x16 f16, fp32 acc), and q_rope; both
+// times scale*log2(e), written in fp16 straight into the per-lane operand
+// order of splitk_mfma_kernel: [b][row block][wave][mt][kb][lane][8], zero
+// for padding rows.  Block = (head, 32 query rows (b, t)); wave w computes
+// latent channels [128w, 128w + 128).  w_uk_f is stored [H][r][d_n].
+__device__ __forceinline__ int64_t qpos(int rb_count, int b, int m, int w, int hf, int kb, int e) {
+  const int rb = m / ROWS, mt = (m % ROWS) / 32, lane = (m % 32) + 32 * hf;
+  return ((((static_cast<int64_t>(b) * rb_count + rb) * 4 + w) * 2 + mt) * KB + kb) * 512 + lane * 8 + e;
+}
+
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_count) {
-  constexpr int RC = 16;
-  extern __shared__ float qs_dyn[];
-  const int h = blockIdx.x;
+  const int h = blockIdx.x, rt = blockIdx.y;
   const int H = a.d.num_heads, dn = a.d.qk_nope_head_dim;
   const int M = H * a.Tq;
   const int nrows = a.B * a.Tq;
-  const int QP = dn + 1;
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, hf = l >> 5, l32 = l & 31;
   f16 *qb = static_cast<f16 *>(a.qbuf);
-  const uint16_t *wk = a.w_uk_f + static_cast<int64_t>(h) * dn * R;
-  auto pos = [&](int b, int m, int w, int hf, int kb, int e) -> int64_t {
-    const int rb = m / ROWS, mt = (m % ROWS) / 32, lane = (m % 32) + 32 * hf;
-    return ((((static_cast<int64_t>(b) * rb_count + rb) * 4 + w) * 2 + mt) * KB + kb) * 512 + lane * 8 + e;
-  };
-  for (int q0 = 0; q0 < nrows; q0 += RC) {
-    const int nr = min(RC, nrows - q0);
-    __syncthreads();
-    for (int e = threadIdx.x; e < nr * dn; e += 256) {
-      const int i = e / dn, k = e % dn;
-      qs_dyn[i * QP + k] = bf16_to_f32(a.q_nope[(static_cast<int64_t>(q0 + i) * H + h) * dn + k]);
-    }
-    __syncthreads();
-    for (int j = threadIdx.x; j < R; j += 256) {
-      float acc[RC];
+  const int q = rt * 32 + l32;
+  const bool q_ok = q < nrows;
+  const uint16_t *arow = a.q_nope + (static_cast<int64_t>(q_ok ? q : 0) * H + h) * dn;
+  const uint16_t *wk = a.w_uk_f + static_cast<int64_t>(h) * R * dn;
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  for (int k0 = 0; k0 < dn; k0 += 16) {
+    const uint4 raw = q_ok ? *reinterpret_cast<const uint4 *>(arow + k0 + 8 * hf) : uint4{0, 0, 0, 0};
+    const uint32_t rr[4] = {raw.x, raw.y, raw.z, raw.w};
+    f16x8 av;
 #pragma unroll
-      for (int i = 0; i < RC; ++i) acc[i] = 0.0f;
-      for (int k = 0; k < dn; ++k) {
-        const float wv = static_cast<float>(bits_f16(wk[static_cast<int64_t>(k) * R + j]));
+    for (int j = 0; j < 4; ++j) {
+      av[2 * j] = static_cast<f16>(bf16_to_f32(static_cast<uint16_t>(rr[j] & 0xffffu)));
+      av[2 * j + 1] = static_cast<f16>(bf16_to_f32(static_cast<uint16_t>(rr[j] >> 16)));
+    }
 #pragma unroll
-        for (int i = 0; i < RC; ++i) acc[i] = fmaf(wv, qs_dyn[i * QP + k], acc[i]);
-      }
-      // inverse of slot_channel
-      const int w = j >> 7, jj = j & 127, hf = jj >> 6, r6 = jj & 63;
-      const int q = r6 >> 4, idx = r6 & 15, i8 = idx >> 3, rem = idx & 7;
-      const int kb = 2 * q + (rem >> 2), e = 2 * (rem & 3) + i8;
-      for (int i = 0; i < nr; ++i) {
-        const int row = q0 + i, b = row / a.Tq, t = row % a.Tq, m = t * H + h;
-        qb[pos(b, m, w, hf, kb, e)] = static_cast<f16>(acc[i] * a.scale_log2);
+    for (int nt = 0; nt < 4; ++nt) {
+      const int j = 128 * w + 32 * nt + l32;
+      const f16x8 bv = *reinterpret_cast<const f16x8 *>(wk + static_cast<int64_t>(j) * dn + k0 + 8 * hf);
+      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[nt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    // inverse of slot_channel for latent channel j = 128w + jj
+    const int jj = 32 * nt + l32, shf = jj >> 6, r6 = jj & 63;
+    const int qd = r6 >> 4, idx = r6 & 15, i8 = idx >> 3, rem = idx & 7;
+    const int kb = 2 * qd + (rem >> 2), e = 2 * (rem & 3) + i8;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int qq = rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+      if (qq < nrows) {
+        const int b = qq / a.Tq, t = qq % a.Tq, m = t * H + h;
+        qb[qpos(rb_count, b, m, w, shf, kb, e)] = static_cast<f16>(acc[nt][v] * a.scale_log2);
       }
     }
-    for (int e = threadIdx.x; e < nr * DR; e += 256) {
-      const int i = e / DR, k = e % DR;
-      const int row = q0 + i, b = row / a.Tq, t = row % a.Tq, m = t * H + h;
-      const float v = bf16_to_f32(a.q_rope[(static_cast<int64_t>(row) * H + h) * DR + k]) * a.scale_log2;
-      qb[pos(b, m, k >> 4, (k >> 3) & 1, 8, k & 7)] = static_cast<f16>(v);
+  }
+  for (int e = threadIdx.x; e < 32 * DR; e += 256) {
+    const int i = e / DR, k = e % DR, qq = rt * 32 + i;
+    if (qq < nrows) {
+      const int b = qq / a.Tq, t = qq % a.Tq, m = t * H + h;
+      const float v = bf16_to_f32(a.q_rope[(static_cast<int64_t>(qq) * H + h) * DR + k]) * a.scale_log2;
+      qb[qpos(rb_count, b, m, k >> 4, (k >> 3) & 1, 8, k & 7)] = static_cast<f16>(v);
     }
   }
   // zero the padding rows of the last row block (one block does it)
-  if (h == 0 && M % ROWS != 0) {
+  if (h == 0 && rt == 0 && M % ROWS != 0) {
     const int pad = rb_count * ROWS - M;
     for (int b = 0; b < a.B; ++b)
       for (int e = threadIdx.x; e < pad * 4 * KB * 16; e += 256) {
         const int m = M + e / (4 * KB * 16);
         const int rest = e % (4 * KB * 16);
-        const int w = rest / (KB * 16), kb = (rest / 16) % KB, hfe = rest % 16;
-        qb[pos(b, m, w, hfe >> 3, kb, hfe & 7)] = static_cast<f16>(0.0f);
+        const int ww = rest / (KB * 16), kb = (rest / 16) % KB, hfe = rest % 16;
+        qb[qpos(rb_count, b, m, ww, hfe >> 3, kb, hfe & 7)] = static_cast<f16>(0.0f);
       }
   }
 }
 
 }  // namespace
+
+bool mfma_absorb_supported(const mla_dims &d) { return d.qk_nope_head_dim % 16 == 0; }
 
 bool mfma_decode_supported(const mla_dims &d, int rows) {
   return d.kv_lora_rank == R && d.qk_rope_head_dim == DR && (d.group_size == 32 || d.group_size == 16) &&
@@ -381,8 +395,8 @@ hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s) {
   TimedLaunch tl("absorb_q", s);
   const int M = a.d.num_heads * a.Tq;
   const int rb_count = (M + ROWS - 1) / ROWS;
-  const size_t lds = static_cast<size_t>(16) * (a.d.qk_nope_head_dim + 1) * sizeof(float);
-  absorb_mfma_kernel<<<a.d.num_heads, 256, lds, s>>>(a, rb_count);
+  const int nrows = a.B * a.Tq;
+  absorb_mfma_kernel<<<dim3(a.d.num_heads, (nrows + 31) / 32), 256, 0, s>>>(a, rb_count);
   return hipGetLastError();
 }
 

@@ -20,8 +20,9 @@ hipError_t launch_prepare_rotation(const float *R, int r, uint16_t *Rt,
 hipError_t launch_group_sse(const float *z, int64_t n, int r, int G,
                             const float *grid, int n_grid, double *sse,
                             float *alpha_out, hipStream_t s);
+// inner > 0: store per-head blocks transposed ([head][r][inner])
 hipError_t launch_fold(const uint16_t *w, int rows, int r, const uint16_t *Rt,
-                       uint16_t *wf, hipStream_t s);
+                       uint16_t *wf, int inner, hipStream_t s);
 
 // ---- append (append.hip) ----
 // z_out != nullptr: write the fp32 rotated latent [n][r] instead of the cache
@@ -48,6 +49,7 @@ struct DecodeArgs {
   int32_t *item_begin;  // [B + 1]
   int32_t *meta;        // [0] = n_items, [1] = chunk tokens
   void *qbuf;           // absorbed queries
+  float *oz;            // combined latent output [B*M][r]
   float *part_o;        // [max_items][M][r]
   float *part_ml;       // [max_items][M][2]  (m in log2 units, l)
   int32_t max_items;
@@ -58,10 +60,12 @@ struct DecodeArgs {
 hipError_t launch_plan(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_absorb_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_combine_upproj(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_upproj(const DecodeArgs &a, hipStream_t s);
 
 // MFMA split-K path (r = 512, d_r = 64): supported() says whether it applies.
 bool mfma_decode_supported(const mla_dims &d, int rows);
+bool mfma_absorb_supported(const mla_dims &d);
 int mfma_row_block();
 hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s);

@@ -72,8 +72,10 @@ def test_fit_clip(wid):
 def test_fold_weights():
     w = S.WORKLOADS[1].with_(num_heads=8)
     layer = C.Layer(w)
-    for got, wt in ((layer.w_uk_f, layer.w_uk), (layer.w_uv_f, layer.w_uv)):
+    for got, wt, tr in ((layer.w_uk_f, layer.w_uk, True), (layer.w_uv_f, layer.w_uv, False)):
         ref = O.fold_weights(wt, layer.R_apply)
+        if tr:  # the K-side fold is stored [H][r][d_n]
+            ref = np.ascontiguousarray(np.swapaxes(ref, 1, 2))
         g = got.float().cpu().numpy().astype(np.float64)
         # fp32 accumulation then one fp16 rounding: the accumulation error can
         # move a value across an fp16 rounding midpoint, so allow one fp16 ulp
