@@ -47,6 +47,13 @@ __device__ __forceinline__ f16x4 ds_read_tr16(const f16 *p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
+// Workgroup barrier that only waits for this wave's LDS operations.  HIP's
+// __syncthreads() also waits for every outstanding global load, which would
+// force the next tile's prefetch to land at the first barrier of each tile.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
@@ -77,6 +84,7 @@ struct __align__(16) Smem {
   f16 z[4][TT * ZSTRIDE];           // dequantised latent tile per wave, [token][slot]
   f16 p[ROWS * PRSTRIDE];           // P [row][token]
   float alpha[ROWS];
+  int resc[4];                      // per wave: some row of it moved its max
 };
 
 struct RawTile {
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sm.sp[w][mt * 16 + v][l + 4 * hf] = sacc[mt][v];
-    __syncthreads();
+    lds_barrier();
 
     // ---- 3. reduce partials + online softmax: one row x 8 tokens per lane ----
     float s[8];
@@ -250,8 +258,10 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     l_run = l_run * alpha + psum;
     *reinterpret_cast<f16x8 *>(sm.p + s_row * PRSTRIDE + 8 * s_k8) = pv;
     if (s_k8 == 0) sm.alpha[s_row] = alpha;
-    // barrier that also tells every wave whether any row moved its max
-    const int rescale = __syncthreads_or(rescaled ? 1 : 0);
+    const int any_w = __any(rescaled ? 1 : 0);
+    if (l == 0) sm.resc[w] = any_w;
+    lds_barrier();
+    const int rescale = sm.resc[0] | sm.resc[1] | sm.resc[2] | sm.resc[3];
 
     // ---- 4. O = alpha * O + P Z ----
     if (rescale) {
