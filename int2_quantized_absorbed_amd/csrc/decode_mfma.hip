@@ -54,6 +54,19 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// x *= al for a value the MFMA accumulates in an AGPR.  Written as inline asm
+// with an AGPR operand so the compiler keeps the accumulators in AGPRs and
+// cannot hoist their copies out of the (rarely taken) rescale branch.
+__device__ __forceinline__ void agpr_scale(float &x, float al) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\t"
+      "v_mul_f32 %1, %1, %2\n\t"
+      "v_accvgpr_write_b32 %0, %1"
+      : "+a"(x), "=&v"(t)
+      : "v"(al));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
@@ -79,12 +92,16 @@ __device__ __forceinline__ int slot_channel(int hf, int kb, int e) {
 constexpr int SPSTRIDE = 68;    // floats per accumulator slot row (2 x 32 lanes + pad)
 constexpr int PRSTRIDE = 40;    // halves per row of P (32 tokens + pad)
 
+// Double-buffered tile state (one barrier per tile):
+//   z   per wave, dequantised latent tile [token][slot] (PV B operand)
+//   sp  partial scores [wave][acc slot][lane (+4 for hf = 1)]
+//   p   P [row][token] (PV A operand), alpha per row, per-wave rescale flags
 struct __align__(16) Smem {
-  float sp[4][32][SPSTRIDE];        // partial scores [wave][acc slot][lane (+4 for hf=1)]
-  f16 z[4][TT * ZSTRIDE];           // dequantised latent tile per wave, [token][slot]
-  f16 p[ROWS * PRSTRIDE];           // P [row][token]
-  float alpha[ROWS];
-  int resc[4];                      // per wave: some row of it moved its max
+  f16 z[2][4][TT * ZSTRIDE];
+  float sp[2][4][32][SPSTRIDE];
+  f16 p[2][ROWS * PRSTRIDE];
+  float alpha[2][ROWS];
+  int resc[2][4];
 };
 
 struct RawTile {
@@ -108,6 +125,40 @@ __device__ __forceinline__ RawTile load_tile(const DecodeArgs &a, int64_t slot, 
   return t;
 }
 
+// codes -> fp16 score B operands.  Per pair of channels: shift, one
+// v_and_or_b32 building (1024 + c) in both halves, subtract 1024 (exact),
+// one fused fp16 multiply-add with the group's (scale, zero).
+template <int G>
+__device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB], uint32_t mask2, f16x2 k1024) {
+  const uint32_t cws[4] = {t.codes.x, t.codes.y, t.codes.z, t.codes.w};
+  const uint32_t szw[4] = {t.sz.x, t.sz.y, t.sz.z, t.sz.w};
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    const int q = kb >> 1;
+    const uint32_t sz = szw[(G == 32) ? (q >> 1) : q];
+    const f16x2 sc = __builtin_bit_cast(f16x2, (sz & 0xffffu) * 0x10001u);
+    const f16x2 zr = __builtin_bit_cast(f16x2, (sz >> 16) * 0x10001u);
+    f16x8 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = ((cws[q] >> (2 * (4 * (kb & 1) + j))) & mask2) | 0x64006400u;
+      const f16x2 c = __builtin_bit_cast(f16x2, x) + k1024;     // exact small integers
+      const f16x2 z2 = __builtin_elementwise_fma(c, sc, zr);   // one rounding
+      v[2 * j] = z2[0];
+      v[2 * j + 1] = z2[1];
+    }
+    bz[kb] = v;
+  }
+  const uint32_t rws[4] = {t.rope.x, t.rope.y, t.rope.z, t.rope.w};
+  f16x8 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = static_cast<f16>(__uint_as_float(rws[j] << 16));
+    v[2 * j + 1] = static_cast<f16>(__uint_as_float(rws[j] & 0xffff0000u));
+  }
+  bz[8] = v;
+}
+
 template <int G>
 __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int rb_count, int n_logical) {
   __shared__ Smem sm;
@@ -127,6 +178,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   const int M = H * a.Tq;
   const int L = a.seq_len[it.b];
   const int64_t base = a.seq_base[it.b];
+  const int n_tiles = (it.t1 - it.t0 + TT - 1) / TT;
 
   // ---- Q~ operands (packed by the absorb kernel in exactly this order) ----
   f16x8 aq[2][KB];
@@ -146,6 +198,8 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   const int s_m = rb * ROWS + s_row;
   int s_vis = -1;  // padding rows are never visible
   if (s_m < M) s_vis = a.causal ? (L - a.Tq + s_m / H + 1) : L;
+  const int s_lim = min(it.t1, s_vis);   // tokens < s_lim are visible to this row
+  const int s_off = 36 * s_hf + 8 * s_k8;
   float m_run = -INFINITY, l_run = 0.0f;
 
   f32x16 o[2][4];
@@ -154,138 +208,131 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x16{};
 
+  uint32_t mask2 = 0x00030003u;
+  asm volatile("" : "+v"(mask2));  // keep the mask in a VGPR: one v_and_or_b32 per pair
   const f16x2 k1024 = {static_cast<f16>(-1024.0f), static_cast<f16>(-1024.0f)};
   const int g16 = l >> 4, s16 = l & 15;
-  f16 *zt_w = sm.z[w] + l32 * ZSTRIDE + 64 * hf;
+  const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);    // transposing-load source row
+  const int pv_col = 16 * (g16 & 1) + 4 * (s16 & 3);  // and column
+  auto tile_slot = [&](int i) -> int64_t {
+    const int ti = min(i, n_tiles - 1);
+    return base + min(it.t0 + ti * TT + l32, it.t1 - 1);
+  };
 
-  RawTile cur = load_tile<G>(a, base + min(it.t0 + l32, it.t1 - 1), w, hf);
-  for (int t0 = it.t0; t0 < it.t1; t0 += TT) {
-    // ---- 0. prefetch the next tile (clamped in-bounds; unused past the end) ----
-    const int tn = t0 + TT;
-    RawTile nxt = cur;
-    if (tn < it.t1) nxt = load_tile<G>(a, base + min(tn + l32, it.t1 - 1), w, hf);
+  // ---- prologue: scores of tile 0 in LDS, tile 1 dequantised, tile 2 in flight ----
+  f16x8 bz[KB];
+  f32x16 sacc[2];
+  {
+    const RawTile r0 = load_tile<G>(a, tile_slot(0), w, hf);
+    const RawTile r1 = load_tile<G>(a, tile_slot(1), w, hf);
+    dequant<G>(r0, bz, mask2, k1024);
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
+    f16 *zt = sm.z[0][w] + l32 * ZSTRIDE + 64 * hf;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = bz[kb];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sm.sp[0][w][mt * 16 + v][l + 4 * hf] = sacc[mt][v];
+    dequant<G>(r1, bz, mask2, k1024);
+  }
+  RawTile raw = load_tile<G>(a, tile_slot(2), w, hf);
+  lds_barrier();
 
-    // ---- 1. dequantise this lane's token into the score B operands ----
-    f16x8 bz[KB];
-    const uint32_t cws[4] = {cur.codes.x, cur.codes.y, cur.codes.z, cur.codes.w};
-    const uint32_t szw[4] = {cur.sz.x, cur.sz.y, cur.sz.z, cur.sz.w};
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      const int q = kb >> 1;                       // dword: channels 16q..16q+15
-      const uint32_t sz = szw[(G == 32) ? (q >> 1) : q];
-      const f16x2 sc = __builtin_bit_cast(f16x2, (sz & 0xffffu) * 0x10001u);
-      const f16x2 zr = __builtin_bit_cast(f16x2, (sz >> 16) * 0x10001u);
-      f16x8 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t x = ((cws[q] >> (2 * (4 * (kb & 1) + j))) & 0x00030003u) | 0x64006400u;
-        const f16x2 c = __builtin_bit_cast(f16x2, x) + k1024;     // exact small integers
-        const f16x2 z2 = __builtin_elementwise_fma(c, sc, zr);   // one rounding
-        v[2 * j] = z2[0];
-        v[2 * j + 1] = z2[1];
-      }
-      bz[kb] = v;
-    }
-    {
-      const uint32_t rws[4] = {cur.rope.x, cur.rope.y, cur.rope.z, cur.rope.w};
-      f16x8 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = static_cast<f16>(bf16_to_f32(static_cast<uint16_t>(rws[j] & 0xffffu)));
-        v[2 * j + 1] = static_cast<f16>(bf16_to_f32(static_cast<uint16_t>(rws[j] >> 16)));
-      }
-      bz[8] = v;
-    }
-
-    // ---- 2. partial scores ----
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  for (int i = 0; i < n_tiles; ++i) {
+    const int buf = i & 1, nb = buf ^ 1;
+    // ---- (a) scores of tile i+1 on MFMA (harmless recompute past the end) ----
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
 
-    // latent tile to LDS (wave-private), row = token, slots 64hf + 8kb + e
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt_w + 8 * kb) = bz[kb];
-    // partial scores to LDS: slot-major, lanes contiguous per half
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sm.sp[w][mt * 16 + v][l + 4 * hf] = sacc[mt][v];
-    lds_barrier();
-
-    // ---- 3. reduce partials + online softmax: one row x 8 tokens per lane ----
+    // ---- (b) online softmax of tile i (vector ALU, overlaps the MFMAs) ----
     float s[8];
-    {
-      const int off = 32 * s_hf + 4 * s_hf + 8 * s_k8;
 #pragma unroll
-      for (int e = 0; e < 8; e += 4) {
-        f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[0][s_rho][off + e]);
+    for (int e = 0; e < 8; e += 4) {
+      f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[buf][0][s_rho][s_off + e]);
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[ww][s_rho][off + e]);
-        s[e] = acc4[0];
-        s[e + 1] = acc4[1];
-        s[e + 2] = acc4[2];
-        s[e + 3] = acc4[3];
-      }
+      for (int ww = 1; ww < 4; ++ww) acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[buf][ww][s_rho][s_off + e]);
+      s[e] = acc4[0];
+      s[e + 1] = acc4[1];
+      s[e + 2] = acc4[2];
+      s[e + 3] = acc4[3];
     }
-    const int tau0 = t0 + 8 * s_k8;
-    const int lim = min(it.t1, s_vis);  // tokens < lim are visible to this row
+    const int ncnt = s_lim - (it.t0 + i * TT + 8 * s_k8);  // visible tokens among my 8
     float tmax = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (tau0 + e >= lim) s[e] = -INFINITY;
+      s[e] = (e < ncnt) ? s[e] : -INFINITY;
       tmax = fmaxf(tmax, s[e]);
     }
     tmax = reduce4<true>(tmax);
-    float alpha = 1.0f;
-    bool rescaled = false;
-    if (tmax > m_run + kRescaleThreshold) {  // also true for the first visible tile
-      alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - tmax);
-      m_run = tmax;
-      rescaled = true;
-    }
+    const bool need = tmax > m_run + kRescaleThreshold;   // true on the first visible tile
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
+    m_run = need ? tmax : m_run;
+    const float m_sub = (m_run == -INFINITY) ? 0.0f : m_run;
     float psum = 0.0f;
     f16x8 pv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = (s[e] == -INFINITY) ? 0.0f : exp2f(s[e] - m_run);
+      const float p = __builtin_amdgcn_exp2f(s[e] - m_sub);  // masked: exp2(-inf) = 0
       psum += p;
       pv[e] = static_cast<f16>(p);
     }
     psum = reduce4<false>(psum);
     l_run = l_run * alpha + psum;
-    *reinterpret_cast<f16x8 *>(sm.p + s_row * PRSTRIDE + 8 * s_k8) = pv;
-    if (s_k8 == 0) sm.alpha[s_row] = alpha;
-    const int any_w = __any(rescaled ? 1 : 0);
-    if (l == 0) sm.resc[w] = any_w;
-    lds_barrier();
-    const int rescale = sm.resc[0] | sm.resc[1] | sm.resc[2] | sm.resc[3];
+    *reinterpret_cast<f16x8 *>(sm.p[buf] + s_row * PRSTRIDE + 8 * s_k8) = pv;
+    if (s_k8 == 0) sm.alpha[buf][s_row] = alpha;
+    const int any_w = __any(need ? 1 : 0);
+    if (l == 0) sm.resc[buf][w] = any_w;
 
-    // ---- 4. O = alpha * O + P Z ----
+    // ---- (c) publish tile i+1: latent tile and partial scores ----
+    {
+      f16 *zt = sm.z[nb][w] + l32 * ZSTRIDE + 64 * hf;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = bz[kb];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sm.sp[nb][w][mt * 16 + v][l + 4 * hf] = sacc[mt][v];
+    }
+    lds_barrier();
+
+    // ---- (d) O = alpha * O + P Z for tile i ----
+    const int rescale = sm.resc[buf][0] | sm.resc[buf][1] | sm.resc[buf][2] | sm.resc[buf][3];
     if (rescale) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float al = sm.alpha[32 * mt + 8 * (v >> 2) + 4 * hf + (v & 3)];
+          const float al = sm.alpha[buf][32 * mt + 8 * (v >> 2) + 4 * hf + (v & 3)];
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) o[mt][nt][v] *= al;
+          for (int nt = 0; nt < 4; ++nt) {
+            float x = o[mt][nt][v];
+            agpr_scale(x, al);
+            o[mt][nt][v] = x;
+          }
         }
     }
+    const f16 *zb_base = sm.z[buf][w] + pv_krow * ZSTRIDE + pv_col;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       f16x8 pa[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
-      // transposing loads: source lane reads 4 slots of token krow
-      const int krow = 16 * ks + 8 * (g16 >> 1) + (s16 >> 2);
-      const int col = 16 * (g16 & 1) + 4 * (s16 & 3);
+        pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p[buf] + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const f16 *z0 = sm.z[w] + krow * ZSTRIDE + 32 * nt + col;
+        const f16 *z0 = zb_base + 16 * ks * ZSTRIDE + 32 * nt;
         const f16x4 lo = ds_read_tr16(z0);
         const f16x4 hi = ds_read_tr16(z0 + 4 * ZSTRIDE);
         const f16x8 zb = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -294,7 +341,9 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
           o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[mt], zb, o[mt][nt], 0, 0, 0);
       }
     }
-    cur = nxt;
+    // ---- (e) dequantise tile i+2 (overlaps the PV MFMAs), prefetch tile i+3 ----
+    dequant<G>(raw, bz, mask2, k1024);
+    raw = load_tile<G>(a, tile_slot(i + 3), w, hf);
   }
 
   // ---- write the partial (O, m, l) of this work item ----
