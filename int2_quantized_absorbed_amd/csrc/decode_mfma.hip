@@ -219,9 +219,28 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     return base + min(it.t0 + ti * TT + l32, it.t1 - 1);
   };
 
-  // ---- prologue: scores of tile 0 in LDS, tile 1 dequantised, tile 2 in flight ----
+  // ---- prologue: tile 0 scores summed in registers, tiles 0 and 1 in the
+  // Z buffers, tile 1 dequantised, tile 2 in flight ----
   f16x8 bz[KB];
   f32x16 sacc[2];
+  auto store_z = [&](int zb, const f16x8 (&v)[KB]) {
+    f16 *zt = sm.z[zb][w] + l32 * ZSTRIDE + 64 * hf;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = v[kb];
+  };
+  auto read_scores = [&](int sb, float (&s8)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 4) {
+      f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[sb][0][s_rho][s_off + e]);
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[sb][ww][s_rho][s_off + e]);
+      s8[e] = acc4[0];
+      s8[e + 1] = acc4[1];
+      s8[e + 2] = acc4[2];
+      s8[e + 3] = acc4[3];
+    }
+  };
+  float s_next[8];
   {
     const RawTile r0 = load_tile<G>(a, tile_slot(0), w, hf);
     const RawTile r1 = load_tile<G>(a, tile_slot(1), w, hf);
@@ -233,17 +252,17 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
-    f16 *zt = sm.z[0][w] + l32 * ZSTRIDE + 64 * hf;
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = bz[kb];
+    store_z(0, bz);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sm.sp[0][w][mt * 16 + v][l + 4 * hf] = sacc[mt][v];
     dequant<G>(r1, bz, mask2, k1024);
+    store_z(1, bz);
   }
   RawTile raw = load_tile<G>(a, tile_slot(2), w, hf);
   lds_barrier();
+  read_scores(0, s_next);
 
   for (int i = 0; i < n_tiles; ++i) {
     const int buf = i & 1, nb = buf ^ 1;
@@ -259,15 +278,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     // ---- (b) online softmax of tile i (vector ALU, overlaps the MFMAs) ----
     float s[8];
 #pragma unroll
-    for (int e = 0; e < 8; e += 4) {
-      f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[buf][0][s_rho][s_off + e]);
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[buf][ww][s_rho][s_off + e]);
-      s[e] = acc4[0];
-      s[e + 1] = acc4[1];
-      s[e + 2] = acc4[2];
-      s[e + 3] = acc4[3];
-    }
+    for (int e = 0; e < 8; ++e) s[e] = s_next[e];
     const int ncnt = s_lim - (it.t0 + i * TT + 8 * s_k8);  // visible tokens among my 8
     float tmax = -INFINITY;
 #pragma unroll
@@ -295,11 +306,8 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     const int any_w = __any(need ? 1 : 0);
     if (l == 0) sm.resc[buf][w] = any_w;
 
-    // ---- (c) publish tile i+1: latent tile and partial scores ----
+    // ---- (c) publish the partial scores of tile i+1 ----
     {
-      f16 *zt = sm.z[nb][w] + l32 * ZSTRIDE + 64 * hf;
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = bz[kb];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -341,9 +349,13 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
           o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[mt], zb, o[mt][nt], 0, 0, 0);
       }
     }
-    // ---- (e) dequantise tile i+2 (overlaps the PV MFMAs), prefetch tile i+3 ----
+    // ---- (e) dequantise tile i+2 into the Z buffer tile i just used (this
+    // wave's own region: its PV reads above were issued first), prefetch
+    // tile i+3 and the summed partial scores of tile i+1 ----
     dequant<G>(raw, bz, mask2, k1024);
+    store_z(buf, bz);
     raw = load_tile<G>(a, tile_slot(i + 3), w, hf);
+    read_scores(nb, s_next);
   }
 
   // ---- write the partial (O, m, l) of this work item ----
