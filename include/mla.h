@@ -241,7 +241,9 @@ mla_status mla_set_decode_variant(int32_t variant);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around
  * every kernel the library enqueues while enabled.  Names: "append_quant",
- * "decode_plan", "absorb_q", "splitk_decode", "combine", "up_proj",
+ * "decode_plan", "absorb_q" (on the MFMA path this kernel also plans the
+ * split-K work, and "decode_plan" is not launched), "splitk_decode",
+ * "combine", "up_proj",
  * "fold_weights", "prepare_rotation", "covariance", "clip_fit".
  * mla_timing_query waits for the recorded events and returns the summed
  * milliseconds and launch count since the last reset.  Process-wide; not

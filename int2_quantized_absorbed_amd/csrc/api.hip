@@ -464,8 +464,9 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
   a.target_items = target_items(M, batch, use_mfma);
   a.tile = use_mfma ? 32 : 16;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_plan(a, s);
-  if (e == hipSuccess) e = use_mfma ? launch_absorb_mfma_layout(a, s) : launch_absorb_f32(a, s);
+  // the MFMA absorb kernel also runs the planner
+  hipError_t e = use_mfma ? launch_absorb_mfma_layout(a, s) : launch_plan(a, s);
+  if (e == hipSuccess && !use_mfma) e = launch_absorb_f32(a, s);
   if (e == hipSuccess) e = use_mfma ? launch_splitk_mfma(a, s) : launch_splitk_valu(a, s);
   if (e == hipSuccess) e = launch_combine(a, s);
   if (e == hipSuccess) e = launch_upproj(a, s);

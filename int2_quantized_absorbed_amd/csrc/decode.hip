@@ -12,83 +12,18 @@
 // Scores are kept in log2 units (q~ and q_rope pre-multiplied by
 // scale * log2 e) so the softmax uses exp2.
 #include "kernels.hpp"
+#include "plan.hpp"
 
 namespace mla {
+
 namespace {
 
-// Token-balanced split-K plan from device seq_len (no host synchronisation).
-// Chunk length C = round_up(ceil(total / target), tile); sequence b gets
-// ceil(L_b / C) items of equal length (rounded up to the tile).  The item
-// count is then at most target + B = max_items.
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ seq_len, int B,
                                                    int target, int tile, int max_items,
                                                    WorkItem *__restrict__ items,
                                                    int32_t *__restrict__ item_begin,
                                                    int32_t *__restrict__ meta) {
-  __shared__ long long red[256];
-  __shared__ int32_t scan[256];
-  __shared__ int32_t carry_s;
-  const int tid = threadIdx.x;
-  long long tot = 0;
-  for (int b = tid; b < B; b += 256) tot += max(0, seq_len[b]);
-  red[tid] = tot;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  const long long total = red[0];
-  long long C = (total + target - 1) / max(target, 1);
-  C = ((C + tile - 1) / tile) * tile;
-  if (C < tile) C = tile;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += 256) {
-    const int b = base + tid;
-    int nb = 0, chunk = 0, L = 0;
-    if (b < B) {
-      L = seq_len[b];
-      if (L > 0) {
-        nb = static_cast<int>((L + C - 1) / C);
-        chunk = (L + nb - 1) / nb;
-        chunk = ((chunk + tile - 1) / tile) * tile;
-        nb = (L + chunk - 1) / chunk;
-      }
-    }
-    scan[tid] = nb;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int v = (tid >= off) ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int carry = carry_s;
-    const int excl = carry + scan[tid] - nb;
-    if (b < B) {
-      item_begin[b] = min(excl, max_items);
-      for (int c = 0; c < nb; ++c) {
-        const int idx = excl + c;
-        if (idx < max_items) {
-          WorkItem it;
-          it.b = b;
-          it.t0 = c * chunk;
-          it.t1 = min(L, (c + 1) * chunk);
-          it.pad = 0;
-          items[idx] = it;
-        }
-      }
-    }
-    __syncthreads();
-    if (tid == 255) carry_s = carry + scan[255];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const int n = min(carry_s, max_items);
-    item_begin[B] = n;
-    meta[0] = n;
-    meta[1] = static_cast<int32_t>(C);
-  }
+  plan_block(seq_len, B, target, tile, max_items, items, item_begin, meta);
 }
 
 // q~ in fp32, row-major [B*M][r + d_r] with M = Tq*H rows per sequence
@@ -253,75 +188,133 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
 
 // Log-sum-exp merge of the split-K partials of one query row (b, t, h):
 // m = max_i m_i, o_z = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i,
-// lse = ln 2 * (m + log2 sum_i 2^(m_i - m) l_i).  One block per row.
-__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+// lse = ln 2 * (m + log2 sum_i 2^(m_i - m) l_i).  One block per row; thread
+// -> (item slice s, 4-channel chunk c).  Slice s folds items ib + s,
+// ib + s + S, ... into a running (max, sum, O) U items per round (addresses
+// clamped and weights zeroed past the end, so the U loads are issued
+// together); the S slice results are then merged in slice order.
+template <int U>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  __shared__ f32x4 part[256];
+  __shared__ float part_m[256], part_l[256];
   const int H = a.d.num_heads, r = a.d.kv_lora_rank;
   const int M = H * a.Tq;
   const int row = blockIdx.x;               // (b*Tq + t)*H + h
   const int q = row / H, h = row % H;
   const int b = q / a.Tq, t = q % a.Tq, m = t * H + h;
   const int ib = a.item_begin[b], ie = a.item_begin[b + 1];
-  float mx = -INFINITY;
-  for (int i = ib; i < ie; ++i) mx = fmaxf(mx, a.part_ml[(static_cast<int64_t>(i) * M + m) * 2]);
-  float den = 0.0f;
-  if (mx != -INFINITY)
-    for (int i = ib; i < ie; ++i) {
-      const float mi = a.part_ml[(static_cast<int64_t>(i) * M + m) * 2];
-      if (mi != -INFINITY) den += exp2f(mi - mx) * a.part_ml[(static_cast<int64_t>(i) * M + m) * 2 + 1];
-    }
-  if (threadIdx.x == 0 && a.lse != nullptr) a.lse[row] = (den > 0.0f) ? (mx + log2f(den)) * kLn2 : -INFINITY;
-  const float inv = (den > 0.0f) ? 1.0f / den : 0.0f;
-  float *dst = a.oz + static_cast<int64_t>(row) * r;
-  for (int j = 4 * threadIdx.x; j < r; j += 4 * blockDim.x) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (den > 0.0f)
-      for (int i = ib; i < ie; ++i) {
-        const float mi = a.part_ml[(static_cast<int64_t>(i) * M + m) * 2];
-        if (mi == -INFINITY) continue;
-        const float wgt = exp2f(mi - mx);
-        acc += wgt * *reinterpret_cast<const f32x4 *>(a.part_o + (static_cast<int64_t>(i) * M + m) * r + j);
+  const int chunks = r >> 2, S = 256 / chunks;
+  const int tid = threadIdx.x, sl = tid / chunks, c = tid % chunks;
+  const float *ml = a.part_ml + static_cast<int64_t>(m) * 2;
+  const float *po = a.part_o + static_cast<int64_t>(m) * r + 4 * c;
+  const int64_t ml_stride = static_cast<int64_t>(M) * 2, po_stride = static_cast<int64_t>(M) * r;
+  float mrun = -INFINITY, lrun = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (sl < S) {
+    for (int k0 = ib + sl; k0 < ie; k0 += U * S) {
+      f32x4 v[U];
+      float2 st[U];
+#pragma unroll
+      for (int e = 0; e < U; ++e) {
+        const int k = min(k0 + e * S, ie - 1);
+        v[e] = *reinterpret_cast<const f32x4 *>(po + k * po_stride);
+        st[e] = *reinterpret_cast<const float2 *>(ml + k * ml_stride);
+        if (k0 + e * S >= ie) st[e].x = -INFINITY;
       }
-    *reinterpret_cast<f32x4 *>(dst + j) = acc * inv;
+      float rm = mrun;
+#pragma unroll
+      for (int e = 0; e < U; ++e) rm = fmaxf(rm, st[e].x);
+      if (rm != -INFINITY) {
+        const float sc = exp2f(mrun - rm);  // 0 while nothing was folded in
+        acc *= sc;
+        lrun *= sc;
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+          const float wgt = st[e].x == -INFINITY ? 0.0f : exp2f(st[e].x - rm);
+          acc += wgt * v[e];
+          lrun += wgt * st[e].y;
+        }
+        mrun = rm;
+      }
+    }
+  }
+  part[tid] = acc;
+  part_m[tid] = mrun;
+  part_l[tid] = lrun;
+  __syncthreads();
+  if (tid < chunks) {
+    float mx = -INFINITY;
+    for (int j = 0; j < S; ++j) mx = fmaxf(mx, part_m[j * chunks + c]);
+    float den = 0.0f;
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (mx != -INFINITY)
+      for (int j = 0; j < S; ++j) {
+        const float mj = part_m[j * chunks + c];
+        if (mj == -INFINITY) continue;
+        const float wgt = exp2f(mj - mx);
+        den += wgt * part_l[j * chunks + c];
+        o += wgt * part[j * chunks + c];
+      }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    *reinterpret_cast<f32x4 *>(a.oz + static_cast<int64_t>(row) * r + 4 * c) = o * inv;
+    if (tid == 0 && a.lse != nullptr) a.lse[row] = den > 0.0f ? (mx + log2f(den)) * kLn2 : -INFINITY;
   }
 }
 
 // out[b,t,h,:] = W~_UV[h] o_z[b,t,h,:] on MFMA (32x32x16 f16, fp32 acc).
 // o_z is split as hi + lo (two fp16 parts) so the product keeps ~fp32
-// precision of o_z; W~_UV is fp16.  Block = (head, 32 query rows); wave w
-// produces output columns [32w, 32w + 32) of each 128-wide slice.
+// precision of o_z; W~_UV is fp16.  Block = (head, 32 output columns, 32
+// query rows); wave w takes a quarter of the latent K-steps (all of its loads
+// are issued before the first product), and the four partial tiles are added
+// in LDS in a fixed order.
 __global__ __launch_bounds__(256) void upproj_mfma_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, rt = blockIdx.y;
+  __shared__ float red[4][16][64];
+  const int h = blockIdx.x, v0 = 32 * blockIdx.y, rt = blockIdx.z;
   const int H = a.d.num_heads, r = a.d.kv_lora_rank, dv = a.d.v_head_dim;
   const int nrows = a.B * a.Tq;
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, hf = l >> 5, l32 = l & 31;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, hf = l >> 5, l32 = l & 31;
   const int q = rt * 32 + l32;              // A-operand row of this lane
   const bool q_ok = q < nrows;
-  const float *arow = a.oz + (static_cast<int64_t>(q_ok ? q : 0) * H + h) * r;
-  for (int v0 = 32 * w; v0 < dv; v0 += 128) {
-    const uint16_t *brow = a.w_uv_f + (static_cast<int64_t>(h) * dv + v0 + l32) * r;
-    f32x16 acc = {};
-    for (int k0 = 0; k0 < r; k0 += 16) {
+  const float *arow = a.oz + (static_cast<int64_t>(q_ok ? q : 0) * H + h) * r + 8 * hf;
+  const uint16_t *brow = a.w_uv_f + (static_cast<int64_t>(h) * dv + v0 + l32) * r + 8 * hf;
+  const int nks = r >> 4, ks0 = (w * nks) >> 2, ks1 = ((w + 1) * nks) >> 2;
+  f32x16 acc = {};
+  for (int ks = ks0; ks < ks1; ks += 8) {
+    f32x4 x[8][2];
+    f16x8 bw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kk = min(ks + e, ks1 - 1) * 16;
+      x[e][0] = *reinterpret_cast<const f32x4 *>(arow + kk);  // row 0 stands in for q >= nrows
+      x[e][1] = *reinterpret_cast<const f32x4 *>(arow + kk + 4);
+      bw[e] = *reinterpret_cast<const f16x8 *>(brow + kk);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (ks + e >= ks1) break;
       f16x8 ahi, alo;
-      const f32x4 x0 = q_ok ? *reinterpret_cast<const f32x4 *>(arow + k0 + 8 * hf) : f32x4{};
-      const f32x4 x1 = q_ok ? *reinterpret_cast<const f32x4 *>(arow + k0 + 8 * hf + 4) : f32x4{};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16 h0 = static_cast<f16>(x0[e]), h1 = static_cast<f16>(x1[e]);
-        ahi[e] = h0;
-        ahi[e + 4] = h1;
-        alo[e] = static_cast<f16>(x0[e] - static_cast<float>(h0));
-        alo[e + 4] = static_cast<f16>(x1[e] - static_cast<float>(h1));
+      for (int j = 0; j < 8; ++j) {
+        const float xv = q_ok ? x[e][j >> 2][j & 3] : 0.0f;
+        const f16 hv = static_cast<f16>(xv);
+        ahi[j] = hv;
+        alo[j] = static_cast<f16>(xv - static_cast<float>(hv));
       }
-      const f16x8 bw = *reinterpret_cast<const f16x8 *>(brow + k0 + 8 * hf);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bw, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bw[e], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bw[e], acc, 0, 0, 0);
     }
-    // C layout: lane holds column v0 + l32, rows 8(v/4) + 4hf + v%4
+  }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int qq = rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-      if (qq < nrows) a.out[(static_cast<int64_t>(qq) * H + h) * dv + v0 + l32] = acc[v];
-    }
+  for (int v = 0; v < 16; ++v) red[w][v][l] = acc[v];
+  __syncthreads();
+  // C layout: lane holds column v0 + l32, rows 8(v/4) + 4hf + v%4
+  for (int e = tid; e < 16 * 64; e += 256) {
+    const int v = e >> 6, ln = e & 63;
+    const int qq = rt * 32 + 8 * (v >> 2) + 4 * (ln >> 5) + (v & 3);
+    if (qq < nrows)
+      a.out[(static_cast<int64_t>(qq) * H + h) * dv + v0 + (ln & 31)] =
+          ((red[0][v][ln] + red[1][v][ln]) + red[2][v][ln]) + red[3][v][ln];
   }
 }
 
@@ -382,7 +375,14 @@ hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s) {
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
   TimedLaunch tl("combine", s);
   const int rows = a.B * a.Tq * a.d.num_heads;
-  combine_kernel<<<rows, 128, 0, s>>>(a);
+  // items per sequence average (target + B) / B; rounds of 16 pay off once
+  // a slice sees more than one round of 8
+  const int per_seq = (a.target_items + a.B) / a.B;
+  const int S = 256 / (a.d.kv_lora_rank / 4);
+  if (per_seq > 8 * S)
+    combine_kernel<16><<<rows, 256, 0, s>>>(a);
+  else
+    combine_kernel<8><<<rows, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -390,7 +390,7 @@ hipError_t launch_upproj(const DecodeArgs &a, hipStream_t s) {
   TimedLaunch tl("up_proj", s);
   if (a.d.v_head_dim % 32 == 0) {
     const int nrows = a.B * a.Tq;
-    upproj_mfma_kernel<<<dim3(a.d.num_heads, (nrows + 31) / 32), 256, 0, s>>>(a);
+    upproj_mfma_kernel<<<dim3(a.d.num_heads, a.d.v_head_dim / 32, (nrows + 31) / 32), 256, 0, s>>>(a);
   } else {
     const int waves = a.d.num_heads * a.d.v_head_dim;
     upproj_valu_kernel<<<(waves + 3) / 4, 256, 0, s>>>(a);

@@ -26,6 +26,7 @@
 // 8 (log2 units); otherwise p = 2^(s - m) <= 256 stays exact enough in fp16
 // and O needs no rescaling.
 #include "kernels.hpp"
+#include "plan.hpp"
 
 namespace mla {
 namespace {
@@ -380,74 +381,97 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 // q~ = W~_UK[h]^T q_nope on MFMA (32x32x16 f16, fp32 acc), and q_rope; both
 // times scale*log2(e), written in fp16 straight into the per-lane operand
 // order of splitk_mfma_kernel: [b][row block][wave][mt][kb][lane][8], zero
-// for padding rows.  Block = (head, 32 query rows (b, t)); wave w computes
-// latent channels [128w, 128w + 128).  w_uk_f is stored [H][r][d_n].
-__device__ __forceinline__ int64_t qpos(int rb_count, int b, int m, int w, int hf, int kb, int e) {
+// for padding rows.  Block = (head, latent quarter = split-K wave slot,
+// 32 query rows (b, t)); wave w computes 32 channels.  The results are staged
+// in LDS so every operand unit (8 halves) is written with one 16-byte store.
+// Block (0, 0) also runs the split-K planner.  w_uk_f is stored [H][r][d_n].
+__device__ __forceinline__ int64_t qpos(int rb_count, int b, int m, int w, int hf, int kb) {
   const int rb = m / ROWS, mt = (m % ROWS) / 32, lane = (m % 32) + 32 * hf;
-  return ((((static_cast<int64_t>(b) * rb_count + rb) * 4 + w) * 2 + mt) * KB + kb) * 512 + lane * 8 + e;
+  return ((((static_cast<int64_t>(b) * rb_count + rb) * 4 + w) * 2 + mt) * KB + kb) * 512 + lane * 8;
 }
 
+constexpr int QTSTRIDE = 136;  // halves per staged row (128 channels + pad)
+
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_count) {
-  const int h = blockIdx.x, rt = blockIdx.y;
+  __shared__ __align__(16) f16 qt[32 * QTSTRIDE];
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    plan_block(a.seq_len, a.B, a.target_items, a.tile, a.max_items, a.items, a.item_begin, a.meta);
+  const int h = blockIdx.x >> 2, cq = blockIdx.x & 3, rt = blockIdx.y;
   const int H = a.d.num_heads, dn = a.d.qk_nope_head_dim;
   const int M = H * a.Tq;
   const int nrows = a.B * a.Tq;
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, hf = l >> 5, l32 = l & 31;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, hf = l >> 5, l32 = l & 31;
   f16 *qb = static_cast<f16 *>(a.qbuf);
   const int q = rt * 32 + l32;
   const bool q_ok = q < nrows;
   const uint16_t *arow = a.q_nope + (static_cast<int64_t>(q_ok ? q : 0) * H + h) * dn;
-  const uint16_t *wk = a.w_uk_f + static_cast<int64_t>(h) * R * dn;
-  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  for (int k0 = 0; k0 < dn; k0 += 16) {
-    const uint4 raw = q_ok ? *reinterpret_cast<const uint4 *>(arow + k0 + 8 * hf) : uint4{0, 0, 0, 0};
-    const uint32_t rr[4] = {raw.x, raw.y, raw.z, raw.w};
-    f16x8 av;
+  const int j = 128 * cq + 32 * w + l32;  // this lane's B column = latent channel
+  const uint16_t *brow = a.w_uk_f + (static_cast<int64_t>(h) * R + j) * dn;
+  f32x16 acc = {};
+  for (int k0 = 0; k0 < dn; k0 += 128) {
+    uint4 raw[8];
+    f16x8 bv[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      av[2 * j] = static_cast<f16>(bf16_to_f32(static_cast<uint16_t>(rr[j] & 0xffffu)));
-      av[2 * j + 1] = static_cast<f16>(bf16_to_f32(static_cast<uint16_t>(rr[j] >> 16)));
+    for (int e = 0; e < 8; ++e) {
+      const int kk = min(k0 + 16 * e, dn - 16) + 8 * hf;
+      raw[e] = *reinterpret_cast<const uint4 *>(arow + kk);  // row 0 stands in for q >= nrows
+      bv[e] = *reinterpret_cast<const f16x8 *>(brow + kk);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int j = 128 * w + 32 * nt + l32;
-      const f16x8 bv = *reinterpret_cast<const f16x8 *>(wk + static_cast<int64_t>(j) * dn + k0 + 8 * hf);
-      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[nt], 0, 0, 0);
-    }
-  }
+    for (int e = 0; e < 8; ++e) {
+      if (k0 + 16 * e >= dn) break;
+      const uint32_t rr[4] = {raw[e].x, raw[e].y, raw[e].z, raw[e].w};
+      f16x8 av;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    // inverse of slot_channel for latent channel j = 128w + jj
-    const int jj = 32 * nt + l32, shf = jj >> 6, r6 = jj & 63;
-    const int qd = r6 >> 4, idx = r6 & 15, i8 = idx >> 3, rem = idx & 7;
-    const int kb = 2 * qd + (rem >> 2), e = 2 * (rem & 3) + i8;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int qq = rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-      if (qq < nrows) {
-        const int b = qq / a.Tq, t = qq % a.Tq, m = t * H + h;
-        qb[qpos(rb_count, b, m, w, shf, kb, e)] = static_cast<f16>(acc[nt][v] * a.scale_log2);
+      for (int j = 0; j < 4; ++j) {
+        av[2 * j] = q_ok ? static_cast<f16>(__uint_as_float(rr[j] << 16)) : f16(0.0f);
+        av[2 * j + 1] = q_ok ? static_cast<f16>(__uint_as_float(rr[j] & 0xffff0000u)) : f16(0.0f);
       }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[e], acc, 0, 0, 0);
     }
   }
-  for (int e = threadIdx.x; e < 32 * DR; e += 256) {
-    const int i = e / DR, k = e % DR, qq = rt * 32 + i;
+  // C layout: column = channel 32w + l32 of the quarter, rows 8(v/4) + 4hf + v%4
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    qt[(8 * (v >> 2) + 4 * hf + (v & 3)) * QTSTRIDE + 32 * w + l32] = static_cast<f16>(acc[v] * a.scale_log2);
+  __syncthreads();
+  // operand units: (row i, lane half uh, K-block kb) -> 8 channels slot_channel(uh, kb, e)
+  for (int u = tid; u < 32 * 16; u += 256) {
+    const int i = u >> 4, uh = (u >> 3) & 1, kb = u & 7;
+    const int qq = rt * 32 + i;
+    if (qq >= nrows) continue;
+    f16x8 v8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v8[e] = qt[i * QTSTRIDE + slot_channel(uh, kb, e)];
+    const int b = qq / a.Tq, t = qq % a.Tq, m = t * H + h;
+    *reinterpret_cast<f16x8 *>(qb + qpos(rb_count, b, m, cq, uh, kb)) = v8;
+  }
+  // rope units: dims 16cq + 8uh + e
+  if (tid < 64) {
+    const int i = tid >> 1, uh = tid & 1, qq = rt * 32 + i;
     if (qq < nrows) {
+      const uint4 raw = *reinterpret_cast<const uint4 *>(a.q_rope + (static_cast<int64_t>(qq) * H + h) * DR + 16 * cq + 8 * uh);
+      const uint32_t rr[4] = {raw.x, raw.y, raw.z, raw.w};
+      f16x8 v8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v8[2 * e] = static_cast<f16>(__uint_as_float(rr[e] << 16) * a.scale_log2);
+        v8[2 * e + 1] = static_cast<f16>(__uint_as_float(rr[e] & 0xffff0000u) * a.scale_log2);
+      }
       const int b = qq / a.Tq, t = qq % a.Tq, m = t * H + h;
-      const float v = bf16_to_f32(a.q_rope[(static_cast<int64_t>(qq) * H + h) * DR + k]) * a.scale_log2;
-      qb[qpos(rb_count, b, m, k >> 4, (k >> 3) & 1, 8, k & 7)] = static_cast<f16>(v);
+      *reinterpret_cast<f16x8 *>(qb + qpos(rb_count, b, m, cq, uh, 8)) = v8;
     }
   }
-  // zero the padding rows of the last row block (one block does it)
+  // zero the padding rows of the last row block for this wave slot
   if (h == 0 && rt == 0 && M % ROWS != 0) {
     const int pad = rb_count * ROWS - M;
-    for (int b = 0; b < a.B; ++b)
-      for (int e = threadIdx.x; e < pad * 4 * KB * 16; e += 256) {
-        const int m = M + e / (4 * KB * 16);
-        const int rest = e % (4 * KB * 16);
-        const int ww = rest / (KB * 16), kb = (rest / 16) % KB, hfe = rest % 16;
-        qb[qpos(rb_count, b, m, ww, hfe >> 3, kb, hfe & 7)] = static_cast<f16>(0.0f);
-      }
+    const f16x8 z8 = {};
+    for (int e = tid; e < a.B * pad * 2 * KB; e += 256) {
+      const int b = e / (pad * 2 * KB), rest = e % (pad * 2 * KB);
+      const int m = M + rest / (2 * KB), uh = (rest / KB) & 1, kb = rest % KB;
+      *reinterpret_cast<f16x8 *>(qb + qpos(rb_count, b, m, cq, uh, kb)) = z8;
+    }
   }
 }
 
@@ -467,7 +491,7 @@ hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s) {
   const int M = a.d.num_heads * a.Tq;
   const int rb_count = (M + ROWS - 1) / ROWS;
   const int nrows = a.B * a.Tq;
-  absorb_mfma_kernel<<<dim3(a.d.num_heads, (nrows + 31) / 32), 256, 0, s>>>(a, rb_count);
+  absorb_mfma_kernel<<<dim3(a.d.num_heads * 4, (nrows + 31) / 32), 256, 0, s>>>(a, rb_count);
   return hipGetLastError();
 }
 

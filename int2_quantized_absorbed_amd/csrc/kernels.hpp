@@ -58,6 +58,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_plan(const DecodeArgs &a, hipStream_t s);
+
 hipError_t launch_absorb_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s);
