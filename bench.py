@@ -56,7 +56,24 @@ def parse():
     ap.add_argument("--copies", type=int, default=8, help="cache copies used in turn")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (for scaling the HBM "
+                         "byte counters of a profiler run) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    """A plain device-to-device copy of known size: a profiler's FETCH_SIZE /
+    WRITE_SIZE for it should read mib MiB each per dispatch."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "dispatches": 3}))
 
 
 def algorithmic_flops(w, lens) -> float:
@@ -76,6 +93,9 @@ def cache_bytes_per_token(w) -> int:
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this path is built and "
               "measured on one MI355X; sharding over GPUs is not part of this build.", file=sys.stderr)
