@@ -49,6 +49,42 @@ __device__ __forceinline__ double latent_f64<uint16_t>(const uint16_t *p, int64_
   return static_cast<double>(bf16_to_f32(p[i]));
 }
 
+// Copy the bf16 side keys (width values each) of tokens [t0, t0 + cnt) into
+// their cache slots, one wave, all lanes moving 16-byte pieces (4-byte pieces
+// when width is not a multiple of 8); slots outside the cache are skipped.
+__device__ __forceinline__ void copy_side_keys(uint16_t *__restrict__ dst, const uint16_t *__restrict__ src,
+                                               int width, const int64_t *__restrict__ slots, int64_t t0,
+                                               int cnt, int64_t capacity, int lane) {
+  if ((width & 7) == 0) {
+    const int per = width / 8, total = cnt * per;
+    for (int e0 = lane; e0 < total; e0 += 64 * 4) {
+      uint4 v[4];
+      int64_t sl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = min(e0 + 64 * j, total - 1), t = e / per;
+        sl[j] = slots[t0 + t];
+        v[j] = reinterpret_cast<const uint4 *>(src + (t0 + t) * width)[e % per];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 64 * j;
+        if (e < total && sl[j] >= 0 && sl[j] < capacity)
+          reinterpret_cast<uint4 *>(dst + sl[j] * width)[e % per] = v[j];
+      }
+    }
+  } else {
+    const int per = width / 2, total = cnt * per;
+    for (int e = lane; e < total; e += 64) {
+      const int t = e / per;
+      const int64_t sl = slots[t0 + t];
+      if (sl >= 0 && sl < capacity)
+        reinterpret_cast<uint32_t *>(dst + sl * width)[e % per] =
+            reinterpret_cast<const uint32_t *>(src + (t0 + t) * width)[e % per];
+    }
+  }
+}
+
 struct AppendParams {
   const void *latent;
   const uint16_t *k_rope;
@@ -134,15 +170,6 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, hf = l >> 5, l32 = l & 31;
 
-  // stage R_apply^T rows [cs*128, +128) into LDS (16-byte chunks)
-  {
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.Rt + static_cast<int64_t>(cs) * kSlice * R);
-    constexpr int CPR = R / 8;  // chunks per row
-    for (int e = tid; e < kSlice * CPR; e += 256) {
-      const int row = e / CPR, c = e % CPR;
-      *reinterpret_cast<uint4 *>(rt_s + row * LS + c * 8) = src[row * CPR + c];
-    }
-  }
   const uint16_t *lat = static_cast<const uint16_t *>(p.latent);
   int64_t tok[2];
   bool valid[2];
@@ -153,7 +180,24 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
     valid[nt] = tok[nt] < p.n;
     brow[nt] = reinterpret_cast<const bf16x8 *>(lat + (valid[nt] ? tok[nt] : 0) * R);
   }
-  __syncthreads();
+  // epilogue inputs, fetched now so their latency hides under the GEMM
+  constexpr int NGT = 32 / G;  // groups per M-tile: 1 (G=32) or 2 (G=16)
+  int64_t slot_of[2] = {-1, -1};
+  if (p.z_out == nullptr) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      if (valid[nt]) slot_of[nt] = p.slots[tok[nt]];
+  }
+  // (the rotation-only launch, z_out != nullptr, has no alpha)
+  float alpha_of[4][NGT] = {};
+  if (p.z_out == nullptr) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int g = 0; g < NGT; ++g) alpha_of[mt][g] = p.alpha[(cs * kSlice + mt * 32) / G + g];
+  }
+  // a wave whose 64 tokens all lie past the end skips the products
+  const bool live = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave < p.n;
 
   f32x16 acc[NACC][4][2];
 #pragma unroll
@@ -163,36 +207,68 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[a][mt][nt] = f32x16{};
 
+  // latent operands stream from HBM in chunks of PD K-steps, double-buffered:
+  // chunk c + 1 is in flight while chunk c is multiplied
+  constexpr int PD = 8;
+  static_assert(KS % PD == 0, "K-steps come in whole chunks");
   const bf16x8 zero8 = {};
-  bf16x8 bcur[2], bnext[2];
+  bf16x8 bq[2][PD][2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) bcur[nt] = valid[nt] ? brow[nt][hf] : zero8;
-#pragma unroll 2
-  for (int ks = 0; ks < KS; ++ks) {
-    if (ks + 1 < KS) {
+  for (int j = 0; j < PD; ++j)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) bnext[nt] = valid[nt] ? brow[nt][2 * (ks + 1) + hf] : zero8;
+    for (int nt = 0; nt < 2; ++nt) bq[0][j][nt] = valid[nt] ? brow[nt][2 * j + hf] : zero8;
+  // stage R_apply^T rows [cs*128, +128) into LDS (16-byte chunks, 16 (or 8)
+  // loads in flight per thread) while the first latent chunk is in flight
+  {
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.Rt + static_cast<int64_t>(cs) * kSlice * R);
+    constexpr int CPR = R / 8;  // chunks per row
+    constexpr int TOTAL = kSlice * CPR;
+    constexpr int SU = TOTAL % (256 * 16) == 0 ? 16 : 8;
+    static_assert(TOTAL % (256 * SU) == 0, "staging loop has no tail");
+    for (int e0 = tid; e0 < TOTAL; e0 += 256 * SU) {
+      uint4 v[SU];
+#pragma unroll
+      for (int j = 0; j < SU; ++j) v[j] = src[e0 + 256 * j];
+#pragma unroll
+      for (int j = 0; j < SU; ++j) {
+        const int e = e0 + 256 * j, row = e / CPR, c = e % CPR;
+        *reinterpret_cast<uint4 *>(rt_s + row * LS + c * 8) = v[j];
+      }
     }
-    bf16x8 a[4];
+  }
+  __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      a[mt] = *reinterpret_cast<const bf16x8 *>(rt_s + (mt * 32 + l32) * LS + ks * 16 + hf * 8);
-    const int par = ks % NACC;
+  for (int c = 0; c < KS / PD; ++c) {
+    if (!live) break;
+    const int cur = c & 1;
+    if (c + 1 < KS / PD) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int j = 0; j < PD; ++j)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        acc[par][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], bcur[nt], acc[par][mt][nt], 0, 0, 0);
+        for (int nt = 0; nt < 2; ++nt)
+          bq[cur ^ 1][j][nt] = valid[nt] ? brow[nt][2 * ((c + 1) * PD + j) + hf] : zero8;
+    }
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) bcur[nt] = bnext[nt];
+    for (int j = 0; j < PD; ++j) {
+      const int ks = c * PD + j;
+      bf16x8 a[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        a[mt] = *reinterpret_cast<const bf16x8 *>(rt_s + (mt * 32 + l32) * LS + ks * 16 + hf * 8);
+      const int par = ks % NACC;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[par][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], bq[cur][j][nt], acc[par][mt][nt], 0, 0, 0);
+    }
   }
 
   // epilogue: lane holds channels 32mt + 8q + 4hf + s (v = 4q + s) of token tok[nt]
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const bool ok = valid[nt];
-    int64_t slot = -1;
-    if (ok && p.z_out == nullptr) slot = p.slots[tok[nt]];
+    const int64_t slot = slot_of[nt];
     const bool write = ok && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -210,7 +286,6 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
         continue;
       }
       // group statistics (exchange with the partner lane l ^ 32, same token)
-      constexpr int NGT = 32 / G;  // groups per M-tile: 1 (G=32) or 2 (G=16)
       constexpr int VPG = 16 / NGT;  // values per lane per group
       QuantParams qp[NGT];
 #pragma unroll
@@ -223,15 +298,29 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         mn = fminf(mn, __shfl_xor(mn, 32));
-        qp[g] = quant_params(mx, mn, p.alpha[ch0 / G + g]);
+        qp[g] = quant_params(mx, mn, alpha_of[mt][g]);
+      }
+      // quotient estimates for all 16 values; the exact division runs only
+      // when some value of the wave lies next to a code boundary
+      float xs[16], us[16];
+      bool near = false;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const QuantParams &qq = qp[v / VPG];
+        xs[v] = __fsub_rn(z[v], qq.zero_f);
+        us[v] = quant_u_estimate(xs[v], qq);
+        near |= qq.scale_f != 0.0f && quant_u_near_boundary(us[v]);
+      }
+      if (near) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (quant_u_near_boundary(us[v])) us[v] = __fdiv_rn(xs[v], qp[v / VPG].scale_f);
       }
       uint32_t dword = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t byte = 0;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) byte |= quant_code(z[4 * q + s], qp[(4 * q) / VPG]) << (2 * s);
-        dword |= byte << (8 * q);
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t code = qp[v / VPG].scale_f == 0.0f ? 0u : quant_code_from_u(us[v]);
+        dword |= code << (2 * v);
       }
       // lane hf=0 holds bytes 0,2,4,6 of the tile's 8 code bytes, hf=1 holds 1,3,5,7
       const uint32_t partner = __shfl_xor(dword, 32);
@@ -252,17 +341,19 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
         }
       }
     }
-    // side keys: the first channel slice copies them, one wave per token row
-    if (cs == 0 && p.z_out == nullptr) {
-      // each lane of the wave handles tokens of its own 64-token range in turn
-      for (int t = 0; t < 32; ++t) {
-        const int64_t tk = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave + nt * 32 + t;
-        if (tk >= p.n) break;
-        const int64_t sl = p.slots[tk];
-        if (sl < 0 || sl >= p.cache.capacity) continue;
-        copy_key(p.cache.k_rope + sl * p.d_r, p.k_rope + tk * p.d_r, p.d_r, l, 64);
-        if (p.d_idx > 0) copy_key(p.cache.idx_key + sl * p.d_idx, p.idx_key + tk * p.d_idx, p.d_idx, l, 64);
-      }
+  }
+  // side keys: channel-slice block cs copies its share of this 256-token
+  // tile (ceil(256 / NSLICE) tokens), a quarter of that per wave, every lane
+  // moving 16-byte pieces
+  if (p.z_out == nullptr) {
+    constexpr int PB = (kTokPerBlock + NSLICE - 1) / NSLICE, PW = (PB + 3) / 4;
+    const int64_t tile_end = min<int64_t>(static_cast<int64_t>(tb + 1) * kTokPerBlock, p.n);
+    const int64_t t0 = static_cast<int64_t>(tb) * kTokPerBlock + cs * PB + w * PW;
+    const int64_t t1 = min<int64_t>(min<int64_t>(t0 + PW, static_cast<int64_t>(tb) * kTokPerBlock + (cs + 1) * PB), tile_end);
+    const int cnt = static_cast<int>(t1 - t0);
+    if (cnt > 0) {
+      copy_side_keys(p.cache.k_rope, p.k_rope, p.d_r, p.slots, t0, cnt, p.cache.capacity, l);
+      if (p.d_idx > 0) copy_side_keys(p.cache.idx_key, p.idx_key, p.d_idx, p.slots, t0, cnt, p.cache.capacity, l);
     }
   }
 }

@@ -61,6 +61,7 @@ struct QuantParams {
   f16 zero;
   float scale_f;  // f32(scale)
   float zero_f;   // f32(zero)
+  float rcp;      // approximate 1 / scale_f (hardware reciprocal, within 1 ulp)
 };
 
 __device__ __forceinline__ QuantParams quant_params(float mx, float mn, float alpha) {
@@ -75,15 +76,35 @@ __device__ __forceinline__ QuantParams quant_params(float mx, float mn, float al
   q.zero = f32_to_f16(lo);
   q.scale_f = static_cast<float>(q.scale);
   q.zero_f = static_cast<float>(q.zero);
+  q.rcp = __builtin_amdgcn_rcpf(q.scale_f);
   return q;
+}
+
+// code = clamp(rint(fl(x / scale)), 0, 3) with x = fl(z - zero) and fl()
+// IEEE round-to-nearest division.  The code only depends on which side of
+// the boundaries 0.5, 1.5, 2.5 the rounded quotient lies, so the quotient is
+// first estimated as fl(x * rcp(scale)): for |u| < 4 it lies within 1e-6 of
+// fl(x / scale) (reciprocal within 1 ulp, product and quotient each rounded
+// once).  Only an estimate within 2e-6 of a boundary (or NaN) needs the
+// exact division; the code is then the same as with exact division always.
+__device__ __forceinline__ float quant_u_estimate(float x, const QuantParams &q) {
+  return __fmul_rn(x, q.rcp);
+}
+__device__ __forceinline__ bool quant_u_near_boundary(float u) {
+  const float dist = fminf(fminf(fabsf(u - 0.5f), fabsf(u - 1.5f)), fabsf(u - 2.5f));
+  return !(dist > 2e-6f);
+}
+// fmaxf/fminf drop a NaN operand, so NaN maps to code 0
+__device__ __forceinline__ uint32_t quant_code_from_u(float u) {
+  return static_cast<uint32_t>(fminf(fmaxf(rintf(u), 0.0f), 3.0f));
 }
 
 __device__ __forceinline__ uint32_t quant_code(float z, const QuantParams &q) {
   if (q.scale_f == 0.0f) return 0u;
-  const float u = __fdiv_rn(__fsub_rn(z, q.zero_f), q.scale_f);
-  // fmaxf/fminf drop a NaN operand, so NaN maps to code 0
-  const float c = fminf(fmaxf(rintf(u), 0.0f), 3.0f);
-  return static_cast<uint32_t>(c);
+  const float x = __fsub_rn(z, q.zero_f);
+  float u = quant_u_estimate(x, q);
+  if (quant_u_near_boundary(u)) u = __fdiv_rn(x, q.scale_f);
+  return quant_code_from_u(u);
 }
 
 // ---------------------------------------------------------------------------
