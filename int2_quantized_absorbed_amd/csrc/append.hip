@@ -8,8 +8,9 @@
 // [llm-helper PR #64, PR description]: a latent layer stores the latent, the
 // rotary key and (GLM-5.3-Flash) the indexer key per token.
 //
-// Two kernels, chosen by input dtype and shape (never by token count, so one
-// layer always quantises the same way):
+// Kernels, chosen by input dtype and shape; for bf16 latents the token count
+// only picks between two kernels that give bit-identical results, so one
+// layer always quantises a token the same way:
 //  * append_mfma_kernel: bf16 latents, r in {128, 256, 384, 512}.  The
 //    rotation z^T = R_apply^T c^T is a bf16 MFMA GEMM (32x32x16, fp32
 //    accumulate) with channels as the M dimension: each lane then holds 16
@@ -17,6 +18,9 @@
 //    exchange for min/max) and the 2-bit codes of 4 consecutive channels form
 //    one byte in-lane.  The R_apply^T slice (128 channels x r) stays in LDS;
 //    latents stream from HBM straight into MFMA B operands.
+//  * append_skinny_kernel: the same shapes for appends of at most 1024 tokens
+//    (a decode step's new tokens): one wave per 32-channel x 32-token tile,
+//    operands straight from memory, the same MFMA sequence per accumulator.
 //  * append_valu_kernel: any other shape and fp32 latents; the dot products
 //    run in fp64 (exact products, fp64 sum) and are rounded once to fp32.
 #include "kernels.hpp"
@@ -155,9 +159,84 @@ __global__ __launch_bounds__(1024) void append_valu_kernel(AppendParams p) {
 constexpr int kSlice = 128;       // channels per block (4 M-tiles of 32)
 constexpr int kTokPerWave = 64;   // 2 N-tiles of 32 tokens
 constexpr int kTokPerBlock = 256; // 4 waves
+constexpr int kSkinnyMaxTokens = 1024;  // appends of at most this many tokens use append_skinny_kernel
 
 template <int R>
 constexpr int lds_stride() { return R + 8; }  // +16 B per row: rows rotate banks
+
+// Epilogue of one 32-channel x 32-token rotation tile in MFMA C layout (lane
+// l holds channels ch0 + 8q + 4hf + s, v = 4q + s, of token tok): the fp32
+// rotated latent for a rotation-only launch, else the group min/max
+// (exchanged with the partner lane l ^ 32), fp16 scale/zero, INT2 codes and
+// their stores into the token's cache slot.
+template <int R, int G>
+__device__ __forceinline__ void tile_epilogue(const AppendParams &p, const f32x16 &z, int64_t tok, bool write,
+                                              int64_t slot, int ch0, const float (&alpha)[32 / G], int hf) {
+  constexpr int NGT = 32 / G;    // groups per tile: 1 (G=32) or 2 (G=16)
+  constexpr int VPG = 16 / NGT;  // values per lane per group
+  if (p.z_out != nullptr) {
+    if (write) {
+      float *dst = p.z_out + tok * R + ch0 + 4 * hf;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4 *>(dst + 8 * q) = f32x4{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+    }
+    return;
+  }
+  QuantParams qp[NGT];
+#pragma unroll
+  for (int g = 0; g < NGT; ++g) {
+    float mx = z[g * VPG], mn = z[g * VPG];
+#pragma unroll
+    for (int v = 1; v < VPG; ++v) {
+      mx = fmaxf(mx, z[g * VPG + v]);
+      mn = fminf(mn, z[g * VPG + v]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    qp[g] = quant_params(mx, mn, alpha[g]);
+  }
+  // quotient estimates for all 16 values; the exact division runs only
+  // when some value of the wave lies next to a code boundary
+  float xs[16], us[16];
+  bool near = false;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const QuantParams &qq = qp[v / VPG];
+    xs[v] = __fsub_rn(z[v], qq.zero_f);
+    us[v] = quant_u_estimate(xs[v], qq);
+    near |= qq.scale_f != 0.0f && quant_u_near_boundary(us[v]);
+  }
+  if (near) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (quant_u_near_boundary(us[v])) us[v] = __fdiv_rn(xs[v], qp[v / VPG].scale_f);
+  }
+  uint32_t dword = 0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const uint32_t code = qp[v / VPG].scale_f == 0.0f ? 0u : quant_code_from_u(us[v]);
+    dword |= code << (2 * v);
+  }
+  // lane hf=0 holds bytes 0,2,4,6 of the tile's 8 code bytes, hf=1 holds 1,3,5,7
+  const uint32_t partner = __shfl_xor(dword, 32);
+  const uint32_t packed = __builtin_amdgcn_perm(partner, dword, hf ? 0x03070206u : 0x05010400u);
+  if (write) {
+    reinterpret_cast<uint32_t *>(p.cache.codes + slot * (R / 4) + ch0 / 4)[hf] = packed;
+    if (NGT == 1) {
+      if (hf == 0) {
+        const uint32_t sz = static_cast<uint32_t>(f16_bits(qp[0].scale)) |
+                            (static_cast<uint32_t>(f16_bits(qp[0].zero)) << 16);
+        reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G] = sz;
+      }
+    } else {
+      const QuantParams &qh = qp[hf & (NGT - 1)];
+      const uint32_t sz = static_cast<uint32_t>(f16_bits(qh.scale)) |
+                          (static_cast<uint32_t>(f16_bits(qh.zero)) << 16);
+      reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G + hf] = sz;
+    }
+  }
+}
 
 template <int R, int G, int NACC>
 __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
@@ -267,79 +346,14 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
   // epilogue: lane holds channels 32mt + 8q + 4hf + s (v = 4q + s) of token tok[nt]
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const bool ok = valid[nt];
     const int64_t slot = slot_of[nt];
-    const bool write = ok && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
+    const bool write = valid[nt] && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       f32x16 z = acc[0][mt][nt];
 #pragma unroll
       for (int a = 1; a < NACC; ++a) z += acc[a][mt][nt];
-      const int ch0 = cs * kSlice + mt * 32;  // first channel of this M-tile
-      if (p.z_out != nullptr) {
-        if (write) {
-          float *dst = p.z_out + tok[nt] * R + ch0 + 4 * hf;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<f32x4 *>(dst + 8 * q) = f32x4{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
-        }
-        continue;
-      }
-      // group statistics (exchange with the partner lane l ^ 32, same token)
-      constexpr int VPG = 16 / NGT;  // values per lane per group
-      QuantParams qp[NGT];
-#pragma unroll
-      for (int g = 0; g < NGT; ++g) {
-        float mx = z[g * VPG], mn = z[g * VPG];
-#pragma unroll
-        for (int v = 1; v < VPG; ++v) {
-          mx = fmaxf(mx, z[g * VPG + v]);
-          mn = fminf(mn, z[g * VPG + v]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mn = fminf(mn, __shfl_xor(mn, 32));
-        qp[g] = quant_params(mx, mn, alpha_of[mt][g]);
-      }
-      // quotient estimates for all 16 values; the exact division runs only
-      // when some value of the wave lies next to a code boundary
-      float xs[16], us[16];
-      bool near = false;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const QuantParams &qq = qp[v / VPG];
-        xs[v] = __fsub_rn(z[v], qq.zero_f);
-        us[v] = quant_u_estimate(xs[v], qq);
-        near |= qq.scale_f != 0.0f && quant_u_near_boundary(us[v]);
-      }
-      if (near) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (quant_u_near_boundary(us[v])) us[v] = __fdiv_rn(xs[v], qp[v / VPG].scale_f);
-      }
-      uint32_t dword = 0;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t code = qp[v / VPG].scale_f == 0.0f ? 0u : quant_code_from_u(us[v]);
-        dword |= code << (2 * v);
-      }
-      // lane hf=0 holds bytes 0,2,4,6 of the tile's 8 code bytes, hf=1 holds 1,3,5,7
-      const uint32_t partner = __shfl_xor(dword, 32);
-      const uint32_t packed = __builtin_amdgcn_perm(partner, dword, hf ? 0x03070206u : 0x05010400u);
-      if (write) {
-        reinterpret_cast<uint32_t *>(p.cache.codes + slot * (R / 4) + ch0 / 4)[hf] = packed;
-        if (NGT == 1) {
-          if (hf == 0) {
-            const uint32_t sz = static_cast<uint32_t>(f16_bits(qp[0].scale)) |
-                                (static_cast<uint32_t>(f16_bits(qp[0].zero)) << 16);
-            reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G] = sz;
-          }
-        } else {
-          const QuantParams &qh = qp[hf & (NGT - 1)];
-          const uint32_t sz = static_cast<uint32_t>(f16_bits(qh.scale)) |
-                              (static_cast<uint32_t>(f16_bits(qh.zero)) << 16);
-          reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G + hf] = sz;
-        }
-      }
+      tile_epilogue<R, G>(p, z, tok[nt], write, slot, cs * kSlice + mt * 32, alpha_of[mt], hf);
     }
   }
   // side keys: channel-slice block cs copies its share of this 256-token
@@ -358,9 +372,79 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
   }
 }
 
+// Small appends (a decode step's few new tokens): one wave per (32-channel
+// tile, 32-token tile).  R_apply^T rows and latents go straight from memory
+// into the MFMA operands (8 K-steps per double-buffered chunk), and every
+// accumulator sees the same MFMA sequence as in append_mfma_kernel (K-steps
+// in order, even/odd partial sums added at the end), so a token gets
+// bit-identical codes whichever kernel appends it.
+template <int R, int G, int NACC>
+__global__ __launch_bounds__(64) void append_skinny_kernel(AppendParams p) {
+  constexpr int KS = R / 16, PD = 8;
+  static_assert(KS % PD == 0, "K-steps come in whole chunks");
+  constexpr int NGT = 32 / G;
+  const int ct = blockIdx.x;  // channels [32 ct, 32 ct + 32)
+  const int l = threadIdx.x, hf = l >> 5, l32 = l & 31;
+  const int64_t tok = static_cast<int64_t>(blockIdx.y) * 32 + l32;
+  const bool valid = tok < p.n;
+  const bf16x8 *arow = reinterpret_cast<const bf16x8 *>(p.Rt + static_cast<int64_t>(32 * ct + l32) * R);
+  const bf16x8 *brow =
+      reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(p.latent) + (valid ? tok : 0) * R);
+  int64_t slot = -1;
+  float alpha[NGT] = {};
+  if (p.z_out == nullptr) {
+    if (valid) slot = p.slots[tok];
+#pragma unroll
+    for (int g = 0; g < NGT; ++g) alpha[g] = p.alpha[(32 * ct) / G + g];
+  }
+  const bf16x8 zero8 = {};
+  bf16x8 aq[2][PD], bq[2][PD];
+#pragma unroll
+  for (int j = 0; j < PD; ++j) {
+    aq[0][j] = arow[2 * j + hf];
+    bq[0][j] = valid ? brow[2 * j + hf] : zero8;
+  }
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) acc[a] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < KS / PD; ++c) {
+    const int cur = c & 1;
+    if (c + 1 < KS / PD) {
+#pragma unroll
+      for (int j = 0; j < PD; ++j) {
+        aq[cur ^ 1][j] = arow[2 * ((c + 1) * PD + j) + hf];
+        bq[cur ^ 1][j] = valid ? brow[2 * ((c + 1) * PD + j) + hf] : zero8;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      const int ks = c * PD + j;
+      acc[ks % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[cur][j], bq[cur][j], acc[ks % NACC], 0, 0, 0);
+    }
+  }
+  f32x16 z = acc[0];
+#pragma unroll
+  for (int a = 1; a < NACC; ++a) z += acc[a];
+  const bool write = valid && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
+  tile_epilogue<R, G>(p, z, tok, write, slot, 32 * ct, alpha, hf);
+  // side keys: the first channel tile copies its 32 tokens' keys
+  if (ct == 0 && p.z_out == nullptr) {
+    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * 32;
+    const int cnt = static_cast<int>(min<int64_t>(32, p.n - t0));
+    copy_side_keys(p.cache.k_rope, p.k_rope, p.d_r, p.slots, t0, cnt, p.cache.capacity, l);
+    if (p.d_idx > 0) copy_side_keys(p.cache.idx_key, p.idx_key, p.d_idx, p.slots, t0, cnt, p.cache.capacity, l);
+  }
+}
+
 template <int R, int G>
 hipError_t launch_mfma_rg(const AppendParams &p, hipStream_t s) {
   constexpr int NACC = 2;
+  if (p.n <= kSkinnyMaxTokens) {
+    const dim3 grid(R / 32, static_cast<unsigned>((p.n + 31) / 32));
+    append_skinny_kernel<R, G, NACC><<<grid, 64, 0, s>>>(p);
+    return hipGetLastError();
+  }
   const size_t lds = static_cast<size_t>(kSlice) * lds_stride<R>() * sizeof(uint16_t);
   static bool attr_set = false;
   if (!attr_set) {

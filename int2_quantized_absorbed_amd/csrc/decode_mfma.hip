@@ -36,7 +36,7 @@ constexpr int DR = 64;
 constexpr int ROWS = 64;        // query rows per workgroup
 constexpr int TT = 32;          // tokens per tile
 constexpr int KB = 9;           // K-blocks of 16 per wave: 8 latent + 1 rope
-constexpr int ZSTRIDE = 144;    // halves per token row of the Z tile (128 + pad)
+constexpr int ZSTRIDE = 128;    // halves per token row of the Z tile (16 chunks of 16 B)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -68,6 +68,11 @@ __device__ __forceinline__ void agpr_scale(float &x, float al) {
       : "v"(al));
 }
 
+// Z tile bank swizzle: 16-byte chunk c of token row r is stored at chunk
+// c ^ zsw(r), which spreads both the per-token 16-byte stores and the
+// transposing 8-byte reads over the LDS banks.
+__device__ __forceinline__ int zsw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
@@ -90,7 +95,7 @@ __device__ __forceinline__ int slot_channel(int hf, int kb, int e) {
   return 64 * hf + 16 * (kb >> 1) + 4 * (kb & 1) + (e >> 1) + 8 * (e & 1);
 }
 
-constexpr int SPSTRIDE = 68;    // floats per accumulator slot row (2 x 32 lanes + pad)
+constexpr int SPSTRIDE = 68;    // floats per accumulator slot row (64 lanes + pad: rows skew by 4 banks)
 constexpr int PRSTRIDE = 40;    // halves per row of P (32 tokens + pad)
 
 // Double-buffered tile state (one barrier per tile):
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   int s_vis = -1;  // padding rows are never visible
   if (s_m < M) s_vis = a.causal ? (L - a.Tq + s_m / H + 1) : L;
   const int s_lim = min(it.t1, s_vis);   // tokens < s_lim are visible to this row
-  const int s_off = 36 * s_hf + 8 * s_k8;
+  const int s_off = 32 * s_hf + 8 * s_k8;
   float m_run = -INFINITY, l_run = 0.0f;
 
   f32x16 o[2][4];
@@ -215,6 +220,9 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   const int g16 = l >> 4, s16 = l & 15;
   const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);    // transposing-load source row
   const int pv_col = 16 * (g16 & 1) + 4 * (s16 & 3);  // and column
+  // swizzle of the source rows (the same for every K-step: row % 4 and
+  // row / 4 % 4 do not depend on it)
+  const int pv_sw[2] = {zsw(pv_krow), zsw(pv_krow + 4)};
   auto tile_slot = [&](int i) -> int64_t {
     const int ti = min(i, n_tiles - 1);
     return base + min(it.t0 + ti * TT + l32, it.t1 - 1);
@@ -224,10 +232,11 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   // Z buffers, tile 1 dequantised, tile 2 in flight ----
   f16x8 bz[KB];
   f32x16 sacc[2];
+  const int zsw_st = zsw(l32);
   auto store_z = [&](int zb, const f16x8 (&v)[KB]) {
-    f16 *zt = sm.z[zb][w] + l32 * ZSTRIDE + 64 * hf;
+    f16 *zt = sm.z[zb][w] + l32 * ZSTRIDE;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = v[kb];
+    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * ((8 * hf + kb) ^ zsw_st)) = v[kb];
   };
   auto read_scores = [&](int sb, float (&s8)[8]) {
 #pragma unroll
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sm.sp[0][w][mt * 16 + v][l + 4 * hf] = sacc[mt][v];
+      for (int v = 0; v < 16; ++v) sm.sp[0][w][mt * 16 + v][l] = sacc[mt][v];
     dequant<G>(r1, bz, mask2, k1024);
     store_z(1, bz);
   }
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sm.sp[nb][w][mt * 16 + v][l + 4 * hf] = sacc[mt][v];
+        for (int v = 0; v < 16; ++v) sm.sp[nb][w][mt * 16 + v][l] = sacc[mt][v];
     }
     lds_barrier();
 
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
           }
         }
     }
-    const f16 *zb_base = sm.z[buf][w] + pv_krow * ZSTRIDE + pv_col;
+    const f16 *zb_base = sm.z[buf][w] + pv_krow * ZSTRIDE + (pv_col & 7);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       f16x8 pa[2];
@@ -341,9 +350,9 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
         pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p[buf] + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const f16 *z0 = zb_base + 16 * ks * ZSTRIDE + 32 * nt;
-        const f16x4 lo = ds_read_tr16(z0);
-        const f16x4 hi = ds_read_tr16(z0 + 4 * ZSTRIDE);
+        const f16 *z0 = zb_base + 16 * ks * ZSTRIDE;
+        const f16x4 lo = ds_read_tr16(z0 + 8 * ((4 * nt + (pv_col >> 3)) ^ pv_sw[0]));
+        const f16x4 hi = ds_read_tr16(z0 + 4 * ZSTRIDE + 8 * ((4 * nt + (pv_col >> 3)) ^ pv_sw[1]));
         const f16x8 zb = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)

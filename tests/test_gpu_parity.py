@@ -94,6 +94,15 @@ APPEND_CASES = [
     ("w4-bf16-idx", 4, dict(), 300),
     ("w1-r256", 1, dict(kv_lora_rank=256), 129),
     ("w1-r96-valu", 1, dict(kv_lora_rank=96), 70),
+    # more than 1024 tokens: the LDS-staged append kernel
+    ("w1-bf16-large-1500", 1, dict(), 1500),
+    ("w1-bf16-large-g16-1100", 1, dict(group_size=16), 1100),
+    ("w4-bf16-idx-large-1300", 4, dict(), 1300),
+    # at most 1024 tokens: the small-append kernel
+    ("w1-bf16-small-8", 1, dict(), 8),
+    ("w1-bf16-small-g16-37", 1, dict(group_size=16), 37),
+    ("w4-bf16-idx-small-64", 4, dict(), 64),
+    ("w1-r256-small-20", 1, dict(kv_lora_rank=256), 20),
 ]
 
 
@@ -130,6 +139,31 @@ def test_append_quant(name, wid, over, n):
         assert np.array_equal(cache.idx_key.float().cpu().numpy()[sl], idx[ok])
     untouched = np.setdiff1d(np.arange(cap), sl)
     assert np.all(cache.codes.cpu().numpy()[untouched] == 0xAB)
+
+
+@pytest.mark.parametrize("group", [32, 16])
+def test_append_small_and_large_batches_agree(group):
+    """Appending tokens a few at a time (the decode step's path) writes the
+    same bytes as appending them in one large call."""
+    w = S.WORKLOADS[1].with_(group_size=group)
+    C.say(f"append batch-size invariance G={group}")
+    layer = C.Layer(w)
+    rng = np.random.default_rng(11)
+    n = 1500  # one call: LDS-staged kernel; pieces of at most 64: small-append kernel
+    c = C.latent_tensor(layer.model.sample(rng, n), "bf16")
+    kr = C.t_bf16(S.rope_keys(rng, n, w.qk_rope_head_dim))
+    slots = torch.arange(n, dtype=torch.int64, device=C.DEV)
+    big = M.Cache(layer.dims, n, C.DEV)
+    M.mla_append_quant(layer.dims, c, kr, None, slots, layer.Rt_d, layer.alpha_d, big)
+    small = M.Cache(layer.dims, n, C.DEV)
+    cuts = [0, 8, 72, 73, 137, 170, 234, 298, 300] + list(range(364, n, 64)) + [n]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        M.mla_append_quant(layer.dims, c[a:b].clone(), kr[a:b].clone(), None, slots[a:b].clone(),
+                           layer.Rt_d, layer.alpha_d, small)
+    torch.cuda.synchronize()
+    assert torch.equal(big.codes, small.codes)
+    assert torch.equal(big.scale_zero.view(torch.int16), small.scale_zero.view(torch.int16))
+    assert torch.equal(big.k_rope.view(torch.int16), small.k_rope.view(torch.int16))
 
 
 def test_append_empty_is_noop():
