@@ -36,7 +36,7 @@ constexpr int DR = 64;
 constexpr int ROWS = 64;        // query rows per workgroup
 constexpr int TT = 32;          // tokens per tile
 constexpr int KB = 9;           // K-blocks of 16 per wave: 8 latent + 1 rope
-constexpr int ZSTRIDE = 128;    // halves per token row of the Z tile (16 chunks of 16 B)
+constexpr int ZSTRIDE = 144;    // halves per token row of the Z tile (128 + pad)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -68,10 +68,12 @@ __device__ __forceinline__ void agpr_scale(float &x, float al) {
       : "v"(al));
 }
 
-// Z tile bank swizzle: 16-byte chunk c of token row r is stored at chunk
-// c ^ zsw(r), which spreads both the per-token 16-byte stores and the
-// transposing 8-byte reads over the LDS banks.
-__device__ __forceinline__ int zsw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// LDS store of a value the MFMA left in an AGPR (gfx950 DS stores take AGPR
+// data), without a copy through a VGPR; the byte offset is an immediate.
+template <int OFF>
+__device__ __forceinline__ void ds_store_agpr(uint32_t lds_addr, float x) {
+  asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(lds_addr), "a"(x), "i"(OFF) : "memory");
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -220,9 +222,6 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   const int g16 = l >> 4, s16 = l & 15;
   const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);    // transposing-load source row
   const int pv_col = 16 * (g16 & 1) + 4 * (s16 & 3);  // and column
-  // swizzle of the source rows (the same for every K-step: row % 4 and
-  // row / 4 % 4 do not depend on it)
-  const int pv_sw[2] = {zsw(pv_krow), zsw(pv_krow + 4)};
   auto tile_slot = [&](int i) -> int64_t {
     const int ti = min(i, n_tiles - 1);
     return base + min(it.t0 + ti * TT + l32, it.t1 - 1);
@@ -232,11 +231,10 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   // Z buffers, tile 1 dequantised, tile 2 in flight ----
   f16x8 bz[KB];
   f32x16 sacc[2];
-  const int zsw_st = zsw(l32);
   auto store_z = [&](int zb, const f16x8 (&v)[KB]) {
-    f16 *zt = sm.z[zb][w] + l32 * ZSTRIDE;
+    f16 *zt = sm.z[zb][w] + l32 * ZSTRIDE + 64 * hf;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * ((8 * hf + kb) ^ zsw_st)) = v[kb];
+    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = v[kb];
   };
   auto read_scores = [&](int sb, float (&s8)[8]) {
 #pragma unroll
@@ -249,6 +247,29 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
       s8[e + 2] = acc4[2];
       s8[e + 3] = acc4[3];
     }
+  };
+  // partial scores -> sm.sp[sb][w][slot][l], slot = 16 mt + v (32 stores
+  // straight from the accumulator AGPRs)
+  auto publish = [&](int sb, const f32x16 (&acc)[2]) {
+    typedef __attribute__((address_space(3))) float lds_float;
+    const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_float *)&sm.sp[sb][w][0][l]));
+    constexpr int RB = SPSTRIDE * 4;  // bytes per slot row
+    ds_store_agpr<0 * RB>(a0, acc[0][0]);   ds_store_agpr<1 * RB>(a0, acc[0][1]);
+    ds_store_agpr<2 * RB>(a0, acc[0][2]);   ds_store_agpr<3 * RB>(a0, acc[0][3]);
+    ds_store_agpr<4 * RB>(a0, acc[0][4]);   ds_store_agpr<5 * RB>(a0, acc[0][5]);
+    ds_store_agpr<6 * RB>(a0, acc[0][6]);   ds_store_agpr<7 * RB>(a0, acc[0][7]);
+    ds_store_agpr<8 * RB>(a0, acc[0][8]);   ds_store_agpr<9 * RB>(a0, acc[0][9]);
+    ds_store_agpr<10 * RB>(a0, acc[0][10]); ds_store_agpr<11 * RB>(a0, acc[0][11]);
+    ds_store_agpr<12 * RB>(a0, acc[0][12]); ds_store_agpr<13 * RB>(a0, acc[0][13]);
+    ds_store_agpr<14 * RB>(a0, acc[0][14]); ds_store_agpr<15 * RB>(a0, acc[0][15]);
+    ds_store_agpr<16 * RB>(a0, acc[1][0]);  ds_store_agpr<17 * RB>(a0, acc[1][1]);
+    ds_store_agpr<18 * RB>(a0, acc[1][2]);  ds_store_agpr<19 * RB>(a0, acc[1][3]);
+    ds_store_agpr<20 * RB>(a0, acc[1][4]);  ds_store_agpr<21 * RB>(a0, acc[1][5]);
+    ds_store_agpr<22 * RB>(a0, acc[1][6]);  ds_store_agpr<23 * RB>(a0, acc[1][7]);
+    ds_store_agpr<24 * RB>(a0, acc[1][8]);  ds_store_agpr<25 * RB>(a0, acc[1][9]);
+    ds_store_agpr<26 * RB>(a0, acc[1][10]); ds_store_agpr<27 * RB>(a0, acc[1][11]);
+    ds_store_agpr<28 * RB>(a0, acc[1][12]); ds_store_agpr<29 * RB>(a0, acc[1][13]);
+    ds_store_agpr<30 * RB>(a0, acc[1][14]); ds_store_agpr<31 * RB>(a0, acc[1][15]);
   };
   float s_next[8];
   {
@@ -263,10 +284,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
       for (int mt = 0; mt < 2; ++mt)
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
     store_z(0, bz);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sm.sp[0][w][mt * 16 + v][l] = sacc[mt][v];
+    publish(0, sacc);
     dequant<G>(r1, bz, mask2, k1024);
     store_z(1, bz);
   }
@@ -317,12 +335,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     if (l == 0) sm.resc[buf][w] = any_w;
 
     // ---- (c) publish the partial scores of tile i+1 ----
-    {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sm.sp[nb][w][mt * 16 + v][l] = sacc[mt][v];
-    }
+    publish(nb, sacc);
     lds_barrier();
 
     // ---- (d) O = alpha * O + P Z for tile i ----
@@ -341,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
           }
         }
     }
-    const f16 *zb_base = sm.z[buf][w] + pv_krow * ZSTRIDE + (pv_col & 7);
+    const f16 *zb_base = sm.z[buf][w] + pv_krow * ZSTRIDE + pv_col;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       f16x8 pa[2];
@@ -350,9 +363,9 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
         pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p[buf] + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const f16 *z0 = zb_base + 16 * ks * ZSTRIDE;
-        const f16x4 lo = ds_read_tr16(z0 + 8 * ((4 * nt + (pv_col >> 3)) ^ pv_sw[0]));
-        const f16x4 hi = ds_read_tr16(z0 + 4 * ZSTRIDE + 8 * ((4 * nt + (pv_col >> 3)) ^ pv_sw[1]));
+        const f16 *z0 = zb_base + 16 * ks * ZSTRIDE + 32 * nt;
+        const f16x4 lo = ds_read_tr16(z0);
+        const f16x4 hi = ds_read_tr16(z0 + 4 * ZSTRIDE);
         const f16x8 zb = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
