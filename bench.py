@@ -87,6 +87,13 @@ def algorithmic_flops(w, lens) -> float:
     return 2.0 * H * (2 * r + dr) * pairs
 
 
+def append_bytes_per_token(w) -> int:
+    """Quantise-on-append traffic per token: bf16 latent, rope (and indexer)
+    key and slot read; codes, fp16 scale/zero and the keys written."""
+    keys = 2 * (w.qk_rope_head_dim + w.index_head_dim)
+    return 2 * w.kv_lora_rank + keys + 8 + w.kv_lora_rank // 4 + 4 * (w.kv_lora_rank // w.group_size) + keys
+
+
 def cache_bytes_per_token(w) -> int:
     return w.kv_lora_rank // 4 + 4 * (w.kv_lora_rank // w.group_size) + 2 * w.qk_rope_head_dim
 
@@ -182,6 +189,35 @@ def main():
             kernels[name] = round(ms / n * 1e3, 3)
     M.mla_timing_enable(False)
 
+    # prefill-sized append (4 sequences x 4096 tokens of the 131k-context
+    # workload, same layer shape) into a separate cache, timed with events
+    n_pre = 4 * 4096
+    pre_lat = S.torch_latents(model, n_pre, seed=6000 + w.wid, device=dev)
+    pre_kr = S.torch_normal_bf16((n_pre, w.qk_rope_head_dim), 7000 + w.wid, dev)
+    pre_idx = S.torch_normal_bf16((n_pre, w.index_head_dim), 8000 + w.wid, dev) if w.index_head_dim else None
+    pre_slots = torch.arange(n_pre, dtype=torch.int64, device=dev)
+    pre_cache = M.Cache(d, n_pre, dev)
+    for _ in range(3):
+        M.mla_append_quant(d, pre_lat, pre_kr, pre_idx, pre_slots, Rt, alpha, pre_cache)
+    torch.cuda.synchronize()
+    M.mla_timing_enable(True)
+    M.mla_timing_reset()
+    for _ in range(20):
+        M.mla_append_quant(d, pre_lat, pre_kr, pre_idx, pre_slots, Rt, alpha, pre_cache)
+    torch.cuda.synchronize()
+    ms, n = M.mla_timing_query("append_quant")
+    M.mla_timing_enable(False)
+    pre_us = ms / n * 1e3
+    pre_bytes = n_pre * append_bytes_per_token(w)
+    pre_flops = 2.0 * n_pre * w.kv_lora_rank * w.kv_lora_rank
+    append_prefill = {
+        "tokens": n_pre, "us": round(pre_us, 3), "algorithmic_bytes": pre_bytes,
+        "GB/s": round(pre_bytes / (pre_us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(pre_bytes / (pre_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "mfma_frac": round(pre_flops / (pre_us * 1e-6) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+    }
+    del pre_lat, pre_kr, pre_idx, pre_cache
+
     total_tokens = int(np.sum(lens))
     bpt = cache_bytes_per_token(w)
     cache_bytes = total_tokens * bpt
@@ -230,6 +266,7 @@ def main():
         "query_tokens_per_s": round(B * tq / (ms_per_step * 1e-3), 1),
         "hbm_frac_step": round(value / PEAK_HBM_GBS, 4),
         "kernel_us": kernels,
+        "append_prefill": append_prefill,
         "roofline": roofline,
     }
 

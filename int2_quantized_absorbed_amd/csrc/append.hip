@@ -157,8 +157,10 @@ __global__ __launch_bounds__(1024) void append_valu_kernel(AppendParams p) {
 // MFMA path
 // ---------------------------------------------------------------------------
 constexpr int kSlice = 128;       // channels per block (4 M-tiles of 32)
-constexpr int kTokPerWave = 64;   // 2 N-tiles of 32 tokens
-constexpr int kTokPerBlock = 256; // 4 waves
+constexpr int kWaves = 8;         // two waves per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTokPerWave = 32;   // one N-tile of 32 tokens
+constexpr int kTokPerBlock = kWaves * kTokPerWave;
 constexpr int kSkinnyMaxTokens = 1024;  // appends of at most this many tokens use append_skinny_kernel
 
 template <int R>
@@ -239,7 +241,7 @@ __device__ __forceinline__ void tile_epilogue(const AppendParams &p, const f32x1
 }
 
 template <int R, int G, int NACC>
-__global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
+__global__ __launch_bounds__(kThreads) void append_mfma_kernel(AppendParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t rt_s[];
   constexpr int KS = R / 16;
   constexpr int NSLICE = R / kSlice;
@@ -249,68 +251,53 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, hf = l >> 5, l32 = l & 31;
 
-  const uint16_t *lat = static_cast<const uint16_t *>(p.latent);
-  int64_t tok[2];
-  bool valid[2];
-  const bf16x8 *brow[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    tok[nt] = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave + nt * 32 + l32;
-    valid[nt] = tok[nt] < p.n;
-    brow[nt] = reinterpret_cast<const bf16x8 *>(lat + (valid[nt] ? tok[nt] : 0) * R);
-  }
+  // this wave's 32 tokens; lanes of tokens past the end read token 0's row
+  // (their output columns are never stored), so every load is unconditional
+  const int64_t wave_tok0 = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave;
+  const int64_t tok = wave_tok0 + l32;
+  const bool valid = tok < p.n;
+  const bf16x8 *brow = reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(p.latent) + (valid ? tok : 0) * R);
   // epilogue inputs, fetched now so their latency hides under the GEMM
   constexpr int NGT = 32 / G;  // groups per M-tile: 1 (G=32) or 2 (G=16)
-  int64_t slot_of[2] = {-1, -1};
+  int64_t slot = -1;
+  float alpha_of[4][NGT] = {};  // (the rotation-only launch, z_out != nullptr, has no alpha)
   if (p.z_out == nullptr) {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      if (valid[nt]) slot_of[nt] = p.slots[tok[nt]];
-  }
-  // (the rotation-only launch, z_out != nullptr, has no alpha)
-  float alpha_of[4][NGT] = {};
-  if (p.z_out == nullptr) {
+    if (valid) slot = p.slots[tok];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int g = 0; g < NGT; ++g) alpha_of[mt][g] = p.alpha[(cs * kSlice + mt * 32) / G + g];
   }
-  // a wave whose 64 tokens all lie past the end skips the products
-  const bool live = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave < p.n;
+  const bool live = wave_tok0 < p.n;  // a wave with no token in range skips the products
 
-  f32x16 acc[NACC][4][2];
+  f32x16 acc[NACC][4];
 #pragma unroll
   for (int a = 0; a < NACC; ++a)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[a][mt][nt] = f32x16{};
+    for (int mt = 0; mt < 4; ++mt) acc[a][mt] = f32x16{};
 
   // latent operands stream from HBM in chunks of PD K-steps, double-buffered:
   // chunk c + 1 is in flight while chunk c is multiplied
   constexpr int PD = 8;
   static_assert(KS % PD == 0, "K-steps come in whole chunks");
-  const bf16x8 zero8 = {};
-  bf16x8 bq[2][PD][2];
+  bf16x8 bq[2][PD];
 #pragma unroll
-  for (int j = 0; j < PD; ++j)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) bq[0][j][nt] = valid[nt] ? brow[nt][2 * j + hf] : zero8;
-  // stage R_apply^T rows [cs*128, +128) into LDS (16-byte chunks, 16 (or 8)
+  for (int j = 0; j < PD; ++j) bq[0][j] = brow[2 * j + hf];
+  // stage R_apply^T rows [cs*128, +128) into LDS (16-byte chunks, several
   // loads in flight per thread) while the first latent chunk is in flight
   {
     const uint4 *src = reinterpret_cast<const uint4 *>(p.Rt + static_cast<int64_t>(cs) * kSlice * R);
     constexpr int CPR = R / 8;  // chunks per row
     constexpr int TOTAL = kSlice * CPR;
-    constexpr int SU = TOTAL % (256 * 16) == 0 ? 16 : 8;
-    static_assert(TOTAL % (256 * SU) == 0, "staging loop has no tail");
-    for (int e0 = tid; e0 < TOTAL; e0 += 256 * SU) {
+    constexpr int SU = TOTAL % (kThreads * 16) == 0 ? 16 : (TOTAL % (kThreads * 8) == 0 ? 8 : 4);
+    static_assert(TOTAL % (kThreads * SU) == 0, "staging loop has no tail");
+    for (int e0 = tid; e0 < TOTAL; e0 += kThreads * SU) {
       uint4 v[SU];
 #pragma unroll
-      for (int j = 0; j < SU; ++j) v[j] = src[e0 + 256 * j];
+      for (int j = 0; j < SU; ++j) v[j] = src[e0 + kThreads * j];
 #pragma unroll
       for (int j = 0; j < SU; ++j) {
-        const int e = e0 + 256 * j, row = e / CPR, c = e % CPR;
+        const int e = e0 + kThreads * j, row = e / CPR, c = e % CPR;
         *reinterpret_cast<uint4 *>(rt_s + row * LS + c * 8) = v[j];
       }
     }
@@ -322,10 +309,7 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
     const int cur = c & 1;
     if (c + 1 < KS / PD) {
 #pragma unroll
-      for (int j = 0; j < PD; ++j)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          bq[cur ^ 1][j][nt] = valid[nt] ? brow[nt][2 * ((c + 1) * PD + j) + hf] : zero8;
+      for (int j = 0; j < PD; ++j) bq[cur ^ 1][j] = brow[2 * ((c + 1) * PD + j) + hf];
     }
 #pragma unroll
     for (int j = 0; j < PD; ++j) {
@@ -337,30 +321,24 @@ __global__ __launch_bounds__(256, 1) void append_mfma_kernel(AppendParams p) {
       const int par = ks % NACC;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[par][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], bq[cur][j][nt], acc[par][mt][nt], 0, 0, 0);
+        acc[par][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], bq[cur][j], acc[par][mt], 0, 0, 0);
     }
   }
 
-  // epilogue: lane holds channels 32mt + 8q + 4hf + s (v = 4q + s) of token tok[nt]
+  // epilogue: lane holds channels 32mt + 8q + 4hf + s (v = 4q + s) of token tok
+  const bool write = valid && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t slot = slot_of[nt];
-    const bool write = valid[nt] && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
+  for (int mt = 0; mt < 4; ++mt) {
+    f32x16 z = acc[0][mt];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x16 z = acc[0][mt][nt];
-#pragma unroll
-      for (int a = 1; a < NACC; ++a) z += acc[a][mt][nt];
-      tile_epilogue<R, G>(p, z, tok[nt], write, slot, cs * kSlice + mt * 32, alpha_of[mt], hf);
-    }
+    for (int a = 1; a < NACC; ++a) z += acc[a][mt];
+    tile_epilogue<R, G>(p, z, tok, write, slot, cs * kSlice + mt * 32, alpha_of[mt], hf);
   }
   // side keys: channel-slice block cs copies its share of this 256-token
-  // tile (ceil(256 / NSLICE) tokens), a quarter of that per wave, every lane
+  // tile (ceil(256 / NSLICE) tokens), an eighth of that per wave, every lane
   // moving 16-byte pieces
   if (p.z_out == nullptr) {
-    constexpr int PB = (kTokPerBlock + NSLICE - 1) / NSLICE, PW = (PB + 3) / 4;
+    constexpr int PB = (kTokPerBlock + NSLICE - 1) / NSLICE, PW = (PB + kWaves - 1) / kWaves;
     const int64_t tile_end = min<int64_t>(static_cast<int64_t>(tb + 1) * kTokPerBlock, p.n);
     const int64_t t0 = static_cast<int64_t>(tb) * kTokPerBlock + cs * PB + w * PW;
     const int64_t t1 = min<int64_t>(min<int64_t>(t0 + PW, static_cast<int64_t>(tb) * kTokPerBlock + (cs + 1) * PB), tile_end);
@@ -397,12 +375,13 @@ __global__ __launch_bounds__(64) void append_skinny_kernel(AppendParams p) {
 #pragma unroll
     for (int g = 0; g < NGT; ++g) alpha[g] = p.alpha[(32 * ct) / G + g];
   }
-  const bf16x8 zero8 = {};
+  // lanes of tokens past the end read token 0's row (their columns are never
+  // stored), so the loads carry no branches
   bf16x8 aq[2][PD], bq[2][PD];
 #pragma unroll
   for (int j = 0; j < PD; ++j) {
     aq[0][j] = arow[2 * j + hf];
-    bq[0][j] = valid ? brow[2 * j + hf] : zero8;
+    bq[0][j] = brow[2 * j + hf];
   }
   f32x16 acc[NACC];
 #pragma unroll
@@ -414,7 +393,7 @@ __global__ __launch_bounds__(64) void append_skinny_kernel(AppendParams p) {
 #pragma unroll
       for (int j = 0; j < PD; ++j) {
         aq[cur ^ 1][j] = arow[2 * ((c + 1) * PD + j) + hf];
-        bq[cur ^ 1][j] = valid ? brow[2 * ((c + 1) * PD + j) + hf] : zero8;
+        bq[cur ^ 1][j] = brow[2 * ((c + 1) * PD + j) + hf];
       }
     }
 #pragma unroll
@@ -454,7 +433,7 @@ hipError_t launch_mfma_rg(const AppendParams &p, hipStream_t s) {
     attr_set = true;
   }
   const int64_t blocks = ((p.n + kTokPerBlock - 1) / kTokPerBlock) * (R / kSlice);
-  append_mfma_kernel<R, G, NACC><<<static_cast<unsigned>(blocks), 256, lds, s>>>(p);
+  append_mfma_kernel<R, G, NACC><<<static_cast<unsigned>(blocks), kThreads, lds, s>>>(p);
   return hipGetLastError();
 }
 
