@@ -241,13 +241,19 @@ __device__ __forceinline__ void tile_epilogue(const AppendParams &p, const f32x1
 }
 
 template <int R, int G, int NACC>
-__global__ __launch_bounds__(kThreads) void append_mfma_kernel(AppendParams p) {
+__global__ __launch_bounds__(kThreads) void append_mfma_kernel(AppendParams p, int n_logical) {
   extern __shared__ __attribute__((aligned(16))) uint16_t rt_s[];
   constexpr int KS = R / 16;
   constexpr int NSLICE = R / kSlice;
   constexpr int LS = lds_stride<R>();
-  const int cs = blockIdx.x % NSLICE;
-  const int tb = blockIdx.x / NSLICE;
+  // XCD-aware order: blocks b, b + 8, ... run on one XCD (one L2); give them
+  // consecutive logical indices, so the NSLICE channel-slice blocks of a
+  // token tile read its latents through the same L2
+  const int per_xcd = static_cast<int>(gridDim.x / 8);
+  const int logical = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+  if (logical >= n_logical) return;  // grid padding (whole block)
+  const int cs = logical % NSLICE;
+  const int tb = logical / NSLICE;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, hf = l >> 5, l32 = l & 31;
 
@@ -433,7 +439,9 @@ hipError_t launch_mfma_rg(const AppendParams &p, hipStream_t s) {
     attr_set = true;
   }
   const int64_t blocks = ((p.n + kTokPerBlock - 1) / kTokPerBlock) * (R / kSlice);
-  append_mfma_kernel<R, G, NACC><<<static_cast<unsigned>(blocks), kThreads, lds, s>>>(p);
+  if (blocks > (int64_t{1} << 30)) return hipErrorInvalidValue;
+  const int64_t grid = (blocks + 7) / 8 * 8;  // a multiple of 8 (XCD-aware order)
+  append_mfma_kernel<R, G, NACC><<<static_cast<unsigned>(grid), kThreads, lds, s>>>(p, static_cast<int>(blocks));
   return hipGetLastError();
 }
 
