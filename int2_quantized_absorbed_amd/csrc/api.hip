@@ -142,11 +142,12 @@ struct WsLayout {
   int max_items = 0;
 };
 
-int target_items(int rows, int B, bool mfma) {
+// Work items that fill the GPU: one resident block per (item, row block).
+int target_items(int rows, bool mfma) {
   const int ncu = device_cu_count();
   const int rb = mfma ? (rows + mfma_row_block() - 1) / mfma_row_block() : (rows + 15) / 16;
   const int slots = mfma ? ncu : 2 * ncu;  // resident blocks per launch
-  const int t = slots / rb - B;
+  const int t = slots / rb;
   return t < 1 ? 1 : t;
 }
 
@@ -154,8 +155,9 @@ WsLayout layout(const mla_dims &d, int B, int Tq) {
   WsLayout w;
   const int r = d.kv_lora_rank, K = r + d.qk_rope_head_dim;
   const int M = d.num_heads * Tq;
-  const int tgt = std::max(target_items(M, B, true), target_items(M, B, false));
-  w.max_items = tgt + B;
+  // the planner emits at most max(target, number of sequences) items
+  const int tgt = std::max(target_items(M, true), target_items(M, false));
+  w.max_items = std::max(tgt, B);
   size_t off = 0;
   w.items = off;
   off = align256(off + sizeof(WorkItem) * w.max_items);
@@ -461,7 +463,7 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
   a.part_o = reinterpret_cast<float *>(ws + w.part_o);
   a.part_ml = reinterpret_cast<float *>(ws + w.part_ml);
   a.max_items = w.max_items;
-  a.target_items = target_items(M, batch, use_mfma);
+  a.target_items = target_items(M, use_mfma);
   a.tile = use_mfma ? 32 : 16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the MFMA absorb kernel also runs the planner

@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 // for padding rows.  Block = (head, latent quarter = split-K wave slot,
 // 32 query rows (b, t)); wave w computes 32 channels.  The results are staged
 // in LDS so every operand unit (8 halves) is written with one 16-byte store.
-// Block (0, 0) also runs the split-K planner.  w_uk_f is stored [H][r][d_n].
+// One extra block runs the split-K planner.  w_uk_f is stored [H][r][d_n].
 __device__ __forceinline__ int64_t qpos(int rb_count, int b, int m, int w, int hf, int kb) {
   const int rb = m / ROWS, mt = (m % ROWS) / 32, lane = (m % 32) + 32 * hf;
   return ((((static_cast<int64_t>(b) * rb_count + rb) * 4 + w) * 2 + mt) * KB + kb) * 512 + lane * 8;
@@ -416,10 +416,16 @@ constexpr int QTSTRIDE = 136;  // halves per staged row (128 channels + pad)
 
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_count) {
   __shared__ __align__(16) f16 qt[32 * QTSTRIDE];
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    plan_block(a.seq_len, a.B, a.target_items, a.tile, a.max_items, a.items, a.item_begin, a.meta);
-  const int h = blockIdx.x >> 2, cq = blockIdx.x & 3, rt = blockIdx.y;
   const int H = a.d.num_heads, dn = a.d.qk_nope_head_dim;
+  // the extra first block column: block (0, 0) plans the split-K work in
+  // parallel with the absorb blocks (and is dispatched first), the rest of
+  // that column has nothing to do
+  if (blockIdx.x == 0) {
+    if (blockIdx.y == 0)
+      plan_block(a.seq_len, a.B, a.target_items, a.tile, a.max_items, a.items, a.item_begin, a.meta);
+    return;
+  }
+  const int h = (blockIdx.x - 1) >> 2, cq = (blockIdx.x - 1) & 3, rt = blockIdx.y;
   const int M = H * a.Tq;
   const int nrows = a.B * a.Tq;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, hf = l >> 5, l32 = l & 31;
@@ -513,7 +519,7 @@ hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s) {
   const int M = a.d.num_heads * a.Tq;
   const int rb_count = (M + ROWS - 1) / ROWS;
   const int nrows = a.B * a.Tq;
-  absorb_mfma_kernel<<<dim3(a.d.num_heads * 4, (nrows + 31) / 32), 256, 0, s>>>(a, rb_count);
+  absorb_mfma_kernel<<<dim3(a.d.num_heads * 4 + 1, (nrows + 31) / 32), 256, 0, s>>>(a, rb_count);
   return hipGetLastError();
 }
 

@@ -5,11 +5,6 @@
 
 namespace mla {
 
-__device__ inline long long plan_wave_sum(long long x) {
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
 __device__ inline int plan_wave_incl_scan(int x, int lane) {
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off);
@@ -19,38 +14,95 @@ __device__ inline int plan_wave_incl_scan(int x, int lane) {
 }
 
 // Token-balanced split-K plan from device seq_len (no host synchronisation),
-// run by one whole block of 256 threads.
-// Chunk length C = round_up(ceil(total / target), tile); sequence b gets
-// ceil(L_b / C) items of equal length (rounded up to the tile).  The item
-// count is then at most target + B = max_items.
+// run by one whole block of 256 threads.  A chunk length C (a multiple of
+// the tile) gives sequence b nb(L_b, C) items of equal length: nb =
+// ceil(L_b / C), the chunk rounded up to the tile, nb recomputed from it.
+// The item count is non-increasing in C; the planner takes the smallest C
+// whose count fits `target` (the work-item slots that fill the GPU), so the
+// grid is as full as the lengths allow, or one item per sequence when even
+// that exceeds target.  max_items bounds the count and the item array.
+__device__ inline int plan_items_of(int L, int C, int tile, int *chunk_out) {
+  if (L <= 0) {
+    *chunk_out = 0;
+    return 0;
+  }
+  int nb = (L + C - 1) / C;
+  int chunk = (L + nb - 1) / nb;
+  chunk = ((chunk + tile - 1) / tile) * tile;
+  *chunk_out = chunk;
+  return (L + chunk - 1) / chunk;
+}
+
 __device__ inline void plan_block(const int32_t *__restrict__ seq_len, int B, int target, int tile,
                                   int max_items, WorkItem *__restrict__ items,
                                   int32_t *__restrict__ item_begin, int32_t *__restrict__ meta) {
   // called by one whole block of 256 threads
   __shared__ long long wsum[4];
+  __shared__ int32_t wne[4], wmax[4], wred[4];
   __shared__ int32_t wtot[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int L0 = tid < B ? seq_len[tid] : 0;
-  long long tot = max(0, L0);
-  for (int b = tid + 256; b < B; b += 256) tot += max(0, seq_len[b]);
-  tot = plan_wave_sum(tot);
-  if (lane == 0) wsum[wv] = tot;
+  auto len_of = [&](int b) -> int { return b < 256 ? L0 : seq_len[b]; };
+  // totals: tokens, non-empty sequences, longest sequence (one barrier pair)
+  long long tot = 0;
+  int ne = 0, lmax = 0;
+  for (int b = tid; b < B; b += 256) {
+    const int L = max(0, len_of(b));
+    tot += L;
+    ne += L > 0;
+    lmax = max(lmax, L);
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    tot += __shfl_xor(tot, off);
+    ne += __shfl_xor(ne, off);
+    lmax = max(lmax, __shfl_xor(lmax, off));
+  }
+  if (lane == 0) {
+    wsum[wv] = tot;
+    wne[wv] = ne;
+    wmax[wv] = lmax;
+  }
   __syncthreads();
   const long long total = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  long long C = (total + target - 1) / max(target, 1);
-  C = ((C + tile - 1) / tile) * tile;
-  if (C < tile) C = tile;
+  const int nonempty = (wne[0] + wne[1]) + (wne[2] + wne[3]);
+  lmax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  // item count at C = k * tile (block-wide sum, two barriers)
+  auto count = [&](int k) -> int {
+    int chunk, n = 0;
+    for (int b = tid; b < B; b += 256) n += plan_items_of(len_of(b), k * tile, tile, &chunk);
+    for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+    __syncthreads();  // wred may still be read from the previous call
+    if (lane == 0) wred[wv] = n;
+    __syncthreads();
+    return (wred[0] + wred[1]) + (wred[2] + wred[3]);
+  };
+  // count(C) >= total / C, so C >= total / target; and every chunk is at
+  // most C, so count(C) <= total / C + nonempty, which fits target once
+  // C >= total / (target - nonempty).  Search the smallest fitting k between.
+  const long long T = target;
+  const int khi = max(1, (lmax + tile - 1) / tile);  // one item per sequence
+  int lo, hi;
+  if (T <= nonempty) {
+    lo = hi = khi;
+  } else {
+    const long long per_lo = T * tile, per_hi = (T - nonempty) * tile;
+    lo = static_cast<int>(min<long long>(khi, max<long long>(1, (total + per_lo - 1) / per_lo)));
+    hi = static_cast<int>(min<long long>(khi, max<long long>(lo, (total + per_hi - 1) / per_hi)));
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (count(mid) <= target)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+  }
+  const int C = lo * tile;
   int carry = 0;
   for (int base = 0; base < B; base += 256) {
     const int b = base + tid;
-    int nb = 0, chunk = 0;
-    const int L = base == 0 ? L0 : (b < B ? seq_len[b] : 0);
-    if (L > 0) {
-      nb = static_cast<int>((L + C - 1) / C);
-      chunk = (L + nb - 1) / nb;
-      chunk = ((chunk + tile - 1) / tile) * tile;
-      nb = (L + chunk - 1) / chunk;
-    }
+    const int L = b < B ? len_of(b) : 0;
+    int chunk;
+    const int nb = plan_items_of(L, C, tile, &chunk);
     const int inc = plan_wave_incl_scan(nb, lane);
     if (lane == 63) wtot[wv] = inc;
     __syncthreads();
@@ -78,7 +130,7 @@ __device__ inline void plan_block(const int32_t *__restrict__ seq_len, int B, in
     const int n = min(carry, max_items);
     item_begin[B] = n;
     meta[0] = n;
-    meta[1] = static_cast<int32_t>(C);
+    meta[1] = C;
   }
 }
 
