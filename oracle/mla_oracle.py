@@ -33,7 +33,10 @@ compared bit for bit.  Readings of points the pages leave open are marked
 Parity status per function (what pins it is in tests/test_oracle_*.py):
 all functions below are pinned, except ``fit_clip``'s choice of objective and
 grid (the pages print no clip values: parity unpinned against the pages; the
-search itself is pinned by brute force).
+search itself is pinned by brute force) and ``calibrate_rotation_weighted``'s
+weighting (a reading of a refinement the pages only name: parity unpinned
+against the pages; its reduction to the unweighted rotation, a closed form
+and its invariants are pinned).
 """
 from __future__ import annotations
 
@@ -111,6 +114,57 @@ def calibrate_rotation(c_cal):
     """
     sigma = latent_covariance(c_cal)
     lam, vec = np.linalg.eigh(sigma)  # LAPACK, eigenvalues ascending
+    order = np.argsort(lam, kind="stable")
+    lam = lam[order]
+    vec = canonical_signs(vec[:, order])
+    return vec.astype(F32), lam, vec
+
+
+def upprojection_metric(w_uk, w_uv) -> np.ndarray:
+    """Latent-space metric of the kv_b_proj up-projection, fp64.
+
+    [OSCAR-MLA] (closing paragraph, the open refinement): make the latent
+    rotation aware of the kv_b_proj up-projection, i.e. shape the INT2 error
+    in the latent directions that matter most after reconstruction.  The
+    up-projection maps a latent error e to the per-head key parts W_UK[h] e
+    and value parts W_UV[h] e, whose total squared size is e^T G e with
+    G = sum_h (W_UK[h]^T W_UK[h] + W_UV[h]^T W_UV[h]).
+    w_uk [H, d_n, r], w_uv [H, d_v, r].  Reading: keys and values weigh
+    equally and queries are not modelled; G is scaled to mean eigenvalue 1
+    (trace r), which leaves every eigenvector below unchanged.
+    """
+    r = np.asarray(w_uk).shape[-1]
+    a = np.asarray(w_uk, dtype=F64).reshape(-1, r)
+    b = np.asarray(w_uv, dtype=F64).reshape(-1, r)
+    g = a.T @ a + b.T @ b
+    return g * (r / np.trace(g))
+
+
+def symmetric_sqrt(g) -> np.ndarray:
+    """G^(1/2) of a symmetric positive semi-definite matrix (eigh, fp64)."""
+    lam, vec = np.linalg.eigh(np.asarray(g, dtype=F64))
+    return (vec * np.sqrt(np.maximum(lam, 0.0))) @ vec.T
+
+
+def calibrate_rotation_weighted(c_cal, w_uk, w_uv):
+    """Up-projection-aware rotation (reading of the open refinement).
+
+    [OSCAR-MLA] names, without fixing it, a rotation aware of the kv_b_proj
+    up-projection.  Reading: weight the latent covariance by the
+    up-projection's metric, Sigma_w = G^(1/2) Sigma G^(1/2) (the covariance
+    of the latent measured in the metric in which reconstruction errors are
+    counted), and take its eigenvectors by ascending eigenvalue with the same
+    sign rule as calibrate_rotation.  The result is orthogonal, so the cache
+    format, the clip fit and decode are unchanged, and for G proportional to
+    the identity it is the unweighted rotation.  Parity unpinned against the
+    pages (they give no formula or numbers for it).
+    Returns (R float32, eigenvalues of Sigma_w float64, R float64).
+    """
+    sigma = latent_covariance(c_cal)
+    s = symmetric_sqrt(upprojection_metric(w_uk, w_uv))
+    sw = s @ sigma @ s
+    sw = 0.5 * (sw + sw.T)
+    lam, vec = np.linalg.eigh(sw)
     order = np.argsort(lam, kind="stable")
     lam = lam[order]
     vec = canonical_signs(vec[:, order])

@@ -98,3 +98,81 @@ def test_rotate_exact_then_single_rounding():
             exact = sum(Fraction(float(c[t, i])) * Fraction(float(Ra[i, j]))
                         for i in range(r))
             assert z[t, j] == np.float32(float(exact))
+
+
+# ---------------------------------------------------------------------------
+# up-projection-aware rotation (a reading of the open refinement)
+# ---------------------------------------------------------------------------
+
+def _orthonormal_rows_weights(rng, H, d, r):
+    """W_UK / W_UV whose stacked rows are orthonormal columns' transposes:
+    sum_h W[h]^T W[h] = I (needs H * d >= r)."""
+    q, _ = np.linalg.qr(rng.standard_normal((H * d, r)))
+    return q.reshape(H, d, r)
+
+
+def test_weighted_rotation_reduces_to_plain_for_isotropic_upprojection():
+    """G proportional to the identity: the weighted rotation is the OSCAR rotation."""
+    rng = np.random.default_rng(21)
+    r, n = 32, 400
+    c = rng.standard_normal((n, r)) * np.exp(np.linspace(-3, 0, r))
+    w_uk = _orthonormal_rows_weights(rng, 4, 8, r) * 3.0   # sum W^T W = 9 I
+    w_uv = _orthonormal_rows_weights(rng, 4, 8, r) * 3.0
+    g = O.upprojection_metric(w_uk, w_uv)
+    assert np.allclose(g, np.eye(r), atol=1e-12)
+    _, lam_p, R_p = O.calibrate_rotation(c)
+    _, lam_w, R_w = O.calibrate_rotation_weighted(c, w_uk, w_uv)
+    assert np.allclose(R_w, R_p, atol=1e-10)
+    assert np.allclose(lam_w, lam_p, rtol=1e-10)
+
+
+def test_weighted_rotation_commuting_closed_form():
+    """Sigma = Q diag(s) Q^T and G = Q diag(g) Q^T share eigenvectors, so
+    Sigma_w = Q diag(s g) Q^T: the columns are Q's, ordered by s*g ascending."""
+    rng = np.random.default_rng(22)
+    r = 12
+    Q, _ = np.linalg.qr(rng.standard_normal((r, r)))
+    s = np.exp(rng.uniform(-4, 0, r))
+    gdiag = rng.uniform(0.1, 3.0, r)
+    # latents with covariance exactly Q diag(s) Q^T: a whitened sample
+    n = 3 * r
+    x = rng.standard_normal((n, r))
+    x = x @ np.linalg.inv(np.linalg.cholesky(x.T @ x / n)).T     # x^T x / n = I
+    c = (x * np.sqrt(s)) @ Q.T
+    # weights with G = Q diag(g) Q^T: W_UK rows = diag(sqrt(g)) Q^T, W_UV = 0
+    w_uk = (np.sqrt(gdiag)[:, None] * Q.T).reshape(1, r, r)
+    w_uv = np.zeros((1, 1, r))
+    _, lam, R = O.calibrate_rotation_weighted(c, w_uk, w_uv)
+    gn = gdiag * (r / gdiag.sum())                  # the metric's scaling
+    order = np.argsort(s * gn)
+    assert np.allclose(lam, (s * gn)[order], rtol=1e-9)
+    for j, k in enumerate(order):
+        assert abs(abs(R[:, j] @ Q[:, k]) - 1.0) < 1e-9
+
+
+def test_weighted_rotation_invariants():
+    rng = np.random.default_rng(23)
+    w = S.WORKLOADS[0]
+    st = S.streams(0)
+    model = S.latent_model(w, st)
+    c = S.calib_latents(w, st, model)
+    w_uk, w_uv = S.weights(w, st)
+    R32, lam, R = O.calibrate_rotation_weighted(c, w_uk, w_uv)
+    r = R.shape[0]
+    assert np.max(np.abs(R.T @ R - np.eye(r))) < 1e-12
+    assert np.all(np.diff(lam) >= 0)
+    # R diagonalises G^(1/2) Sigma G^(1/2), computed here from its parts
+    g = O.upprojection_metric(w_uk, w_uv)
+    ev, evec = np.linalg.eigh(g)
+    gh = evec @ np.diag(np.sqrt(ev)) @ evec.T
+    assert np.max(np.abs(gh @ gh - g)) < 1e-10
+    cc = np.asarray(c, np.float64)
+    sw = gh @ (cc.T @ cc / cc.shape[0]) @ gh
+    d = R.T @ sw @ R
+    off = d - np.diag(np.diag(d))
+    assert np.max(np.abs(off)) < 1e-10 * np.max(np.abs(sw))
+    assert np.allclose(np.diag(d), lam, rtol=1e-9, atol=1e-14)
+    # sign rule
+    for j in range(r):
+        assert R[np.argmax(np.abs(R[:, j])), j] > 0
+    assert R32.dtype == np.float32
