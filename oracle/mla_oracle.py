@@ -140,28 +140,40 @@ def upprojection_metric(w_uk, w_uv) -> np.ndarray:
     return g * (r / np.trace(g))
 
 
-def symmetric_sqrt(g) -> np.ndarray:
-    """G^(1/2) of a symmetric positive semi-definite matrix (eigh, fp64)."""
+METRIC_RIDGE = 1e-8   # added to G's eigenvalues (G has mean eigenvalue 1)
+
+
+def metric_inv_sqrt(g) -> np.ndarray:
+    """(G + ridge I)^(-1/2) of the symmetric positive semi-definite metric (eigh, fp64).
+
+    Reading: a ridge of 1e-8 of the mean eigenvalue keeps latent directions
+    the up-projection ignores finite (they get the largest weighted variance
+    and end in the coarsest groups).
+    """
     lam, vec = np.linalg.eigh(np.asarray(g, dtype=F64))
-    return (vec * np.sqrt(np.maximum(lam, 0.0))) @ vec.T
+    return (vec / np.sqrt(np.maximum(lam, 0.0) + METRIC_RIDGE)) @ vec.T
 
 
 def calibrate_rotation_weighted(c_cal, w_uk, w_uv):
     """Up-projection-aware rotation (reading of the open refinement).
 
     [OSCAR-MLA] names, without fixing it, a rotation aware of the kv_b_proj
-    up-projection.  Reading: weight the latent covariance by the
-    up-projection's metric, Sigma_w = G^(1/2) Sigma G^(1/2) (the covariance
-    of the latent measured in the metric in which reconstruction errors are
-    counted), and take its eigenvectors by ascending eigenvalue with the same
-    sign rule as calibrate_rotation.  The result is orthogonal, so the cache
-    format, the clip fit and decode are unchanged, and for G proportional to
-    the identity it is the unweighted rotation.  Parity unpinned against the
-    pages (they give no formula or numbers for it).
+    up-projection that shapes the INT2 error toward the latent directions
+    that matter least after reconstruction.  Reading: take the eigenvectors,
+    by ascending eigenvalue and with calibrate_rotation's sign rule, of
+    Sigma_w = G^(-1/2) Sigma G^(-1/2), the latent covariance measured against
+    the up-projection's metric G.  Directions the up-projection amplifies get
+    a small weighted variance and share the first, finest INT2 groups; those
+    it ignores come last.  The result is orthogonal, so the cache format, the
+    clip fit and decode are unchanged, and for G proportional to the identity
+    it is the unweighted rotation.  (Of the weightings tried on synthetic
+    up-projections that amplify a few latent directions, this one gave the
+    lowest reconstruction error in G's metric; G^(1/2) Sigma G^(1/2) made it
+    worse than no weighting.)  Parity unpinned against the pages.
     Returns (R float32, eigenvalues of Sigma_w float64, R float64).
     """
     sigma = latent_covariance(c_cal)
-    s = symmetric_sqrt(upprojection_metric(w_uk, w_uv))
+    s = metric_inv_sqrt(upprojection_metric(w_uk, w_uv))
     sw = s @ sigma @ s
     sw = 0.5 * (sw + sw.T)
     lam, vec = np.linalg.eigh(sw)

@@ -123,12 +123,13 @@ def test_weighted_rotation_reduces_to_plain_for_isotropic_upprojection():
     _, lam_p, R_p = O.calibrate_rotation(c)
     _, lam_w, R_w = O.calibrate_rotation_weighted(c, w_uk, w_uv)
     assert np.allclose(R_w, R_p, atol=1e-10)
-    assert np.allclose(lam_w, lam_p, rtol=1e-10)
+    assert np.allclose(lam_w, lam_p / (1.0 + O.METRIC_RIDGE), rtol=1e-10)
 
 
 def test_weighted_rotation_commuting_closed_form():
     """Sigma = Q diag(s) Q^T and G = Q diag(g) Q^T share eigenvectors, so
-    Sigma_w = Q diag(s g) Q^T: the columns are Q's, ordered by s*g ascending."""
+    Sigma_w = Q diag(s / (g + ridge)) Q^T: the columns are Q's, ordered by
+    s / g ascending."""
     rng = np.random.default_rng(22)
     r = 12
     Q, _ = np.linalg.qr(rng.standard_normal((r, r)))
@@ -144,8 +145,9 @@ def test_weighted_rotation_commuting_closed_form():
     w_uv = np.zeros((1, 1, r))
     _, lam, R = O.calibrate_rotation_weighted(c, w_uk, w_uv)
     gn = gdiag * (r / gdiag.sum())                  # the metric's scaling
-    order = np.argsort(s * gn)
-    assert np.allclose(lam, (s * gn)[order], rtol=1e-9)
+    wv = s / (gn + O.METRIC_RIDGE)
+    order = np.argsort(wv)
+    assert np.allclose(lam, wv[order], rtol=1e-9)
     for j, k in enumerate(order):
         assert abs(abs(R[:, j] @ Q[:, k]) - 1.0) < 1e-9
 
@@ -161,11 +163,11 @@ def test_weighted_rotation_invariants():
     r = R.shape[0]
     assert np.max(np.abs(R.T @ R - np.eye(r))) < 1e-12
     assert np.all(np.diff(lam) >= 0)
-    # R diagonalises G^(1/2) Sigma G^(1/2), computed here from its parts
+    # R diagonalises (G + ridge)^(-1/2) Sigma (G + ridge)^(-1/2), built here from its parts
     g = O.upprojection_metric(w_uk, w_uv)
     ev, evec = np.linalg.eigh(g)
-    gh = evec @ np.diag(np.sqrt(ev)) @ evec.T
-    assert np.max(np.abs(gh @ gh - g)) < 1e-10
+    gh = evec @ np.diag(1.0 / np.sqrt(ev + O.METRIC_RIDGE)) @ evec.T
+    assert np.max(np.abs(np.linalg.inv(gh @ gh) - (g + O.METRIC_RIDGE * np.eye(len(g))))) < 1e-8
     cc = np.asarray(c, np.float64)
     sw = gh @ (cc.T @ cc / cc.shape[0]) @ gh
     d = R.T @ sw @ R
@@ -176,3 +178,55 @@ def test_weighted_rotation_invariants():
     for j in range(r):
         assert R[np.argmax(np.abs(R[:, j])), j] > 0
     assert R32.dtype == np.float32
+
+
+def test_weighted_rotation_effect_on_upprojected_error():
+    """What the weighting is for (a directional check, not a pin): with an
+    up-projection that amplifies a few latent directions, the INT2 error of
+    the reconstruction, counted in the up-projection's metric, is lower with
+    the weighted rotation than with the unweighted one."""
+    rng = np.random.default_rng(24)
+    r, G = 64, 16
+    w = S.WORKLOADS[0]
+    st = S.streams(0)
+    model = S.latent_model(w, st)
+    c_cal = S.calib_latents(w, st, model)
+    c_test = model.sample(rng, 512)
+    # up-projection: random, with 8 latent directions amplified 30x
+    w_uk = rng.standard_normal((4, 32, r)) / 8
+    w_uv = rng.standard_normal((4, 32, r)) / 8
+    boost = np.ones(r)
+    boost[rng.choice(r, 8, replace=False)] = 30.0
+    Qb, _ = np.linalg.qr(rng.standard_normal((r, r)))
+    amp = Qb @ np.diag(boost) @ Qb.T
+    w_uk, w_uv = w_uk @ amp, w_uv @ amp
+    g = O.upprojection_metric(w_uk, w_uv)
+
+    def err(R32):
+        Ra = O.rotation_apply(R32)
+        alpha, _ = O.fit_clip(c_cal, R32, G)
+        q = O.quantize_cache(c_test, Ra, alpha, G)
+        zh = O.dequantize(q["codes"], q["scale_h"], q["zero_h"], G)
+        e = O.unrotate(zh, Ra) - np.asarray(c_test, np.float64)
+        return float(np.mean(np.einsum("ni,ij,nj->n", e, g, e)))
+
+    e_plain = err(O.calibrate_rotation(c_cal)[0])
+    e_weighted = err(O.calibrate_rotation_weighted(c_cal, w_uk, w_uv)[0])
+    print(f"up-projected INT2 error: unweighted {e_plain:.4g}, weighted {e_weighted:.4g}")
+    assert e_weighted < e_plain
+
+
+def test_upprojection_metric_is_the_reconstruction_norm():
+    """e^T G e is the squared size of the up-projected error, summed over
+    heads' key and value parts (explicit per-head products), scaled by
+    r / (sum of squared weights)."""
+    rng = np.random.default_rng(25)
+    H, dn, dv, r = 3, 5, 7, 11
+    w_uk = rng.standard_normal((H, dn, r))
+    w_uv = rng.standard_normal((H, dv, r))
+    g = O.upprojection_metric(w_uk, w_uv)
+    scale = r / (np.sum(w_uk ** 2) + np.sum(w_uv ** 2))
+    for _ in range(5):
+        e = rng.standard_normal(r)
+        direct = sum(np.sum((w_uk[h] @ e) ** 2) + np.sum((w_uv[h] @ e) ** 2) for h in range(H))
+        assert np.isclose(e @ g @ e, scale * direct, rtol=1e-12)
