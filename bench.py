@@ -125,11 +125,23 @@ def main():
     model = S.latent_model(w, st)
     c_cal = S.calib_latents(w, st, model)
     c_cal_d = bf(c_cal)
+    w_uk, w_uv = S.weights(w, st)
+    # calibration (synchronous calls, timed on the host clock: set-up, not
+    # part of the step)
+    t = time.perf_counter()
     R, _ = M.mla_calibrate_rotation(d, c_cal_d)
+    t_rot = time.perf_counter() - t
+    t = time.perf_counter()
+    M.mla_calibrate_rotation_weighted(d, c_cal_d, bf(w_uk), bf(w_uv))
+    t_rotw = time.perf_counter() - t
     Rt = M.mla_prepare_rotation(d, R)
     grid = [1.0 - 0.05 * k for k in range(11)]
+    torch.cuda.synchronize()
+    t = time.perf_counter()
     alpha, _ = M.mla_fit_clip(d, c_cal_d, Rt, grid)
-    w_uk, w_uv = S.weights(w, st)
+    t_clip = time.perf_counter() - t
+    calibration = {"calib_tokens": int(c_cal.shape[0]), "rotation_ms": round(t_rot * 1e3, 2),
+                   "rotation_weighted_ms": round(t_rotw * 1e3, 2), "fit_clip_ms": round(t_clip * 1e3, 2)}
     uk_f, uv_f = M.mla_fold_absorb_weights(d, bf(w_uk), bf(w_uv), Rt)
 
     lens = S.seq_lens(w, st)
@@ -267,6 +279,7 @@ def main():
         "hbm_frac_step": round(value / PEAK_HBM_GBS, 4),
         "kernel_us": kernels,
         "append_prefill": append_prefill,
+        "calibration": calibration,
         "roofline": roofline,
     }
 

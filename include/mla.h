@@ -109,6 +109,38 @@ mla_status mla_calibrate_rotation(const mla_dims *dims, const void *c_cal,
                                   double *eig_out, void *stream);
 
 /* ------------------------------------------------------------------------
+ * mla_calibrate_rotation_weighted — up-projection-aware rotation
+ *
+ * [OSCAR issue #10, maintainer reply, closing paragraph]: the open
+ * refinement is a latent rotation aware of the kv_b_proj up-projection, so
+ * that the INT2 error lands in the latent directions that matter least
+ * after reconstruction.  The page gives no formula; this entry point
+ * implements one reading: with G = sum_h (W_UK[h]^T W_UK[h] +
+ * W_UV[h]^T W_UV[h]) (the metric in which the up-projection counts latent
+ * errors, scaled to trace r) and Sigma the uncentred latent covariance as
+ * in mla_calibrate_rotation, R holds the eigenvectors of
+ * (G + 1e-8 I)^(-1/2) Sigma (G + 1e-8 I)^(-1/2) by ascending eigenvalue,
+ * signed as there: directions the up-projection amplifies share the first,
+ * finest INT2 groups.  R is orthogonal, so mla_prepare_rotation,
+ * mla_fit_clip, mla_fold_absorb_weights, the cache format and decode are
+ * used unchanged; for G proportional to the identity R equals
+ * mla_calibrate_rotation's.
+ *   c_cal    device [n_cal][r], bf16 or fp32 (dtype)
+ *   w_uk     device [H][d_n][r] bf16 (un-folded W_UK)
+ *   w_uv     device [H][d_v][r] bf16 (un-folded W_UV)
+ *   R_out    device [r][r] fp32, layout as in mla_calibrate_rotation
+ *   eig_out  host [r] fp64 eigenvalues of the weighted covariance, ascending
+ *            (may be NULL)
+ * Synchronous: returns after R_out is written.  Allocates device scratch.
+ * Errors: INVALID_ARG (n_cal < 1, NULL pointers, dims), NUMERIC (zero or
+ * non-finite weights, non-finite covariance, no convergence), HIP.
+ * ---------------------------------------------------------------------- */
+mla_status mla_calibrate_rotation_weighted(const mla_dims *dims, const void *c_cal,
+                                           mla_dtype dtype, int64_t n_cal,
+                                           const uint16_t *w_uk, const uint16_t *w_uv,
+                                           float *R_out, double *eig_out, void *stream);
+
+/* ------------------------------------------------------------------------
  * mla_prepare_rotation — the rotation as applied: R_apply = bf16(R)
  *
  * Writes R_apply_t[j*r + i] = bf16_round_nearest_even(R[i*r + j]) (the

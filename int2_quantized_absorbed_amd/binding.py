@@ -45,6 +45,8 @@ class mla_cache(ctypes.Structure):
 _P = ctypes.c_void_p
 _SIGS = {
     "mla_calibrate_rotation": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, ctypes.c_int, ctypes.c_int64, _P, _P, _P]),
+    "mla_calibrate_rotation_weighted": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, ctypes.c_int, ctypes.c_int64,
+                                                      _P, _P, _P, _P, _P]),
     "mla_prepare_rotation": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, _P, _P]),
     "mla_fit_clip": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, ctypes.c_int, ctypes.c_int64, _P, _P,
                                     ctypes.c_int32, _P, _P, _P]),
@@ -190,6 +192,25 @@ def mla_calibrate_rotation(dims: Dims, c_cal: torch.Tensor):
     st = lib().mla_calibrate_rotation(ctypes.byref(d), _ptr(c_cal), _dtype_code(c_cal), c_cal.shape[0],
                                       _ptr(R), eig.ctypes.data_as(ctypes.c_void_p), _stream())
     _check(st, "mla_calibrate_rotation")
+    return R, eig
+
+
+def mla_calibrate_rotation_weighted(dims: Dims, c_cal: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor):
+    """Up-projection-aware rotation.  w_uk [H, d_n, r] and w_uv [H, d_v, r] bf16
+    (un-folded).  Returns (R [r, r] fp32 device tensor, eigenvalues float64 numpy [r])."""
+    r, H = dims.kv_lora_rank, dims.num_heads
+    _need(c_cal, "c_cal", (torch.bfloat16, torch.float32))
+    if c_cal.dim() != 2 or c_cal.shape[1] != r:
+        raise ValueError("c_cal must be [n_cal, kv_lora_rank]")
+    _need(w_uk, "w_uk", torch.bfloat16, (H, dims.qk_nope_head_dim, r))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, dims.v_head_dim, r))
+    R = torch.empty((r, r), dtype=torch.float32, device=c_cal.device)
+    eig = np.empty(r, dtype=np.float64)
+    d = dims.c()
+    st = lib().mla_calibrate_rotation_weighted(ctypes.byref(d), _ptr(c_cal), _dtype_code(c_cal), c_cal.shape[0],
+                                               _ptr(w_uk), _ptr(w_uv), _ptr(R),
+                                               eig.ctypes.data_as(ctypes.c_void_p), _stream())
+    _check(st, "mla_calibrate_rotation_weighted")
     return R, eig
 
 

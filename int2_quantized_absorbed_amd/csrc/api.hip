@@ -289,6 +289,93 @@ mla_status mla_calibrate_rotation(const mla_dims *dims, const void *c_cal, mla_d
   return MLA_OK;
 }
 
+mla_status mla_calibrate_rotation_weighted(const mla_dims *dims, const void *c_cal, mla_dtype dtype,
+                                           int64_t n_cal, const uint16_t *w_uk, const uint16_t *w_uv,
+                                           float *R_out, double *eig_out, void *stream) {
+  std::string why;
+  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "mla_calibrate_rotation_weighted: " + why);
+  if (c_cal == nullptr || w_uk == nullptr || w_uv == nullptr || R_out == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "mla_calibrate_rotation_weighted: NULL device pointer");
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_FP32)
+    return fail(MLA_ERR_INVALID_ARG, "mla_calibrate_rotation_weighted: dtype must be bf16 or fp32");
+  if (n_cal < 1) return fail(MLA_ERR_INVALID_ARG, "mla_calibrate_rotation_weighted: n_cal must be >= 1");
+  const int r = dims->kv_lora_rank;
+  if (r > 4096) return fail(MLA_ERR_UNSUPPORTED, "mla_calibrate_rotation_weighted: kv_lora_rank > 4096");
+  const int64_t n_uk = static_cast<int64_t>(dims->num_heads) * dims->qk_nope_head_dim;
+  const int64_t n_uv = static_cast<int64_t>(dims->num_heads) * dims->v_head_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t rr = static_cast<size_t>(r) * r;
+  double *d_all = nullptr;
+  MLA_HIP_CHECK(hipMalloc(&d_all, 3 * rr * sizeof(double)), "hipMalloc(covariances)");
+  std::vector<double> sig(rr), guk(rr), guv(rr);
+  // Sigma = C^T C / n over the calibration latents; W^T W / rows for the
+  // stacked rows of W_UK and of W_UV (the same fp64 covariance kernel)
+  hipError_t e = launch_covariance(c_cal, dtype, n_cal, r, d_all, s);
+  if (e == hipSuccess) e = launch_covariance(w_uk, MLA_DTYPE_BF16, n_uk, r, d_all + rr, s);
+  if (e == hipSuccess) e = launch_covariance(w_uv, MLA_DTYPE_BF16, n_uv, r, d_all + 2 * rr, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(sig.data(), d_all, rr * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(guk.data(), d_all + rr, rr * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(guv.data(), d_all + 2 * rr, rr * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(d_all);
+  if (e != hipSuccess) return hip_fail(e, "mla_calibrate_rotation_weighted: covariances");
+  // G = sum_h W_UK[h]^T W_UK[h] + W_UV[h]^T W_UV[h], scaled to trace r
+  std::vector<double> g(rr);
+  double tr = 0.0;
+  for (size_t i = 0; i < rr; ++i) g[i] = guk[i] * static_cast<double>(n_uk) + guv[i] * static_cast<double>(n_uv);
+  for (int i = 0; i < r; ++i) tr += g[static_cast<size_t>(i) * r + i];
+  if (!(tr > 0.0) || !std::isfinite(tr))
+    return fail(MLA_ERR_NUMERIC, "mla_calibrate_rotation_weighted: up-projection weights are zero or not finite");
+  for (size_t i = 0; i < rr; ++i) g[i] *= static_cast<double>(r) / tr;
+  // (G + ridge I)^(-1/2) = V diag(1 / sqrt(max(lambda, 0) + ridge)) V^T; the
+  // ridge keeps latent directions the up-projection ignores finite (they get
+  // the largest weighted variance and the coarsest groups)
+  constexpr double kMetricRidge = 1e-8;  // G has mean eigenvalue 1
+  std::vector<double> gv(r), gvec(rr), gh(rr, 0.0), tmp(rr, 0.0), sw(rr, 0.0);
+  if (!eigh_ascending(r, g.data(), gv.data(), gvec.data()))
+    return fail(MLA_ERR_NUMERIC, "mla_calibrate_rotation_weighted: eigensolver did not converge on the metric");
+  for (int k = 0; k < r; ++k) {
+    const double sq = 1.0 / std::sqrt(std::max(gv[k], 0.0) + kMetricRidge);
+    for (int i = 0; i < r; ++i) {
+      const double vik = gvec[static_cast<size_t>(i) * r + k] * sq;
+      if (vik == 0.0) continue;
+      double *row = gh.data() + static_cast<size_t>(i) * r;
+      for (int j = 0; j < r; ++j) row[j] += vik * gvec[static_cast<size_t>(j) * r + k];
+    }
+  }
+  // Sigma_w = G^(-1/2) Sigma G^(-1/2), symmetrised
+  auto matmul = [r](const std::vector<double> &a, const std::vector<double> &b, std::vector<double> &c) {
+    std::fill(c.begin(), c.end(), 0.0);
+    for (int i = 0; i < r; ++i)
+      for (int k = 0; k < r; ++k) {
+        const double aik = a[static_cast<size_t>(i) * r + k];
+        if (aik == 0.0) continue;
+        const double *brow = b.data() + static_cast<size_t>(k) * r;
+        double *crow = c.data() + static_cast<size_t>(i) * r;
+        for (int j = 0; j < r; ++j) crow[j] += aik * brow[j];
+      }
+  };
+  matmul(gh, sig, tmp);
+  matmul(tmp, gh, sw);
+  for (int i = 0; i < r; ++i)
+    for (int j = i + 1; j < r; ++j) {
+      const double m = 0.5 * (sw[static_cast<size_t>(i) * r + j] + sw[static_cast<size_t>(j) * r + i]);
+      sw[static_cast<size_t>(i) * r + j] = m;
+      sw[static_cast<size_t>(j) * r + i] = m;
+    }
+  std::vector<double> vals(r), vecs(rr);
+  if (!eigh_ascending(r, sw.data(), vals.data(), vecs.data()))
+    return fail(MLA_ERR_NUMERIC, "mla_calibrate_rotation_weighted: non-finite covariance or eigensolver did not converge");
+  std::vector<float> R(rr);
+  for (size_t i = 0; i < rr; ++i) R[i] = static_cast<float>(vecs[i]);
+  MLA_HIP_CHECK(hipMemcpyAsync(R_out, R.data(), rr * sizeof(float), hipMemcpyHostToDevice, s),
+                "mla_calibrate_rotation_weighted: copy R");
+  MLA_HIP_CHECK(hipStreamSynchronize(s), "mla_calibrate_rotation_weighted: synchronize");
+  if (eig_out != nullptr) std::memcpy(eig_out, vals.data(), sizeof(double) * r);
+  clear_error();
+  return MLA_OK;
+}
+
 mla_status mla_prepare_rotation(const mla_dims *dims, const float *R, uint16_t *R_apply_t, void *stream) {
   std::string why;
   if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "mla_prepare_rotation: " + why);

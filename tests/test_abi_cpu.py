@@ -112,6 +112,12 @@ def test_calibration_argument_checks():
     P = ctypes.c_void_p(256)
     assert lib.mla_calibrate_rotation(ctypes.byref(d), P, 0, 0, P, None, None) == Bd.MLA_ERR_INVALID_ARG
     assert lib.mla_calibrate_rotation(ctypes.byref(d), P, 5, 10, P, None, None) == Bd.MLA_ERR_INVALID_ARG
+    W = lib.mla_calibrate_rotation_weighted
+    assert W(ctypes.byref(d), P, 0, 0, P, P, P, None, None) == Bd.MLA_ERR_INVALID_ARG      # n_cal < 1
+    assert W(ctypes.byref(d), P, 5, 10, P, P, P, None, None) == Bd.MLA_ERR_INVALID_ARG     # dtype
+    assert W(ctypes.byref(d), P, 0, 10, None, P, P, None, None) == Bd.MLA_ERR_INVALID_ARG  # w_uk NULL
+    assert W(ctypes.byref(d), P, 0, 10, P, None, P, None, None) == Bd.MLA_ERR_INVALID_ARG  # w_uv NULL
+    assert W(None, P, 0, 10, P, P, P, None, None) == Bd.MLA_ERR_INVALID_ARG                # dims NULL
     grid = (ctypes.c_float * 2)(1.0, 1.5)
     assert lib.mla_fit_clip(ctypes.byref(d), P, 0, 10, P, grid, 2, P, None, None) == Bd.MLA_ERR_INVALID_ARG
     assert lib.mla_fit_clip(ctypes.byref(d), P, 0, 10, P, grid, 0, P, None, None) == Bd.MLA_ERR_INVALID_ARG

@@ -44,6 +44,32 @@ def test_calibrate_rotation(wid):
     assert np.max(np.abs(R64.T @ R64 - np.eye(w.kv_lora_rank))) <= 1e-6
 
 
+@pytest.mark.parametrize("wid", [0, 1])
+def test_calibrate_rotation_weighted(wid):
+    """Up-projection-aware rotation against the oracle (same reading): columns
+    equal up to sign, eigenvalues to 1e-6 relative."""
+    w = S.WORKLOADS[wid]
+    C.say(f"calibrate_rotation_weighted workload {wid}")
+    st = S.streams(w.wid)
+    model = S.latent_model(w, st)
+    c_cal = S.calib_latents(w, st, model)
+    w_uk, w_uv = S.weights(w, st)
+    _, lam_o, R_o = O.calibrate_rotation_weighted(c_cal, w_uk, w_uv)
+    d = C.dims_of(w)
+    R_g, lam_g = M.mla_calibrate_rotation_weighted(d, C.latent_tensor(c_cal, w.latent_dtype), C.t_bf16(w_uk),
+                                                   C.t_bf16(w_uv))
+    R_g = R_g.cpu().numpy().astype(np.float64)
+    assert np.allclose(lam_g, lam_o, rtol=1e-6, atol=1e-9 * np.max(np.abs(lam_o)))
+    # well-separated eigenvalues: the column itself is fixed up to sign
+    gaps = np.diff(lam_o)
+    sep = np.ones_like(lam_o, dtype=bool)
+    sep[1:] &= gaps > 1e-6 * lam_o[-1]
+    sep[:-1] &= gaps > 1e-6 * lam_o[-1]
+    dots = np.abs(np.sum(R_g * R_o, axis=0))
+    assert np.all(dots[sep] > 1 - 1e-5), dots[sep].min()
+    assert np.max(np.abs(R_g.T @ R_g - np.eye(R_g.shape[0]))) < 1e-5
+
+
 def test_prepare_rotation_bit_exact():
     w = S.WORKLOADS[1]
     rng = np.random.default_rng(3)
