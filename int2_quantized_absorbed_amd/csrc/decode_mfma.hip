@@ -36,7 +36,11 @@ constexpr int DR = 64;
 constexpr int ROWS = 64;        // query rows per workgroup
 constexpr int TT = 32;          // tokens per tile
 constexpr int KB = 9;           // K-blocks of 16 per wave: 8 latent + 1 rope
-constexpr int ZSTRIDE = 144;    // halves per token row of the Z tile (128 + pad)
+// Z tile rows: 128 halves + 16 pad, so the four rows a transposing load
+// reads fall in separate banks.  16-byte chunk c of row t is stored at chunk
+// c ^ ((t >> 3) & 1): without it, the 16-byte stores of tokens t and t + 8
+// hit the same banks.
+constexpr int ZSTRIDE = 144;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -68,8 +72,34 @@ __device__ __forceinline__ void agpr_scale(float &x, float al) {
       : "v"(al));
 }
 
+// The hardware does not interlock a register an MFMA is still writing
+// against a later non-MFMA read, and the compiler does not see into inline
+// asm, so asm that reads MFMA results must first wait the XDL write -> read
+// latency itself: 24 wait states cover an 8-pass MFMA with margin.  Taking
+// both accumulator tuples as operands orders this after their last MFMA and
+// every asm read of them after this.
+__device__ __forceinline__ void mfma_results_settle(f32x16 &a0, f32x16 &a1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a0), "+a"(a1));
+}
+
+// The same for the eight output accumulators before the rescale reads them
+// (kAfterMfma) and, after the rescale's asm wrote them, before the next MFMA
+// takes them as its accumulator input.
+template <bool kAfterMfma>
+__device__ __forceinline__ void o_settle(f32x16 (&o)[2][4]) {
+  if (kAfterMfma)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]), "+a"(o[1][0]), "+a"(o[1][1]),
+                   "+a"(o[1][2]), "+a"(o[1][3]));
+  else
+    asm volatile("s_nop 4"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]), "+a"(o[1][0]), "+a"(o[1][1]),
+                   "+a"(o[1][2]), "+a"(o[1][3]));
+}
+
 // LDS store of a value the MFMA left in an AGPR (gfx950 DS stores take AGPR
 // data), without a copy through a VGPR; the byte offset is an immediate.
+// Call mfma_results_settle on the accumulators first.
 template <int OFF>
 __device__ __forceinline__ void ds_store_agpr(uint32_t lds_addr, float x) {
   asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(lds_addr), "a"(x), "i"(OFF) : "memory");
@@ -91,10 +121,10 @@ __device__ __forceinline__ float reduce4(float x) {
 
 // Channel of latent K-slot e (0..7) in K-block kb (0..7) for lane half hf,
 // relative to the wave's first channel.  Matches the dequantisation below:
-// half2 j of block kb holds the codes of channels 16*(kb/2) + 4*(kb%2) + j
-// and that + 8.
+// half2 j of block kb comes from byte j of code word kb/2 (channels
+// 16*(kb/2) + 4j .. + 3), taking its channels kb%2 and kb%2 + 2.
 __device__ __forceinline__ int slot_channel(int hf, int kb, int e) {
-  return 64 * hf + 16 * (kb >> 1) + 4 * (kb & 1) + (e >> 1) + 8 * (e & 1);
+  return 64 * hf + 16 * (kb >> 1) + 4 * (e >> 1) + (kb & 1) + 2 * (e & 1);
 }
 
 constexpr int SPSTRIDE = 68;    // floats per accumulator slot row (64 lanes + pad: rows skew by 4 banks)
@@ -133,29 +163,37 @@ __device__ __forceinline__ RawTile load_tile(const DecodeArgs &a, int64_t slot, 
   return t;
 }
 
-// codes -> fp16 score B operands.  Per pair of channels: shift, one
-// v_and_or_b32 building (1024 + c) in both halves, subtract 1024 (exact),
-// one fused fp16 multiply-add with the group's (scale, zero).
+// Code byte pair -> exact fp16 pair: with every 2-bit code alone in a
+// nibble (bits 2-3 clear) the nibble is an OCP e2m1 number of value c/2,
+// and gfx950's packed fp4 -> f16 conversion with scale 2 returns (c_lo, c_hi)
+// exactly (low nibble in the low half).
+template <int BYTE>
+__device__ __forceinline__ f16x2 code_pair(uint32_t nibbles) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nibbles, 2.0f, BYTE);
+}
+
+// codes -> fp16 score B operands.  Per code word (16 channels): two masks
+// split the codes of channels (4j, 4j+2) and (4j+1, 4j+3) into nibbles, then
+// per pair one conversion and one fused fp16 multiply-add with the group's
+// (scale, zero): z_hat = zero + scale * c with one rounding.
 template <int G>
-__device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB], uint32_t mask2, f16x2 k1024) {
+__device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB]) {
   const uint32_t cws[4] = {t.codes.x, t.codes.y, t.codes.z, t.codes.w};
   const uint32_t szw[4] = {t.sz.x, t.sz.y, t.sz.z, t.sz.w};
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    const int q = kb >> 1;
+  for (int q = 0; q < 4; ++q) {
     const uint32_t sz = szw[(G == 32) ? (q >> 1) : q];
     const f16x2 sc = __builtin_bit_cast(f16x2, (sz & 0xffffu) * 0x10001u);
     const f16x2 zr = __builtin_bit_cast(f16x2, (sz >> 16) * 0x10001u);
-    f16x8 v;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t x = ((cws[q] >> (2 * (4 * (kb & 1) + j))) & mask2) | 0x64006400u;
-      const f16x2 c = __builtin_bit_cast(f16x2, x) + k1024;     // exact small integers
-      const f16x2 z2 = __builtin_elementwise_fma(c, sc, zr);   // one rounding
-      v[2 * j] = z2[0];
-      v[2 * j + 1] = z2[1];
+    for (int odd = 0; odd < 2; ++odd) {
+      const uint32_t u = (cws[q] >> (2 * odd)) & 0x33333333u;
+      const f16x2 c0 = __builtin_elementwise_fma(code_pair<0>(u), sc, zr);
+      const f16x2 c1 = __builtin_elementwise_fma(code_pair<1>(u), sc, zr);
+      const f16x2 c2 = __builtin_elementwise_fma(code_pair<2>(u), sc, zr);
+      const f16x2 c3 = __builtin_elementwise_fma(code_pair<3>(u), sc, zr);
+      bz[2 * q + odd] = f16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
     }
-    bz[kb] = v;
   }
   const uint32_t rws[4] = {t.rope.x, t.rope.y, t.rope.z, t.rope.w};
   f16x8 v;
@@ -209,6 +247,10 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   const int s_lim = min(it.t1, s_vis);   // tokens < s_lim are visible to this row
   const int s_off = 32 * s_hf + 8 * s_k8;
   float m_run = -INFINITY, l_run = 0.0f;
+  // tiles [0, full_tiles) are visible to every row of this wave: no masking
+  int vmin = s_lim - it.t0;
+  for (int off = 32; off > 0; off >>= 1) vmin = min(vmin, __shfl_xor(vmin, off));
+  const int full_tiles = __builtin_amdgcn_readfirstlane(vmin > 0 ? vmin / TT : 0);
 
   f32x16 o[2][4];
 #pragma unroll
@@ -216,12 +258,10 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x16{};
 
-  uint32_t mask2 = 0x00030003u;
-  asm volatile("" : "+v"(mask2));  // keep the mask in a VGPR: one v_and_or_b32 per pair
-  const f16x2 k1024 = {static_cast<f16>(-1024.0f), static_cast<f16>(-1024.0f)};
   const int g16 = l >> 4, s16 = l & 15;
   const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);    // transposing-load source row
-  const int pv_col = 16 * (g16 & 1) + 4 * (s16 & 3);  // and column
+  // and column (rows pv_krow + 16 ks (+ 4) share bit 3 of pv_krow: one swizzle)
+  const int pv_col = (16 * (g16 & 1) + 4 * (s16 & 3)) ^ (8 * ((g16 >> 1) & 1));
   auto tile_slot = [&](int i) -> int64_t {
     const int ti = min(i, n_tiles - 1);
     return base + min(it.t0 + ti * TT + l32, it.t1 - 1);
@@ -231,10 +271,12 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   // Z buffers, tile 1 dequantised, tile 2 in flight ----
   f16x8 bz[KB];
   f32x16 sacc[2];
+  const int zsw = 8 * ((l32 >> 3) & 1);  // chunk kb goes to kb ^ 1 in rows 8..15, 24..31
   auto store_z = [&](int zb, const f16x8 (&v)[KB]) {
     f16 *zt = sm.z[zb][w] + l32 * ZSTRIDE + 64 * hf;
+    f16 *ze = zt + zsw, *zo = zt - zsw;  // even and odd kb
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(zt + 8 * kb) = v[kb];
+    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(((kb & 1) ? zo : ze) + 8 * kb) = v[kb];
   };
   auto read_scores = [&](int sb, float (&s8)[8]) {
 #pragma unroll
@@ -250,7 +292,8 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   };
   // partial scores -> sm.sp[sb][w][slot][l], slot = 16 mt + v (32 stores
   // straight from the accumulator AGPRs)
-  auto publish = [&](int sb, const f32x16 (&acc)[2]) {
+  auto publish = [&](int sb, f32x16 (&acc)[2]) {
+    mfma_results_settle(acc[0], acc[1]);
     typedef __attribute__((address_space(3))) float lds_float;
     const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_float *)&sm.sp[sb][w][0][l]));
     constexpr int RB = SPSTRIDE * 4;  // bytes per slot row
@@ -275,7 +318,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   {
     const RawTile r0 = load_tile<G>(a, tile_slot(0), w, hf);
     const RawTile r1 = load_tile<G>(a, tile_slot(1), w, hf);
-    dequant<G>(r0, bz, mask2, k1024);
+    dequant<G>(r0, bz);
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
 #pragma unroll
@@ -285,7 +328,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
     store_z(0, bz);
     publish(0, sacc);
-    dequant<G>(r1, bz, mask2, k1024);
+    dequant<G>(r1, bz);
     store_z(1, bz);
   }
   RawTile raw = load_tile<G>(a, tile_slot(2), w, hf);
@@ -294,6 +337,16 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 
   for (int i = 0; i < n_tiles; ++i) {
     const int buf = i & 1, nb = buf ^ 1;
+    // masking first, so the score MFMAs and the softmax below stay in one
+    // basic block and can interleave
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = s_next[e];
+    if (i >= full_tiles) {
+      const int ncnt = s_lim - (it.t0 + i * TT + 8 * s_k8);  // visible tokens among my 8
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = (e < ncnt) ? s[e] : -INFINITY;
+    }
     // ---- (a) scores of tile i+1 on MFMA (harmless recompute past the end) ----
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
@@ -304,16 +357,9 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
 
     // ---- (b) online softmax of tile i (vector ALU, overlaps the MFMAs) ----
-    float s[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = s_next[e];
-    const int ncnt = s_lim - (it.t0 + i * TT + 8 * s_k8);  // visible tokens among my 8
     float tmax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      s[e] = (e < ncnt) ? s[e] : -INFINITY;
-      tmax = fmaxf(tmax, s[e]);
-    }
+    for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
     tmax = reduce4<true>(tmax);
     const bool need = tmax > m_run + kRescaleThreshold;   // true on the first visible tile
     const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
@@ -341,6 +387,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     // ---- (d) O = alpha * O + P Z for tile i ----
     const int rescale = sm.resc[buf][0] | sm.resc[buf][1] | sm.resc[buf][2] | sm.resc[buf][3];
     if (rescale) {
+      o_settle<true>(o);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -353,6 +400,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
             o[mt][nt][v] = x;
           }
         }
+      o_settle<false>(o);
     }
     const f16 *zb_base = sm.z[buf][w] + pv_krow * ZSTRIDE + pv_col;
 #pragma unroll
@@ -375,7 +423,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     // ---- (e) dequantise tile i+2 into the Z buffer tile i just used (this
     // wave's own region: its PV reads above were issued first), prefetch
     // tile i+3 and the summed partial scores of tile i+1 ----
-    dequant<G>(raw, bz, mask2, k1024);
+    dequant<G>(raw, bz);
     store_z(buf, bz);
     raw = load_tile<G>(a, tile_slot(i + 3), w, hf);
     read_scores(nb, s_next);
