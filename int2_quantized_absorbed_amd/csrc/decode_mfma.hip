@@ -12,16 +12,20 @@
 // Per 32-token tile:
 //   1. each lane loads one token's 2-bit codes for 64 channels (16 B), its
 //      groups' fp16 scale/zero and 8 rope values, and dequantises them in
-//      registers straight into the fp16 B operands of the score MFMA
+//      registers straight into the fp16 operands of the score MFMA
 //      (v_mfma_f32_32x32x16_f16): z_hat = zero + scale * code with one fp16
 //      rounding (codes enter as exact small integers);
-//   2. partial scores S_w[64 rows x 32 tokens] = Q~_w Z_w^T (K = 128 + 16);
-//   3. the partials are summed through LDS (each lane's accumulator slots
-//      line up across waves), each wave runs the online softmax for 16 rows
-//      (32-lane max/sum via DPP within 16 lanes + one lane swap), writes P^T
-//      in fp16 to LDS;
-//   4. O_w[64 x 128] += P Z_w with P and Z read back through the gfx950
+//   2. partial scores S_w^T[32 tokens x 64 rows] = Z_w Q~_w^T (K = 128 + 16),
+//      token-major so each lane's accumulator quads go to LDS as 16-byte
+//      stores;
+//   3. the four partials are summed on reading, each wave runs the online
+//      softmax for 16 rows (a row's 32 tokens on one lane quad, max and sum
+//      by DPP), writes P in fp16 to LDS;
+//   4. O_w[64 x 128] += P Z_w with Z read back through the gfx950
 //      transposing LDS load (ds_read_b64_tr_b16).
+// The tile loop is software-pipelined: the scores of tile i+1 are on the
+// MFMA pipe while the softmax of tile i runs, and their partials are
+// published while the PV of tile i runs (two LDS barriers per tile).
 // The running max is only moved when a tile's max exceeds it by more than
 // 8 (log2 units); otherwise p = 2^(s - m) <= 256 stays exact enough in fp16
 // and O needs no rescaling.
@@ -97,12 +101,12 @@ __device__ __forceinline__ void o_settle(f32x16 (&o)[2][4]) {
                    "+a"(o[1][2]), "+a"(o[1][3]));
 }
 
-// LDS store of a value the MFMA left in an AGPR (gfx950 DS stores take AGPR
-// data), without a copy through a VGPR; the byte offset is an immediate.
-// Call mfma_results_settle on the accumulators first.
+// 16-byte LDS store of four values an MFMA left in AGPRs (gfx950 DS stores
+// take AGPR data), without copies through VGPRs; the byte offset is an
+// immediate.  Call mfma_results_settle on the accumulators first.
 template <int OFF>
-__device__ __forceinline__ void ds_store_agpr(uint32_t lds_addr, float x) {
-  asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(lds_addr), "a"(x), "i"(OFF) : "memory");
+__device__ __forceinline__ void ds_store_agpr4(uint32_t lds_addr, f32x4 x) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(lds_addr), "a"(x), "i"(OFF) : "memory");
 }
 
 template <int CTRL>
@@ -127,7 +131,6 @@ __device__ __forceinline__ int slot_channel(int hf, int kb, int e) {
   return 64 * hf + 16 * (kb >> 1) + 4 * (e >> 1) + (kb & 1) + 2 * (e & 1);
 }
 
-constexpr int SPSTRIDE = 68;    // floats per accumulator slot row (64 lanes + pad: rows skew by 4 banks)
 constexpr int PRSTRIDE = 40;    // halves per row of P (32 tokens + pad)
 
 // Double-buffered tile state (one barrier per tile):
@@ -136,10 +139,10 @@ constexpr int PRSTRIDE = 40;    // halves per row of P (32 tokens + pad)
 //   p   P [row][token] (PV A operand), alpha per row, per-wave rescale flags
 struct __align__(16) Smem {
   f16 z[2][4][TT * ZSTRIDE];
-  float sp[2][4][32][SPSTRIDE];
-  f16 p[2][ROWS * PRSTRIDE];
-  float alpha[2][ROWS];
-  int resc[2][4];
+  float sp[4][2][64][16];  // [wave][mt][lane][16 scores, 16-byte quads swizzled]
+  f16 p[ROWS * PRSTRIDE];
+  float alpha[ROWS];
+  int resc[4];
 };
 
 struct RawTile {
@@ -239,13 +242,13 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 
   // ---- softmax ownership: lane -> (accumulator slot, lane half, 8 tokens) ----
   // slot rho = 8w + (l >> 3) maps to row 32(rho/16) + 8((rho%16)/4) + 4*shf + rho%4
-  const int s_rho = 8 * w + (l >> 3), s_hf = (l >> 2) & 1, s_k8 = l & 3;
-  const int s_row = 32 * (s_rho >> 4) + 8 * ((s_rho & 15) >> 2) + 4 * s_hf + (s_rho & 3);
+  // softmax ownership: lane -> (row, 8 consecutive tokens); a row's four
+  // lanes form a quad
+  const int s_row = 16 * w + (l >> 2), s_k8 = l & 3;
   const int s_m = rb * ROWS + s_row;
   int s_vis = -1;  // padding rows are never visible
   if (s_m < M) s_vis = a.causal ? (L - a.Tq + s_m / H + 1) : L;
   const int s_lim = min(it.t1, s_vis);   // tokens < s_lim are visible to this row
-  const int s_off = 32 * s_hf + 8 * s_k8;
   float m_run = -INFINITY, l_run = 0.0f;
   // tiles [0, full_tiles) are visible to every row of this wave: no masking
   int vmin = s_lim - it.t0;
@@ -278,41 +281,36 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(((kb & 1) ? zo : ze) + 8 * kb) = v[kb];
   };
-  auto read_scores = [&](int sb, float (&s8)[8]) {
+  // Summed scores of the owned (row, 8 tokens): in the transposed score
+  // layout token 8j + 4h + e of row r sits in lane (r % 32) + 32h, slot
+  // 4j + e, of accumulator r / 32; each lane's four 16-byte quads are
+  // stored XOR-swizzled by bits 2-3 of the lane (conflict-free stores and
+  // loads in 16-lane groups).
+  const int s_lane = s_row & 31, s_mt = s_row >> 5;
+  const int s_q = s_k8 ^ ((s_lane >> 2) & 3);
+  auto read_scores = [&](float (&s8)[8]) {
 #pragma unroll
-    for (int e = 0; e < 8; e += 4) {
-      f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[sb][0][s_rho][s_off + e]);
+    for (int h = 0; h < 2; ++h) {
+      f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[0][s_mt][s_lane + 32 * h][4 * s_q]);
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[sb][ww][s_rho][s_off + e]);
-      s8[e] = acc4[0];
-      s8[e + 1] = acc4[1];
-      s8[e + 2] = acc4[2];
-      s8[e + 3] = acc4[3];
+      for (int ww = 1; ww < 4; ++ww)
+        acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[ww][s_mt][s_lane + 32 * h][4 * s_q]);
+      s8[4 * h] = acc4[0];
+      s8[4 * h + 1] = acc4[1];
+      s8[4 * h + 2] = acc4[2];
+      s8[4 * h + 3] = acc4[3];
     }
   };
-  // partial scores -> sm.sp[sb][w][slot][l], slot = 16 mt + v (32 stores
-  // straight from the accumulator AGPRs)
-  auto publish = [&](int sb, f32x16 (&acc)[2]) {
-    mfma_results_settle(acc[0], acc[1]);
-    typedef __attribute__((address_space(3))) float lds_float;
-    const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_float *)&sm.sp[sb][w][0][l]));
-    constexpr int RB = SPSTRIDE * 4;  // bytes per slot row
-    ds_store_agpr<0 * RB>(a0, acc[0][0]);   ds_store_agpr<1 * RB>(a0, acc[0][1]);
-    ds_store_agpr<2 * RB>(a0, acc[0][2]);   ds_store_agpr<3 * RB>(a0, acc[0][3]);
-    ds_store_agpr<4 * RB>(a0, acc[0][4]);   ds_store_agpr<5 * RB>(a0, acc[0][5]);
-    ds_store_agpr<6 * RB>(a0, acc[0][6]);   ds_store_agpr<7 * RB>(a0, acc[0][7]);
-    ds_store_agpr<8 * RB>(a0, acc[0][8]);   ds_store_agpr<9 * RB>(a0, acc[0][9]);
-    ds_store_agpr<10 * RB>(a0, acc[0][10]); ds_store_agpr<11 * RB>(a0, acc[0][11]);
-    ds_store_agpr<12 * RB>(a0, acc[0][12]); ds_store_agpr<13 * RB>(a0, acc[0][13]);
-    ds_store_agpr<14 * RB>(a0, acc[0][14]); ds_store_agpr<15 * RB>(a0, acc[0][15]);
-    ds_store_agpr<16 * RB>(a0, acc[1][0]);  ds_store_agpr<17 * RB>(a0, acc[1][1]);
-    ds_store_agpr<18 * RB>(a0, acc[1][2]);  ds_store_agpr<19 * RB>(a0, acc[1][3]);
-    ds_store_agpr<20 * RB>(a0, acc[1][4]);  ds_store_agpr<21 * RB>(a0, acc[1][5]);
-    ds_store_agpr<22 * RB>(a0, acc[1][6]);  ds_store_agpr<23 * RB>(a0, acc[1][7]);
-    ds_store_agpr<24 * RB>(a0, acc[1][8]);  ds_store_agpr<25 * RB>(a0, acc[1][9]);
-    ds_store_agpr<26 * RB>(a0, acc[1][10]); ds_store_agpr<27 * RB>(a0, acc[1][11]);
-    ds_store_agpr<28 * RB>(a0, acc[1][12]); ds_store_agpr<29 * RB>(a0, acc[1][13]);
-    ds_store_agpr<30 * RB>(a0, acc[1][14]); ds_store_agpr<31 * RB>(a0, acc[1][15]);
+  // partial scores -> sm.sp[sb][w][mt][l]: four 16-byte stores per
+  // accumulator; quad j of lane l at quad j ^ ((l >> 2) & 3)
+  const int p_sw = (l >> 2) & 3;
+  auto publish = [&](f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4 *>(&sm.sp[w][mt][l][4 * (j ^ p_sw)]) =
+            f32x4{acc[mt][4 * j], acc[mt][4 * j + 1], acc[mt][4 * j + 2], acc[mt][4 * j + 3]};
   };
   float s_next[8];
   {
@@ -325,15 +323,14 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bz[kb], aq[mt][kb], sacc[mt], 0, 0, 0);
     store_z(0, bz);
-    publish(0, sacc);
+    publish(sacc);
     dequant<G>(r1, bz);
-    store_z(1, bz);
   }
   RawTile raw = load_tile<G>(a, tile_slot(2), w, hf);
   lds_barrier();
-  read_scores(0, s_next);
+  read_scores(s_next);
 
   for (int i = 0; i < n_tiles; ++i) {
     const int buf = i & 1, nb = buf ^ 1;
@@ -354,7 +351,10 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[mt][kb], bz[kb], sacc[mt], 0, 0, 0);
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bz[kb], aq[mt][kb], sacc[mt], 0, 0, 0);
+    // Z of tile i+1 to its buffer (last read by the PV of tile i-1), while
+    // the MFMAs run
+    store_z(nb, bz);
 
     // ---- (b) online softmax of tile i (vector ALU, overlaps the MFMAs) ----
     float tmax = -INFINITY;
@@ -375,24 +375,23 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     }
     psum = reduce4<false>(psum);
     l_run = l_run * alpha + psum;
-    *reinterpret_cast<f16x8 *>(sm.p[buf] + s_row * PRSTRIDE + 8 * s_k8) = pv;
-    if (s_k8 == 0) sm.alpha[buf][s_row] = alpha;
-    const int any_w = __any(need ? 1 : 0);
-    if (l == 0) sm.resc[buf][w] = any_w;
+    *reinterpret_cast<f16x8 *>(sm.p + s_row * PRSTRIDE + 8 * s_k8) = pv;
+    // every lane stores (the quad's lanes and the wave's lanes store equal
+    // values to one address), which keeps this block branch-free
+    sm.alpha[s_row] = alpha;
+    sm.resc[w] = __any(need ? 1 : 0);
+    lds_barrier();  // A: P, alpha and the rescale flags of tile i
 
-    // ---- (c) publish the partial scores of tile i+1 ----
-    publish(nb, sacc);
-    lds_barrier();
 
     // ---- (d) O = alpha * O + P Z for tile i ----
-    const int rescale = sm.resc[buf][0] | sm.resc[buf][1] | sm.resc[buf][2] | sm.resc[buf][3];
+    const int rescale = sm.resc[0] | sm.resc[1] | sm.resc[2] | sm.resc[3];
     if (rescale) {
       o_settle<true>(o);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float al = sm.alpha[buf][32 * mt + 8 * (v >> 2) + 4 * hf + (v & 3)];
+          const float al = sm.alpha[32 * mt + 8 * (v >> 2) + 4 * hf + (v & 3)];
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
             float x = o[mt][nt][v];
@@ -408,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
       f16x8 pa[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p[buf] + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
+        pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const f16 *z0 = zb_base + 16 * ks * ZSTRIDE + 32 * nt;
@@ -423,10 +422,13 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     // ---- (e) dequantise tile i+2 into the Z buffer tile i just used (this
     // wave's own region: its PV reads above were issued first), prefetch
     // tile i+3 and the summed partial scores of tile i+1 ----
+    // ---- (c) partial scores of tile i+1 to LDS (their MFMAs finished
+    // during the softmax), next tile's operands ----
+    publish(sacc);
     dequant<G>(raw, bz);
-    store_z(buf, bz);
     raw = load_tile<G>(a, tile_slot(i + 3), w, hf);
-    read_scores(nb, s_next);
+    lds_barrier();  // B: partial scores of tile i+1
+    read_scores(s_next);
   }
 
   // ---- write the partial (O, m, l) of this work item ----
