@@ -36,7 +36,10 @@ grid (the pages print no clip values: parity unpinned against the pages; the
 search itself is pinned by brute force) and ``calibrate_rotation_weighted``'s
 weighting (a reading of a refinement the pages only name: parity unpinned
 against the pages; its reduction to the unweighted rotation, a closed form
-and its invariants are pinned).
+and its invariants are pinned).  The sparse decode functions
+(``index_scores``, ``index_topk``, ``sparse_absorbed_attention``) follow a
+reading of an indexer the pages only name: pinned by brute force, sorting and
+the reduction to dense attention, unpinned against the pages.
 """
 from __future__ import annotations
 
@@ -533,6 +536,70 @@ def rotated_attention(q_nope, q_rope, w_uk, w_uv, z_hat, k_rope, r_apply,
 def default_softmax_scale(d_n, d_r) -> float:
     """Reading: 1/sqrt(qk_nope_head_dim + qk_rope_head_dim), no extra factor."""
     return 1.0 / np.sqrt(d_n + d_r)
+
+
+# --------------------------------------------------------------------------
+# Sparse decode through the indexer key  [LLMH-SIZE: the latent layers of
+# GLM-5.3-Flash carry a sparse-attention indexer and cache its key]
+# --------------------------------------------------------------------------
+
+
+def index_scores(q_idx, k_idx) -> np.ndarray:
+    """Indexer score of every cached token for one query, fp32.
+
+    Reading (the pages name the indexer and its cached key, nothing more):
+    the score of token tau is the dot product of the query's index vector
+    q_idx [d_idx] with the token's cached index key k_idx [L, d_idx], both
+    bf16-valued, accumulated in IEEE fp32 in channel order e = 0 .. d_idx-1
+    (one rounding per addition; each bf16 x bf16 product is exact in fp32).
+    """
+    q = np.asarray(q_idx, dtype=F32)
+    k = np.asarray(k_idx, dtype=F32)
+    s = np.zeros(k.shape[0], dtype=F32)
+    for e in range(k.shape[1]):
+        s = (s + (k[:, e] * q[e]).astype(F32)).astype(F32)
+    return s
+
+
+def score_order_key(scores) -> np.ndarray:
+    """Total order on fp32 scores as unsigned integers (larger = higher).
+
+    Sign-magnitude bits mapped to an ordered integer: negative values have
+    all bits flipped, non-negative ones get the sign bit set.  This is the
+    float order, with -0 just below +0.
+    """
+    b = np.ascontiguousarray(np.asarray(scores, dtype=F32)).view(np.uint32).astype(np.uint64)
+    neg = (b >> np.uint64(31)) == 1
+    return np.where(neg, (~b) & np.uint64(0xFFFFFFFF), b | np.uint64(0x80000000))
+
+
+def index_topk(scores, k) -> np.ndarray:
+    """Token indices selected for attention, ascending.
+
+    Reading: the k tokens of highest indexer score; equal scores go to the
+    lower token index; fewer than k tokens select them all.
+    """
+    L = len(scores)
+    if k >= L:
+        return np.arange(L, dtype=np.int64)
+    key = score_order_key(scores)
+    order = np.lexsort((np.arange(L), -key.astype(np.float64)))  # key desc, index asc
+    # key fits in 32 bits, so the float64 negation above is exact
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def sparse_absorbed_attention(q_nope, q_rope, w_uk, w_uv, z_hat, k_rope, r_apply,
+                              scale, selected):
+    """Absorbed decode of one query token over the selected tokens only.
+
+    Reading: the indexer's selection replaces the visible window; attention
+    over it is the absorbed form above with the unselected tokens left out.
+    q_nope [1, H, d_n], q_rope [1, H, d_r]; selected: token indices.
+    """
+    sel = np.asarray(selected, dtype=np.int64)
+    return absorbed_attention(q_nope, q_rope, w_uk, w_uv,
+                              np.asarray(z_hat)[sel], np.asarray(k_rope)[sel],
+                              r_apply, scale, causal=False)
 
 
 # --------------------------------------------------------------------------
