@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=8, help="cache copies used in turn")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sparse", action="store_true",
+                    help="skip the sparse (indexer top-k) decode measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the HBM "
                          "byte counters of a profiler run) and exit")
@@ -283,11 +285,107 @@ def main():
         "roofline": roofline,
     }
 
+    if not args.no_sparse:
+        del caches
+        torch.cuda.empty_cache()
+        result["sparse_decode"] = sparse_bench(M, S, dev, args)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, st, c_cal, lat_seed=1000 + w.wid, lens=lens, base=base,
                                               model=model, w_uk=w_uk, w_uv=w_uv, qn=qn, qr=qr, kr=kr,
                                               out=out, budget=args.cpu_seconds, scale=scale)
     print(json.dumps(result))
+
+
+def sparse_bench(M, S, dev, args):
+    """Sparse decode through the indexer key on the GLM-5.3-Flash-like layer
+    (64 heads, 64-dim indexer key), 4 sequences of 262,144 tokens, top-2048
+    selection per sequence: index scores + exact top-k, then absorbed decode
+    over the selected tokens; the dense decode of the same cache for context."""
+    import torch
+    w = S.WORKLOADS[4]
+    st = S.streams(w.wid)
+    d = M.Dims(w.kv_lora_rank, w.qk_rope_head_dim, w.qk_nope_head_dim, w.v_head_dim, w.num_heads,
+               w.group_size, w.index_head_dim)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev).to(torch.bfloat16)
+    model = S.latent_model(w, st)
+    c_cal_d = bf(S.calib_latents(w, st, model))
+    w_uk, w_uv = S.weights(w, st)
+    R, _ = M.mla_calibrate_rotation(d, c_cal_d)
+    Rt = M.mla_prepare_rotation(d, R)
+    alpha, _ = M.mla_fit_clip(d, c_cal_d, Rt, [1.0 - 0.05 * k for k in range(11)])
+    uk_f, uv_f = M.mla_fold_absorb_weights(d, bf(w_uk), bf(w_uv), Rt)
+    lens = S.seq_lens(w, st)
+    base, cap = S.contiguous_layout(lens)
+    B = len(lens)
+    cache = M.Cache(d, cap, dev)
+    for a in range(0, cap, 1 << 18):  # append in pieces to bound the latent buffer
+        n = min(1 << 18, cap - a)
+        lat = S.torch_latents(model, n, seed=1000 + w.wid + a, device=dev)
+        kr = S.torch_normal_bf16((n, w.qk_rope_head_dim), 2000 + w.wid + a, dev)
+        idx = S.torch_normal_bf16((n, w.index_head_dim), 3000 + w.wid + a, dev)
+        M.mla_append_quant(d, lat, kr, idx, torch.arange(a, a + n, dtype=torch.int64, device=dev), Rt, alpha,
+                           cache)
+        del lat, kr, idx
+    top_k = 2048
+    q_idx = S.torch_normal_bf16((B, w.index_head_dim), 9000 + w.wid, dev)
+    qn = S.torch_normal_bf16((B, 1, w.num_heads, w.qk_nope_head_dim), 4000 + w.wid, dev)
+    qr = S.torch_normal_bf16((B, 1, w.num_heads, w.qk_rope_head_dim), 5000 + w.wid, dev)
+    seq_base = torch.from_numpy(base).to(dev)
+    seq_len = torch.from_numpy(lens).to(dev)
+    ws_i = torch.empty(M.mla_index_topk_workspace_size(d, B, cap), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(M.mla_decode_workspace_size(d, B, 1), dtype=torch.uint8, device=dev)
+    sel = torch.zeros((B, top_k), dtype=torch.int32, device=dev)
+    n_sel = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, 1, w.num_heads, w.v_head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, 1, w.num_heads), dtype=torch.float32, device=dev)
+    scale = 1.0 / float(np.sqrt(w.qk_nope_head_dim + w.qk_rope_head_dim))
+
+    def step():
+        M.mla_index_topk(d, q_idx, cache, seq_base, seq_len, top_k, ws_i, sel, n_sel)
+        M.mla_decode_sparse(d, qn, qr, uk_f, uv_f, cache, seq_base, sel, n_sel, scale, ws_d, out, lse)
+
+    def dense():
+        M.mla_decode_absorbed(d, qn, qr, uk_f, uv_f, cache, seq_base, seq_len, 1, False, scale, ws_d, out, lse)
+
+    n = max(args.steps // 2, 10)
+    timings = {}
+    for name, fn in (("sparse", step), ("dense", dense)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        timings[name] = (time.perf_counter() - t) * 1e3 / n
+    M.mla_timing_enable(True)
+    M.mla_timing_reset()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    k_us = {}
+    for name in ("index_score", "index_select", "absorb_q", "splitk_decode", "combine", "up_proj"):
+        ms, cnt = M.mla_timing_query(name)
+        if cnt:
+            k_us[name] = round(ms / cnt * 1e3, 3)
+    M.mla_timing_enable(False)
+    tokens = int(np.sum(lens))
+    score_bytes = tokens * (2 * w.index_head_dim + 4)   # read the index key, write one fp32 score
+    sc_us = k_us.get("index_score")
+    return {
+        "workload": "glm53flash-layer-b4-ctx256k-top2048", "batch": B, "context_tokens": tokens,
+        "heads": w.num_heads, "index_head_dim": w.index_head_dim, "top_k": top_k,
+        "ms_per_step": round(timings["sparse"], 5),
+        "query_tokens_per_s": round(B / (timings["sparse"] * 1e-3), 1),
+        "dense_ms_per_step": round(timings["dense"], 5),
+        "kernel_us": k_us,
+        "index_score_roofline": {
+            "bound": "hbm", "achieved": round(score_bytes / (sc_us * 1e-6) / 1e9, 1) if sc_us else None,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(score_bytes / (sc_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4) if sc_us else None,
+            "algorithmic_bytes_per_launch": score_bytes},
+    }
 
 
 def cpu_baseline(w, st, c_cal, lat_seed, lens, base, model, w_uk, w_uv, qn, qr, kr, out, budget, scale):

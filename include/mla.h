@@ -257,6 +257,57 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope,
                                void *stream);
 
 /* ------------------------------------------------------------------------
+ * Sparse decode through the cached indexer key
+ * [LLMH-SIZE: GLM-5.3-Flash's latent layers carry a sparse-attention indexer
+ * and cache its key]
+ *
+ * The pages name the indexer and its cached key, not its scoring rule.  The
+ * rule implemented here is one reading: one index query vector per sequence,
+ *   score_tau = q_idx[b] . idx_key[seq_base[b] + tau]
+ * accumulated in fp32 in channel order (bf16 x bf16 products are exact in
+ * fp32), and the selection is the top_k tokens by score with equal scores
+ * going to the lower token index (fewer than top_k tokens: all of them).
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of workspace mla_index_topk needs (0 for invalid arguments): one fp32
+ * score per cache slot plus per-sequence histograms and counts. */
+size_t mla_index_topk_workspace_size(const mla_dims *dims, int32_t batch,
+                                     int64_t capacity);
+
+/* mla_index_topk — select the tokens a query attends to.
+ *   q_idx [B][index_head_dim] bf16 (device): the index query vectors
+ *   cache: idx_key must be set (index_head_dim > 0, a multiple of 8, <= 256)
+ *   seq_base [B] int64, seq_len [B] int32 (device), as for decode
+ *   sel [B][top_k] int32 (device, out): the selected token indices of
+ *     sequence b (0-based within the sequence), ascending, in
+ *     sel[b*top_k .. b*top_k + n_sel[b] - 1]; the rest is left untouched
+ *   n_sel [B] int32 (device, out): min(top_k, seq_len[b])
+ * Exact: the selection is decided on the fp32 scores with no approximate
+ * step (radix select on unique 64-bit keys).  Asynchronous; no host
+ * synchronisation.  The caller keeps seq_base[b] + seq_len[b] <= capacity. */
+mla_status mla_index_topk(const mla_dims *dims, const uint16_t *q_idx,
+                          const mla_cache *cache, const int64_t *seq_base,
+                          const int32_t *seq_len, int32_t batch, int32_t top_k,
+                          void *workspace, size_t workspace_bytes,
+                          int32_t *sel, int32_t *n_sel, void *stream);
+
+/* mla_decode_sparse — mla_decode_absorbed for one query token per sequence
+ * (tq = 1) over the selected tokens only: token t < n_sel[b] of sequence b is
+ * cache slot seq_base[b] + sel[b*top_k + t] (sel, n_sel as written by
+ * mla_index_topk, or any indices the caller keeps inside the sequence).
+ * Same operands, workspace (mla_decode_workspace_size(dims, batch, 1)),
+ * outputs and error behaviour as mla_decode_absorbed; a sequence with
+ * n_sel[b] = 0 gets out = 0 and lse = -inf. */
+mla_status mla_decode_sparse(const mla_dims *dims, const uint16_t *q_nope,
+                             const uint16_t *q_rope, const uint16_t *w_uk_f,
+                             const uint16_t *w_uv_f, const mla_cache *cache,
+                             const int64_t *seq_base, const int32_t *sel,
+                             const int32_t *n_sel, int32_t batch, int32_t top_k,
+                             float softmax_scale, void *workspace,
+                             size_t workspace_bytes, float *out, float *lse,
+                             void *stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics
  * ---------------------------------------------------------------------- */
 

@@ -57,6 +57,12 @@ _SIGS = {
     "mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, _P, _P, _P, ctypes.POINTER(mla_cache),
                                            _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                            _P, ctypes.c_size_t, _P, _P, _P]),
+    "mla_index_topk_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(mla_dims), ctypes.c_int32, ctypes.c_int64]),
+    "mla_index_topk": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, ctypes.POINTER(mla_cache), _P, _P,
+                                      ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P, _P, _P]),
+    "mla_decode_sparse": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, _P, _P, _P, ctypes.POINTER(mla_cache),
+                                         _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                         _P, ctypes.c_size_t, _P, _P, _P]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_abi_version": (ctypes.c_int32, []),
@@ -307,6 +313,67 @@ def mla_decode_absorbed(dims: Dims, q_nope, q_rope, w_uk_f, w_uv_f, cache: Cache
                                    float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
                                    _stream())
     _check(st, "mla_decode_absorbed")
+    return out, lse
+
+
+def mla_index_topk_workspace_size(dims: Dims, batch: int, capacity: int) -> int:
+    return int(lib().mla_index_topk_workspace_size(ctypes.byref(dims.c()), int(batch), int(capacity)))
+
+
+def mla_index_topk(dims: Dims, q_idx, cache: Cache, seq_base, seq_len, top_k: int, workspace=None, sel=None,
+                   n_sel=None):
+    """Returns (sel [B, top_k] int32, n_sel [B] int32); see include/mla.h."""
+    B = seq_len.shape[0]
+    dev = seq_len.device
+    _need(q_idx, "q_idx", torch.bfloat16, (B, dims.index_head_dim))
+    _need(seq_base, "seq_base", torch.int64, (B,))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    need = mla_index_topk_workspace_size(dims, B, cache.capacity)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    if sel is None:
+        sel = torch.zeros((B, top_k), dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(sel, "sel", torch.int32, (B, top_k))
+    _need(n_sel, "n_sel", torch.int32, (B,))
+    d, c = dims.c(), cache.c()
+    st = lib().mla_index_topk(ctypes.byref(d), _ptr(q_idx), ctypes.byref(c), _ptr(seq_base), _ptr(seq_len), B,
+                              int(top_k), _ptr(workspace), workspace.numel(), _ptr(sel), _ptr(n_sel), _stream())
+    _check(st, "mla_index_topk")
+    return sel, n_sel
+
+
+def mla_decode_sparse(dims: Dims, q_nope, q_rope, w_uk_f, w_uv_f, cache: Cache, seq_base, sel, n_sel,
+                      softmax_scale: float, workspace=None, out=None, lse=None):
+    """Returns (out [B, 1, H, d_v] fp32, lse [B, 1, H] fp32) over the selected tokens."""
+    H, r = dims.num_heads, dims.kv_lora_rank
+    B, top_k = sel.shape
+    dev = q_nope.device
+    _need(q_nope, "q_nope", torch.bfloat16, (B, 1, H, dims.qk_nope_head_dim))
+    _need(q_rope, "q_rope", torch.bfloat16, (B, 1, H, dims.qk_rope_head_dim))
+    _need(w_uk_f, "w_uk_f", torch.float16, (H, r, dims.qk_nope_head_dim))
+    _need(w_uv_f, "w_uv_f", torch.float16, (H, dims.v_head_dim, r))
+    _need(seq_base, "seq_base", torch.int64, (B,))
+    _need(sel, "sel", torch.int32, (B, top_k))
+    _need(n_sel, "n_sel", torch.int32, (B,))
+    need = mla_decode_workspace_size(dims, B, 1)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((B, 1, H, dims.v_head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, 1, H, dims.v_head_dim))
+    _need(lse, "lse", torch.float32, (B, 1, H))
+    d, c = dims.c(), cache.c()
+    st = lib().mla_decode_sparse(ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk_f), _ptr(w_uv_f),
+                                 ctypes.byref(c), _ptr(seq_base), _ptr(sel), _ptr(n_sel), B, int(top_k),
+                                 float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+                                 _stream())
+    _check(st, "mla_decode_sparse")
     return out, lse
 
 

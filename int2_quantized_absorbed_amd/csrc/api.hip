@@ -486,46 +486,54 @@ size_t mla_decode_workspace_size(const mla_dims *dims, int32_t batch, int32_t tq
   return layout(*dims, batch, tq).total;
 }
 
-mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, const uint16_t *q_rope,
-                               const uint16_t *w_uk_f, const uint16_t *w_uv_f, const mla_cache *cache,
-                               const int64_t *seq_base, const int32_t *seq_len, int32_t batch, int32_t tq,
-                               int32_t causal, float softmax_scale, void *workspace, size_t workspace_bytes,
-                               float *out, float *lse, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the dense and the sparse entry points: with sel != nullptr the
+// tokens of sequence b are the slots seq_base[b] + sel[b * sel_stride + t],
+// t < seq_len[b] (the selected counts).
+mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_nope, const uint16_t *q_rope,
+                       const uint16_t *w_uk_f, const uint16_t *w_uv_f, const mla_cache *cache,
+                       const int64_t *seq_base, const int32_t *seq_len, const int32_t *sel, int32_t sel_stride,
+                       int32_t batch, int32_t tq, int32_t causal, float softmax_scale, void *workspace,
+                       size_t workspace_bytes, float *out, float *lse, void *stream) {
+  const std::string F = std::string(fn) + ": ";
   std::string why;
-  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed: " + why);
-  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed: batch must be >= 0");
-  if (tq < 1 || tq > 64) return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed: tq must be in 1..64");
-  if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed: causal must be 0 or 1");
-  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed: softmax_scale not finite");
-  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed: cache is NULL");
+  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, F + "" + why);
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, F + "batch must be >= 0");
+  if (tq < 1 || tq > 64) return fail(MLA_ERR_INVALID_ARG, F + "tq must be in 1..64");
+  if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, F + "causal must be 0 or 1");
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, F + "softmax_scale not finite");
+  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, F + "cache is NULL");
   if (batch == 0) {
     clear_error();
     return MLA_OK;
   }
   if (!q_nope || !q_rope || !w_uk_f || !w_uv_f || !seq_base || !seq_len || !workspace || !out ||
       !cache->codes || !cache->scale_zero || !cache->k_rope)
-    return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed: NULL device pointer");
+    return fail(MLA_ERR_INVALID_ARG, F + "NULL device pointer");
   const void *ptrs[] = {q_nope, q_rope, w_uk_f, w_uv_f, seq_base, seq_len, workspace, out, lse,
                         cache->codes, cache->scale_zero, cache->k_rope};
   for (const void *p : ptrs)
     if (p != nullptr && !aligned16(p))
-      return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed: device pointers must be 16-byte aligned");
+      return fail(MLA_ERR_INVALID_ARG, F + "device pointers must be 16-byte aligned");
   if (dims->kv_lora_rank > 512)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_absorbed: kv_lora_rank > 512");
+    return fail(MLA_ERR_UNSUPPORTED, F + "kv_lora_rank > 512");
   const int M = dims->num_heads * tq;
   bool use_mfma = false;
   if (g_decode_variant == 2) {
     if (!mfma_decode_supported(*dims, M))
-      return fail(MLA_ERR_UNSUPPORTED, "mla_decode_absorbed: no MFMA kernel for this shape");
+      return fail(MLA_ERR_UNSUPPORTED, F + "no MFMA kernel for this shape");
     use_mfma = true;
   } else if (g_decode_variant == 0) {
     use_mfma = M >= 16 && mfma_decode_supported(*dims, M);
   }
   if (use_mfma && !mfma_absorb_supported(*dims))
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_absorbed: qk_nope_head_dim must be a multiple of 16 for the MFMA path");
+    return fail(MLA_ERR_UNSUPPORTED, F + "qk_nope_head_dim must be a multiple of 16 for the MFMA path");
   const WsLayout w = layout(*dims, batch, tq);
   if (workspace_bytes < w.total)
-    return fail(MLA_ERR_WORKSPACE, "mla_decode_absorbed: workspace needs " + std::to_string(w.total) + " bytes");
+    return fail(MLA_ERR_WORKSPACE, F + "workspace needs " + std::to_string(w.total) + " bytes");
   DecodeArgs a;
   a.d = *dims;
   a.q_nope = q_nope;
@@ -552,6 +560,8 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
   a.max_items = w.max_items;
   a.target_items = target_items(M, use_mfma);
   a.tile = use_mfma ? 32 : 16;
+  a.sel = sel;
+  a.sel_stride = sel_stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the MFMA absorb kernel also runs the planner
   hipError_t e = use_mfma ? launch_absorb_mfma_layout(a, s) : launch_plan(a, s);
@@ -559,9 +569,93 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
   if (e == hipSuccess) e = use_mfma ? launch_splitk_mfma(a, s) : launch_splitk_valu(a, s);
   if (e == hipSuccess) e = launch_combine(a, s);
   if (e == hipSuccess) e = launch_upproj(a, s);
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_absorbed");
+  if (e != hipSuccess) return hip_fail(e, fn);
   clear_error();
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, const uint16_t *q_rope,
+                               const uint16_t *w_uk_f, const uint16_t *w_uv_f, const mla_cache *cache,
+                               const int64_t *seq_base, const int32_t *seq_len, int32_t batch, int32_t tq,
+                               int32_t causal, float softmax_scale, void *workspace, size_t workspace_bytes,
+                               float *out, float *lse, void *stream) {
+  return decode_impl("mla_decode_absorbed", dims, q_nope, q_rope, w_uk_f, w_uv_f, cache, seq_base, seq_len,
+                     nullptr, 0, batch, tq, causal, softmax_scale, workspace, workspace_bytes, out, lse, stream);
+}
+
+size_t mla_index_topk_workspace_size(const mla_dims *dims, int32_t batch, int64_t capacity) {
+  std::string why;
+  if (!dims_valid(dims, &why) || batch < 0 || capacity < 0) return 0;
+  size_t off = align256(static_cast<size_t>(capacity) * sizeof(float));        // scores
+  off = align256(off + sizeof(uint32_t) * 8 * 256 * static_cast<size_t>(batch));  // histograms
+  off = align256(off + sizeof(int32_t) * index_chunks() * static_cast<size_t>(batch));  // chunk counts
+  return off;
+}
+
+mla_status mla_index_topk(const mla_dims *dims, const uint16_t *q_idx, const mla_cache *cache,
+                          const int64_t *seq_base, const int32_t *seq_len, int32_t batch, int32_t top_k,
+                          void *workspace, size_t workspace_bytes, int32_t *sel, int32_t *n_sel, void *stream) {
+  std::string why;
+  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: " + why);
+  if (dims->index_head_dim <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: the layer has no indexer key (index_head_dim = 0)");
+  if (dims->index_head_dim % 8 != 0 || dims->index_head_dim > 256)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_index_topk: index_head_dim must be a multiple of 8, at most 256");
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: batch must be >= 0");
+  if (top_k < 1) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: top_k must be >= 1");
+  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: cache is NULL");
+  if (batch == 0) {
+    clear_error();
+    return MLA_OK;
+  }
+  if (!q_idx || !seq_base || !seq_len || !workspace || !sel || !n_sel || !cache->idx_key)
+    return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: NULL device pointer");
+  const void *ptrs[] = {q_idx, seq_base, seq_len, workspace, sel, n_sel, cache->idx_key};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: device pointers must be 16-byte aligned");
+  const size_t need = mla_index_topk_workspace_size(dims, batch, cache->capacity);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "mla_index_topk: workspace needs " + std::to_string(need) + " bytes");
+  IndexArgs a;
+  a.q_idx = q_idx;
+  a.idx_key = cache->idx_key;
+  a.seq_base = seq_base;
+  a.seq_len = seq_len;
+  a.B = batch;
+  a.d_idx = dims->index_head_dim;
+  a.top_k = top_k;
+  a.n_chunks = index_chunks();
+  char *ws = static_cast<char *>(workspace);
+  size_t off = 0;
+  a.scores = reinterpret_cast<float *>(ws + off);
+  off = align256(off + static_cast<size_t>(cache->capacity) * sizeof(float));
+  a.hist = reinterpret_cast<uint32_t *>(ws + off);
+  off = align256(off + sizeof(uint32_t) * 8 * 256 * static_cast<size_t>(batch));
+  a.counts = reinterpret_cast<int32_t *>(ws + off);
+  a.sel = sel;
+  a.n_sel = n_sel;
+  hipError_t e = launch_index_topk(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mla_index_topk");
+  clear_error();
+  return MLA_OK;
+}
+
+mla_status mla_decode_sparse(const mla_dims *dims, const uint16_t *q_nope, const uint16_t *q_rope,
+                             const uint16_t *w_uk_f, const uint16_t *w_uv_f, const mla_cache *cache,
+                             const int64_t *seq_base, const int32_t *sel, const int32_t *n_sel, int32_t batch,
+                             int32_t top_k, float softmax_scale, void *workspace, size_t workspace_bytes,
+                             float *out, float *lse, void *stream) {
+  if (top_k < 1) return fail(MLA_ERR_INVALID_ARG, "mla_decode_sparse: top_k must be >= 1");
+  if (batch > 0 && (sel == nullptr || n_sel == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_sparse: NULL device pointer");
+  if (batch > 0 && (!aligned16(sel) || !aligned16(n_sel)))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_sparse: device pointers must be 16-byte aligned");
+  return decode_impl("mla_decode_sparse", dims, q_nope, q_rope, w_uk_f, w_uv_f, cache, seq_base, n_sel, sel, top_k,
+                     batch, 1, 0, softmax_scale, workspace, workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

@@ -89,6 +89,8 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
   const int row0 = rb * ROWS;
   const int L = a.seq_len[it.b];
   const int64_t base = a.seq_base[it.b];
+  const int32_t *sel = a.sel ? a.sel + static_cast<int64_t>(it.b) * a.sel_stride : nullptr;
+  auto slot_of = [&](int tau) -> int64_t { return base + (sel ? sel[tau] : tau); };
   const float *qbuf = static_cast<const float *>(a.qbuf);
   for (int e = tid; e < ROWS * K; e += 256) {
     const int i = e / K, k = e % K;
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
       const int tau = t0 + tk;
       float v = 0.0f;
       if (tau < it.t1) {
-        const int64_t slot = base + tau;
+        const int64_t slot = slot_of(tau);
         const uint32_t byte = a.cache.codes[slot * (r / 4) + j / 4];
         const uint32_t code = (byte >> (2 * (j & 3))) & 3u;
         const uint32_t sz = sz32[slot * (r / G) + j / G];
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
     for (int e = tid; e < TT * dr; e += 256) {
       const int tk = e / dr, k = e % dr;
       const int tau = t0 + tk;
-      z_s[tk * KP + r + k] = (tau < it.t1) ? bf16_to_f32(a.cache.k_rope[(base + tau) * dr + k]) : 0.0f;
+      z_s[tk * KP + r + k] = (tau < it.t1) ? bf16_to_f32(a.cache.k_rope[slot_of(tau) * dr + k]) : 0.0f;
     }
     __syncthreads();
     if (scorer) {

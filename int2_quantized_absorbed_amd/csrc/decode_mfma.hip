@@ -265,9 +265,11 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);    // transposing-load source row
   // and column (rows pv_krow + 16 ks (+ 4) share bit 3 of pv_krow: one swizzle)
   const int pv_col = (16 * (g16 & 1) + 4 * (s16 & 3)) ^ (8 * ((g16 >> 1) & 1));
+  const int32_t *sel = a.sel ? a.sel + static_cast<int64_t>(it.b) * a.sel_stride : nullptr;
   auto tile_slot = [&](int i) -> int64_t {
     const int ti = min(i, n_tiles - 1);
-    return base + min(it.t0 + ti * TT + l32, it.t1 - 1);
+    const int t = min(it.t0 + ti * TT + l32, it.t1 - 1);
+    return base + (sel ? sel[t] : t);
   };
 
   // ---- prologue: tile 0 scores summed in registers, tiles 0 and 1 in the

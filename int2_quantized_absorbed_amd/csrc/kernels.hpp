@@ -55,9 +55,30 @@ struct DecodeArgs {
   int32_t max_items;
   int32_t target_items;
   int32_t tile;
+  // sparse decode: token t of sequence b is cache slot seq_base[b] +
+  // sel[b * sel_stride + t] (seq_len then holds the selected counts); dense
+  // decode: sel == nullptr and token t is slot seq_base[b] + t
+  const int32_t *sel;
+  int32_t sel_stride;
 };
 
 hipError_t launch_plan(const DecodeArgs &a, hipStream_t s);
+
+// ---- indexer top-k (index.hip) ----
+struct IndexArgs {
+  const uint16_t *q_idx;    // [B][d_idx] bf16
+  const uint16_t *idx_key;  // cache index keys [capacity][d_idx] bf16
+  const int64_t *seq_base;
+  const int32_t *seq_len;
+  int32_t B, d_idx, top_k, n_chunks;
+  float *scores;            // [capacity], by cache slot
+  uint32_t *hist;           // [8][B][256]
+  int32_t *counts;          // [B][n_chunks]
+  int32_t *sel;             // [B][top_k]
+  int32_t *n_sel;           // [B]
+};
+int index_chunks();
+hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s);
 
 hipError_t launch_absorb_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s);

@@ -88,6 +88,46 @@ def test_decode_argument_checks():
                                    1 << 40, P, P, None) == Bd.MLA_ERR_UNSUPPORTED
 
 
+def test_index_topk_argument_checks():
+    lib = M.lib()
+    d = _dims(index_head_dim=64)
+    P = ctypes.c_void_p(256)
+    cache = Bd.mla_cache(256, 256, 256, 256, 1000)
+    call = lambda **kw: lib.mla_index_topk(
+        ctypes.byref(kw.get("d", d)), kw.get("q", P), ctypes.byref(kw.get("cache", cache)), P, P, kw.get("B", 2),
+        kw.get("k", 64), P, kw.get("wsb", 1 << 40), kw.get("sel", P), P, None)
+    assert call(d=_dims(index_head_dim=0)) == Bd.MLA_ERR_INVALID_ARG       # no indexer key
+    assert call(d=_dims(index_head_dim=12)) == Bd.MLA_ERR_UNSUPPORTED
+    assert call(k=0) == Bd.MLA_ERR_INVALID_ARG
+    assert call(B=-1) == Bd.MLA_ERR_INVALID_ARG
+    assert call(q=ctypes.c_void_p(0)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(sel=ctypes.c_void_p(260)) == Bd.MLA_ERR_INVALID_ARG       # misaligned
+    assert call(cache=Bd.mla_cache(256, 256, 256, 0, 1000)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(wsb=16) == Bd.MLA_ERR_WORKSPACE
+    assert call(B=0) == Bd.MLA_OK
+    # one score per cache slot, and a histogram and chunk counts per sequence
+    w1 = lib.mla_index_topk_workspace_size(ctypes.byref(d), 1, 1000)
+    assert w1 >= 4000 and lib.mla_index_topk_workspace_size(ctypes.byref(d), 2, 1000) > w1
+    assert lib.mla_index_topk_workspace_size(ctypes.byref(d), -1, 1000) == 0
+
+
+def test_decode_sparse_argument_checks():
+    lib = M.lib()
+    d = _dims()
+    P = ctypes.c_void_p(256)
+    cache = Bd.mla_cache(256, 256, 256, 0, 1000)
+    call = lambda **kw: lib.mla_decode_sparse(
+        ctypes.byref(d), P, P, P, P, ctypes.byref(cache), P, kw.get("sel", P), kw.get("n_sel", P), kw.get("B", 2),
+        kw.get("k", 64), 0.07, P, kw.get("wsb", 1 << 40), P, P, None)
+    assert call(k=0) == Bd.MLA_ERR_INVALID_ARG
+    assert call(sel=ctypes.c_void_p(0)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(n_sel=ctypes.c_void_p(264)) == Bd.MLA_ERR_INVALID_ARG     # misaligned
+    assert call(B=-1) == Bd.MLA_ERR_INVALID_ARG
+    assert call(wsb=16) == Bd.MLA_ERR_WORKSPACE
+    assert "mla_decode_sparse" in M.mla_last_error()
+    assert call(B=0) == Bd.MLA_OK
+
+
 def test_append_argument_checks():
     lib = M.lib()
     d = _dims()
