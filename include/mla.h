@@ -276,14 +276,15 @@ size_t mla_index_topk_workspace_size(const mla_dims *dims, int32_t batch,
 
 /* mla_index_topk — select the tokens a query attends to.
  *   q_idx [B][index_head_dim] bf16 (device): the index query vectors
- *   cache: idx_key must be set (index_head_dim > 0, a multiple of 8, <= 256)
+ *   cache: idx_key must be set (index_head_dim 64 or 128, else UNSUPPORTED)
  *   seq_base [B] int64, seq_len [B] int32 (device), as for decode
  *   sel [B][top_k] int32 (device, out): the selected token indices of
  *     sequence b (0-based within the sequence), ascending, in
  *     sel[b*top_k .. b*top_k + n_sel[b] - 1]; the rest is left untouched
  *   n_sel [B] int32 (device, out): min(top_k, seq_len[b])
  * Exact: the selection is decided on the fp32 scores with no approximate
- * step (radix select on unique 64-bit keys).  Asynchronous; no host
+ * step (radix select on the scores, ties resolved by token index).
+ * Asynchronous; no host
  * synchronisation.  The caller keeps seq_base[b] + seq_len[b] <= capacity. */
 mla_status mla_index_topk(const mla_dims *dims, const uint16_t *q_idx,
                           const mla_cache *cache, const int64_t *seq_base,

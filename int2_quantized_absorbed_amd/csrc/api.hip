@@ -591,8 +591,8 @@ size_t mla_index_topk_workspace_size(const mla_dims *dims, int32_t batch, int64_
   std::string why;
   if (!dims_valid(dims, &why) || batch < 0 || capacity < 0) return 0;
   size_t off = align256(static_cast<size_t>(capacity) * sizeof(float));        // scores
-  off = align256(off + sizeof(uint32_t) * 8 * 256 * static_cast<size_t>(batch));  // histograms
-  off = align256(off + sizeof(int32_t) * index_chunks() * static_cast<size_t>(batch));  // chunk counts
+  off = align256(off + sizeof(uint32_t) * 4 * 256 * static_cast<size_t>(batch));  // histograms
+  off = align256(off + sizeof(int32_t) * 2 * index_chunks() * static_cast<size_t>(batch));  // chunk counts
   return off;
 }
 
@@ -603,8 +603,8 @@ mla_status mla_index_topk(const mla_dims *dims, const uint16_t *q_idx, const mla
   if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: " + why);
   if (dims->index_head_dim <= 0)
     return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: the layer has no indexer key (index_head_dim = 0)");
-  if (dims->index_head_dim % 8 != 0 || dims->index_head_dim > 256)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_index_topk: index_head_dim must be a multiple of 8, at most 256");
+  if (dims->index_head_dim != 64 && dims->index_head_dim != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_index_topk: index_head_dim must be 64 or 128");
   if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: batch must be >= 0");
   if (top_k < 1) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: top_k must be >= 1");
   if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, "mla_index_topk: cache is NULL");
@@ -634,7 +634,7 @@ mla_status mla_index_topk(const mla_dims *dims, const uint16_t *q_idx, const mla
   a.scores = reinterpret_cast<float *>(ws + off);
   off = align256(off + static_cast<size_t>(cache->capacity) * sizeof(float));
   a.hist = reinterpret_cast<uint32_t *>(ws + off);
-  off = align256(off + sizeof(uint32_t) * 8 * 256 * static_cast<size_t>(batch));
+  off = align256(off + sizeof(uint32_t) * 4 * 256 * static_cast<size_t>(batch));
   a.counts = reinterpret_cast<int32_t *>(ws + off);
   a.sel = sel;
   a.n_sel = n_sel;

@@ -72,8 +72,8 @@ struct IndexArgs {
   const int32_t *seq_len;
   int32_t B, d_idx, top_k, n_chunks;
   float *scores;            // [capacity], by cache slot
-  uint32_t *hist;           // [8][B][256]
-  int32_t *counts;          // [B][n_chunks]
+  uint32_t *hist;           // [4][B][256]
+  int32_t *counts;          // [B][n_chunks][2]: above / equal to the threshold
   int32_t *sel;             // [B][top_k]
   int32_t *n_sel;           // [B]
 };
