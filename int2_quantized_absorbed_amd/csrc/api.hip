@@ -151,6 +151,14 @@ int target_items(int rows, bool mfma) {
   return t < 1 ? 1 : t;
 }
 
+// Shortest split-K chunk, in tokens: below it the fixed cost of an item
+// (query rows in, partial rows out, the combine reading them back) outweighs
+// spreading a short context over more compute units.
+#ifndef MLA_SPLIT_MIN_TOKENS
+#define MLA_SPLIT_MIN_TOKENS 32
+#endif
+int min_chunk_tiles(int tile) { return (MLA_SPLIT_MIN_TOKENS + tile - 1) / tile; }
+
 WsLayout layout(const mla_dims &d, int B, int Tq) {
   WsLayout w;
   const int r = d.kv_lora_rank, K = r + d.qk_rope_head_dim;
@@ -560,6 +568,7 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
   a.max_items = w.max_items;
   a.target_items = target_items(M, use_mfma);
   a.tile = use_mfma ? 32 : 16;
+  a.min_chunk_tiles = min_chunk_tiles(a.tile);
   a.sel = sel;
   a.sel_stride = sel_stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -587,13 +596,37 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
                      nullptr, 0, batch, tq, causal, softmax_scale, workspace, workspace_bytes, out, lse, stream);
 }
 
+namespace {
+// Workspace of mla_index_topk: scores, histograms, prefixes, chunk counts.
+struct IndexWorkspace {
+  size_t scores, hist, pfx_bits, pfx_rank, chunk_above, chunk_suf, total;
+};
+
+IndexWorkspace index_workspace(int32_t batch, int64_t capacity) {
+  const size_t B = static_cast<size_t>(batch), nc = static_cast<size_t>(mla::index_chunks());
+  IndexWorkspace w;
+  size_t off = 0;
+  w.scores = off;
+  off = align256(off + static_cast<size_t>(capacity) * sizeof(float));
+  w.hist = off;
+  off = align256(off + sizeof(uint32_t) * mla::index_passes() * mla::index_hist_bins() * B);
+  w.pfx_bits = off;
+  off = align256(off + sizeof(uint32_t) * (mla::index_passes() - 1) * B);
+  w.pfx_rank = off;
+  off = align256(off + sizeof(int32_t) * (mla::index_passes() - 1) * B);
+  w.chunk_above = off;
+  off = align256(off + sizeof(int32_t) * nc * B);
+  w.chunk_suf = off;
+  off = align256(off + sizeof(int32_t) * nc * mla::index_last_bins() * B);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
 size_t mla_index_topk_workspace_size(const mla_dims *dims, int32_t batch, int64_t capacity) {
   std::string why;
   if (!dims_valid(dims, &why) || batch < 0 || capacity < 0) return 0;
-  size_t off = align256(static_cast<size_t>(capacity) * sizeof(float));        // scores
-  off = align256(off + sizeof(uint32_t) * 4 * 256 * static_cast<size_t>(batch));  // histograms
-  off = align256(off + sizeof(int32_t) * 2 * index_chunks() * static_cast<size_t>(batch));  // chunk counts
-  return off;
+  return index_workspace(batch, capacity).total;
 }
 
 mla_status mla_index_topk(const mla_dims *dims, const uint16_t *q_idx, const mla_cache *cache,
@@ -630,12 +663,13 @@ mla_status mla_index_topk(const mla_dims *dims, const uint16_t *q_idx, const mla
   a.top_k = top_k;
   a.n_chunks = index_chunks();
   char *ws = static_cast<char *>(workspace);
-  size_t off = 0;
-  a.scores = reinterpret_cast<float *>(ws + off);
-  off = align256(off + static_cast<size_t>(cache->capacity) * sizeof(float));
-  a.hist = reinterpret_cast<uint32_t *>(ws + off);
-  off = align256(off + sizeof(uint32_t) * 4 * 256 * static_cast<size_t>(batch));
-  a.counts = reinterpret_cast<int32_t *>(ws + off);
+  const IndexWorkspace w = index_workspace(batch, cache->capacity);
+  a.scores = reinterpret_cast<float *>(ws + w.scores);
+  a.hist = reinterpret_cast<uint32_t *>(ws + w.hist);
+  a.pfx_bits = reinterpret_cast<uint32_t *>(ws + w.pfx_bits);
+  a.pfx_rank = reinterpret_cast<int32_t *>(ws + w.pfx_rank);
+  a.chunk_above = reinterpret_cast<int32_t *>(ws + w.chunk_above);
+  a.chunk_suf = reinterpret_cast<int32_t *>(ws + w.chunk_suf);
   a.sel = sel;
   a.n_sel = n_sel;
   hipError_t e = launch_index_topk(a, static_cast<hipStream_t>(stream));

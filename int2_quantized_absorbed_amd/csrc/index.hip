@@ -9,136 +9,43 @@
 // multiply-add rounds exactly like a separate add), and the selection is the
 // top_k tokens by score, equal scores going to the lower token index.
 //
-// Selection = radix select on the scores as ordered 32-bit keys (ordered()
-// maps fp32 to an unsigned integer with the same order), four passes of 8
-// bits from the top.  Pass p histograms digit p of the keys that match the
-// prefix fixed by passes 0..p-1; every block re-derives that prefix from the
-// earlier histograms (a block-wide scan per pass), so no pass needs a
-// separate launch for it.  The k-th largest key T then selects every token
-// with key > T and, of the tokens with key == T, the lowest-indexed ones
-// still needed; a count pass and a write pass emit them in token order.
+// Selection = radix select on the scores as ordered 32-bit keys (ordered_bits
+// maps fp32 to an unsigned integer with the same order), three digits from
+// the top: 12, 12 and 8 bits.  Pass p histograms digit p of the keys that
+// match the prefix fixed by the passes before it; the score kernel does pass
+// 0 as it writes the scores.  Each later launch reads the prefix the launch
+// before it derived and extends it by one digit from that launch's histogram
+// (one block-wide scan), so every launch scans one histogram.  The k-th
+// largest key T selects every token with key > T and, of the tokens with
+// key == T, the lowest-indexed ones still needed.  The last radix pass also
+// keeps, per chunk of the sequence, the count of keys above its prefix and
+// the suffix sums of its own last-digit histogram, from which the write pass
+// knows how many tokens every earlier chunk selects without a count pass.
 #include "kernels.hpp"
 
 namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPasses = 4;
+constexpr int kPasses = 3;
+constexpr int kHistBins = 4096;  // per (pass, sequence) slot: the widest digit
+constexpr int kLastBins = 256;
+
+__host__ __device__ constexpr int digit_bits(int p) { return p == kPasses - 1 ? 8 : 12; }
+__host__ __device__ constexpr int digit_shift(int p) { return p == 0 ? 20 : (p == 1 ? 8 : 0); }
+
+static_assert(digit_bits(0) + digit_bits(1) + digit_bits(2) == 32, "three digits cover the key");
+static_assert(digit_shift(1) + digit_bits(1) == digit_shift(0), "digits are contiguous");
+static_assert(digit_shift(2) + digit_bits(2) == digit_shift(1), "digits are contiguous");
+static_assert((1 << digit_bits(kPasses - 1)) == kLastBins, "last digit");
 
 __device__ __forceinline__ uint32_t ordered_bits(float s) {
   const uint32_t b = __float_as_uint(s);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// scores[base + t] = q_idx[b] . idx_key[base + t], t < L_b.  Block (b, 0)
-// also clears pass 0's histogram of b.  D = index_head_dim (compile-time,
-// so each lane's key loads are all in flight together).
-template <int D>
-__global__ __launch_bounds__(kThreads) void index_score_kernel(IndexArgs a) {
-  __shared__ float q[D];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  for (int e = tid; e < D; e += kThreads) q[e] = bf16_to_f32(a.q_idx[static_cast<int64_t>(b) * D + e]);
-  if (blockIdx.y == 0) a.hist[(0 * a.B + b) * 256 + tid] = 0u;
-  __syncthreads();
-  const int L = a.seq_len[b];
-  const int64_t base = a.seq_base[b];
-  for (int t = blockIdx.y * kThreads + tid; t < L; t += gridDim.y * kThreads) {
-    const uint4 *k = reinterpret_cast<const uint4 *>(a.idx_key + (base + t) * D);
-    uint4 raw[D / 8];
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) raw[i] = k[i];
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = __builtin_fmaf(__uint_as_float(w[j] << 16), q[8 * i + 2 * j], acc);
-        acc = __builtin_fmaf(__uint_as_float(w[j] & 0xffff0000u), q[8 * i + 2 * j + 1], acc);
-      }
-    }
-    a.scores[base + t] = acc;
-  }
-}
-
-// Prefix (the key bits fixed by the first p passes) and the rank still to
-// find inside it, from the histograms of sequence b.  Called by the whole
-// block; per pass one block-wide scan over the 256 bins from the top.
-struct Prefix {
-  uint32_t bits;
-  int k_rem;
-};
-
-__device__ Prefix derive_prefix(const uint32_t *hist, int B, int b, int p, int k) {
-  __shared__ int wtot[kThreads / 64];
-  __shared__ Prefix px;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  Prefix x{0u, k};
-  for (int q = 0; q < p; ++q) {
-    // thread i looks at bin 255 - i: inclusive count of keys in bins >= it
-    const int c = static_cast<int>(hist[(static_cast<int64_t>(q) * B + b) * 256 + 255 - tid]);
-    int inc = c;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(inc, off);
-      if (lane >= off) inc += y;
-    }
-    if (lane == 63) wtot[wv] = inc;
-    __syncthreads();
-    for (int j = 0; j < wv; ++j) inc += wtot[j];
-    const int above = inc - c;
-    if (above < x.k_rem && inc >= x.k_rem) {
-      px.bits = (x.bits << 8) | static_cast<uint32_t>(255 - tid);
-      px.k_rem = x.k_rem - above;
-    }
-    __syncthreads();
-    x = px;
-    __syncthreads();  // px and wtot are rewritten by the next pass
-  }
-  return x;
-}
-
-// Chunk c of sequence b: tokens [c * chunk, (c + 1) * chunk), chunk =
-// ceil(L / n_chunks); the block reads it kUnroll groups of kThreads tokens at
-// a time, loads first (clamped to the chunk, so none is predicated).
-constexpr int kUnroll = 4;
-
-__device__ __forceinline__ void chunk_range(int L, int n_chunks, int c, int *t0, int *t1) {
-  const int cl = (L + n_chunks - 1) / n_chunks;
-  *t0 = min(L, c * cl);
-  *t1 = min(L, *t0 + cl);
-}
-
-template <typename F>
-__device__ __forceinline__ void for_chunk_keys(const float *scores, int64_t base, int t0, int t1, F f) {
-  const int tid = threadIdx.x;
-  for (int g = t0; g < t1; g += kUnroll * kThreads) {
-    uint32_t key[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) key[u] = ordered_bits(scores[base + min(g + u * kThreads + tid, t1 - 1)]);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) f(g + u * kThreads, g + u * kThreads + tid, key[u]);
-  }
-}
-
-// Pass p: histogram of digit p over the keys matching the prefix.  Block
-// (b, 0) clears the next pass's histogram of b.
-__global__ __launch_bounds__(kThreads) void radix_pass_kernel(IndexArgs a, int p) {
-  __shared__ uint32_t h[256];
-  const int b = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  const int L = a.seq_len[b];
-  if (L <= a.top_k) return;  // everything is selected
-  h[tid] = 0u;
-  const Prefix pre = derive_prefix(a.hist, a.B, b, p, a.top_k);
-  if (c == 0 && p + 1 < kPasses) a.hist[(static_cast<int64_t>(p + 1) * a.B + b) * 256 + tid] = 0u;
-  __syncthreads();
-  const int shift = 24 - 8 * p;
-  int t0, t1;
-  chunk_range(L, a.n_chunks, c, &t0, &t1);
-  for_chunk_keys(a.scores, a.seq_base[b], t0, t1, [&](int, int t, uint32_t key) {
-    if (t < t1 && (p == 0 || (key >> (shift + 8)) == pre.bits)) atomicAdd(&h[(key >> shift) & 255u], 1u);
-  });
-  __syncthreads();
-  if (h[tid] != 0u) atomicAdd(&a.hist[(static_cast<int64_t>(p) * a.B + b) * 256 + tid], h[tid]);
+__device__ __forceinline__ uint32_t *hist_of(const IndexArgs &a, int p, int b) {
+  return a.hist + (static_cast<int64_t>(p) * a.B + b) * kHistBins;
 }
 
 // Block-wide exclusive scan of one int per thread; total in *tot.
@@ -158,81 +65,281 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wtot, int *tot) {
   return before + inc - v;
 }
 
-// Count pass: per chunk, tokens above the threshold key and tokens equal to it.
-__global__ __launch_bounds__(kThreads) void select_count_kernel(IndexArgs a) {
-  __shared__ int wsum[2][kThreads / 64];
-  const int b = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  const int L = a.seq_len[b];
-  const bool all = L <= a.top_k;
-  const uint32_t thr = all ? 0u : derive_prefix(a.hist, a.B, b, kPasses, a.top_k).bits;
-  int t0, t1;
-  chunk_range(L, a.n_chunks, c, &t0, &t1);
-  int gt = 0, eq = 0;
-  for_chunk_keys(a.scores, a.seq_base[b], t0, t1, [&](int, int t, uint32_t key) {
-    gt += (t < t1 && (all || key > thr)) ? 1 : 0;
-    eq += (t < t1 && !all && key == thr) ? 1 : 0;
-  });
-  for (int off = 32; off > 0; off >>= 1) {
-    gt += __shfl_xor(gt, off);
-    eq += __shfl_xor(eq, off);
+// Clears the three histograms of every sequence (grid (B, kPasses)).
+__global__ __launch_bounds__(kThreads) void index_clear_kernel(IndexArgs a) {
+  uint4 *h = reinterpret_cast<uint4 *>(hist_of(a, blockIdx.y, blockIdx.x));
+#pragma unroll
+  for (int i = 0; i < kHistBins / 4 / kThreads; ++i) h[i * kThreads + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Flushes a block's LDS histogram into the global one (nonzero bins only).
+template <int NB>
+__device__ __forceinline__ void flush_hist(const uint32_t *h, uint32_t *g) {
+#pragma unroll
+  for (int i = 0; i < NB / kThreads; ++i) {
+    const int bin = i * kThreads + threadIdx.x;
+    if (h[bin] != 0u) atomicAdd(&g[bin], h[bin]);
   }
-  if ((tid & 63) == 0) {
-    wsum[0][tid >> 6] = gt;
-    wsum[1][tid >> 6] = eq;
+}
+
+// scores[base + t] = q_idx[b] . idx_key[base + t], t < L_b, and radix pass
+// 0 (digit 0 of every key) when the sequence has more than top_k tokens.
+// D = index_head_dim (compile-time, so each lane's key loads are all in
+// flight together).
+template <int D>
+__global__ __launch_bounds__(kThreads) void index_score_kernel(IndexArgs a) {
+  __shared__ float q[D];
+  __shared__ uint32_t h[1 << digit_bits(0)];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < D; e += kThreads) q[e] = bf16_to_f32(a.q_idx[static_cast<int64_t>(b) * D + e]);
+  const int L = a.seq_len[b];
+  const bool radix = L > a.top_k;
+  if (radix) {
+#pragma unroll
+    for (int i = 0; i < (1 << digit_bits(0)) / kThreads; ++i) h[i * kThreads + tid] = 0u;
   }
   __syncthreads();
-  if (tid == 0) {
-    a.counts[(b * a.n_chunks + c) * 2 + 0] = (wsum[0][0] + wsum[0][1]) + (wsum[0][2] + wsum[0][3]);
-    a.counts[(b * a.n_chunks + c) * 2 + 1] = (wsum[1][0] + wsum[1][1]) + (wsum[1][2] + wsum[1][3]);
+  const int64_t base = a.seq_base[b];
+  for (int t = blockIdx.y * kThreads + tid; t < L; t += gridDim.y * kThreads) {
+    const uint4 *k = reinterpret_cast<const uint4 *>(a.idx_key + (base + t) * D);
+    uint4 raw[D / 8];
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) raw[i] = k[i];
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = __builtin_fmaf(__uint_as_float(w[j] << 16), q[8 * i + 2 * j], acc);
+        acc = __builtin_fmaf(__uint_as_float(w[j] & 0xffff0000u), q[8 * i + 2 * j + 1], acc);
+      }
+    }
+    a.scores[base + t] = acc;
+    if (radix) atomicAdd(&h[ordered_bits(acc) >> digit_shift(0)], 1u);
+  }
+  if (!radix) return;  // uniform over the block
+  __syncthreads();
+  flush_hist<1 << digit_bits(0)>(h, hist_of(a, 0, b));
+}
+
+// The key bits fixed so far and the rank still to find among the keys that
+// carry them.
+struct Prefix {
+  uint32_t bits;
+  int k_rem;
+};
+
+// Extends `x` (the prefix after passes 0..p-1) by digit p, from pass p's
+// histogram of sequence b: the bin, counted from the top, in which the
+// k_rem-th largest matching key falls.  Called by the whole block; thread i
+// reads the i-th run of NB / kThreads bins from the top.
+template <int P>
+__device__ Prefix extend_prefix(const IndexArgs &a, int b, Prefix x) {
+  constexpr int NB = 1 << digit_bits(P), M = NB / kThreads;
+  __shared__ int wtot[kThreads / 64];
+  __shared__ Prefix px;
+  const int tid = threadIdx.x;
+  const uint32_t *hist = hist_of(a, P, b) + NB - (tid + 1) * M;  // bins [NB - (tid+1)M, NB - tid M)
+  uint32_t c[M];
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < M / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4 *>(hist)[i];
+      c[4 * i] = v.x;
+      c[4 * i + 1] = v.y;
+      c[4 * i + 2] = v.z;
+      c[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < M; ++i) c[i] = hist[i];
+  }
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) sum += static_cast<int>(c[i]);
+  if (tid == 0) px = Prefix{x.bits << digit_bits(P), x.k_rem};  // kept only if no bin matches
+  int tot;
+  const int above = block_excl_scan(sum, wtot, &tot);
+  if (above < x.k_rem && above + sum >= x.k_rem) {
+    int run = above;
+#pragma unroll
+    for (int i = M - 1; i >= 0; --i) {  // descending bins
+      const int ci = static_cast<int>(c[i]);
+      if (run < x.k_rem && run + ci >= x.k_rem) {
+        px.bits = (x.bits << digit_bits(P)) | static_cast<uint32_t>(NB - (tid + 1) * M + i);
+        px.k_rem = x.k_rem - run;
+      }
+      run += ci;
+    }
+  }
+  __syncthreads();
+  const Prefix r = px;
+  __syncthreads();  // px is rewritten by a later call
+  return r;
+}
+
+// Prefix after passes 0..P-1: pass 0 needs nothing; later ones read what the
+// previous launch stored for sequence b.
+template <int P>
+__device__ __forceinline__ Prefix stored_prefix(const IndexArgs &a, int b) {
+  if constexpr (P == 0) {
+    return Prefix{0u, a.top_k};
+  } else {
+    return Prefix{a.pfx_bits[(P - 1) * a.B + b], a.pfx_rank[(P - 1) * a.B + b]};
+  }
+}
+
+// Chunk c of sequence b: tokens [c * cl, (c + 1) * cl), cl = ceil(L /
+// n_chunks).  A group is kUnroll * kThreads consecutive tokens; thread i
+// holds tokens g + kUnroll i + u, u < kUnroll (contiguous per thread, so a
+// block-wide scan of per-thread counts follows token order).  Loads are
+// clamped to the chunk, so none is predicated; the caller never loads from
+// an empty chunk.
+constexpr int kUnroll = 4;
+constexpr int kGroup = kUnroll * kThreads;
+
+__device__ __forceinline__ void chunk_range(int L, int n_chunks, int c, int *t0, int *t1) {
+  const int cl = (L + n_chunks - 1) / n_chunks;
+  *t0 = min(L, c * cl);
+  *t1 = min(L, *t0 + cl);
+}
+
+__device__ __forceinline__ void load_group(const float *scores, int64_t base, int g, int t1, uint32_t key[kUnroll]) {
+  const int t = g + kUnroll * static_cast<int>(threadIdx.x);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) key[u] = ordered_bits(scores[base + min(t + u, t1 - 1)]);
+}
+
+// Radix pass P (1 .. kPasses-1) over chunk blockIdx.y of sequence blockIdx.x:
+// histogram of digit P over the keys that match the prefix.  The last pass
+// also stores the chunk's count of keys above the prefix and the suffix sums
+// of its own histogram.
+template <int P>
+__global__ __launch_bounds__(kThreads) void radix_pass_kernel(IndexArgs a) {
+  constexpr int NB = 1 << digit_bits(P);
+  constexpr bool kLast = P == kPasses - 1;
+  __shared__ uint32_t h[NB];
+  __shared__ int wtot[kThreads / 64];
+  const int b = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int L = a.seq_len[b];
+  if (L <= a.top_k) return;  // everything is selected
+  const int64_t base = a.seq_base[b];
+  int t0, t1;
+  chunk_range(L, a.n_chunks, c, &t0, &t1);
+  uint32_t key[kUnroll];
+  if (t0 < t1) load_group(a.scores, base, t0, t1, key);  // in flight while the prefix is derived
+#pragma unroll
+  for (int i = 0; i < NB / kThreads; ++i) h[i * kThreads + tid] = 0u;
+  const Prefix pre = extend_prefix<P - 1>(a, b, stored_prefix<P - 1>(a, b));
+  if (c == 0 && tid == 0) {
+    a.pfx_bits[(P - 1) * a.B + b] = pre.bits;
+    a.pfx_rank[(P - 1) * a.B + b] = pre.k_rem;
+  }
+  constexpr int kShift = digit_shift(P);
+  int above = 0;
+  for (int g = t0; g < t1; g += kGroup) {
+    if (g != t0) load_group(a.scores, base, g, t1, key);
+    const int t = g + kUnroll * tid;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t hi = key[u] >> (kShift + digit_bits(P));
+      if (t + u < t1 && hi == pre.bits) atomicAdd(&h[(key[u] >> kShift) & (NB - 1)], 1u);
+      if (kLast) above += (t + u < t1 && hi > pre.bits) ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  flush_hist<NB>(h, hist_of(a, P, b));
+  if constexpr (kLast) {
+    // thread i: bin NB-1-i; inclusive count of the chunk's matching keys in bins >= it
+    const int own = static_cast<int>(h[NB - 1 - tid]);
+    int tot;
+    const int excl = block_excl_scan(own, wtot, &tot);
+    const int64_t row = static_cast<int64_t>(b) * a.n_chunks + c;
+    a.chunk_suf[row * NB + NB - 1 - tid] = excl + own;
+    block_excl_scan(above, wtot, &tot);
+    if (tid == 0) a.chunk_above[row] = tot;
   }
 }
 
 // Write pass: each chunk writes its selected tokens, in token order, after
-// those of the chunks before it; of the tokens equal to the threshold key
-// the first k_eq in token order are selected.  Block (b, 0) writes n_sel[b].
+// those of the chunks before it.  A token is selected if its key is above
+// the threshold key T, or equal to T with fewer than k_eq tokens equal to T
+// before it; the selected tokens before a token number (keys above T before
+// it) + min(keys equal to T before it, k_eq).  Block (b, 0) writes n_sel[b].
 __global__ __launch_bounds__(kThreads) void select_write_kernel(IndexArgs a) {
+  constexpr int P = kPasses - 1;
   __shared__ int wtot[kThreads / 64];
   const int b = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int L = a.seq_len[b];
   const bool all = L <= a.top_k;
-  const Prefix pre = all ? Prefix{0u, 0} : derive_prefix(a.hist, a.B, b, kPasses, a.top_k);
-  const uint32_t thr = pre.bits;
-  const int k_eq = pre.k_rem;  // tokens needed from those equal to the threshold
-  // counts of the chunks before this one (one per thread, n_chunks <= kThreads)
-  int gt_before, eq_before;
-  {
-    const int j = tid;
-    const int g = j < c ? a.counts[(b * a.n_chunks + j) * 2 + 0] : 0;
-    const int e = j < c ? a.counts[(b * a.n_chunks + j) * 2 + 1] : 0;
-    block_excl_scan(g, wtot, &gt_before);
-    block_excl_scan(e, wtot, &eq_before);
-  }
-  if (c == 0 && tid == 0) a.n_sel[b] = min(L, a.top_k);
+  const int64_t base = a.seq_base[b];
   int t0, t1;
   chunk_range(L, a.n_chunks, c, &t0, &t1);
-  int eq_run = eq_before;                          // equal-key tokens before this group
-  int pos = gt_before + min(eq_before, k_eq);      // selected tokens before this group
-  for_chunk_keys(a.scores, a.seq_base[b], t0, t1, [&](int, int t, uint32_t key) {
-    const int is_gt = (t < t1 && (all || key > thr)) ? 1 : 0;
-    const int is_eq = (t < t1 && !all && key == thr) ? 1 : 0;
-    int n_eq, n_sel;
-    const int eq_rank = eq_run + block_excl_scan(is_eq, wtot, &n_eq);
-    const int sel = is_gt | ((is_eq && eq_rank < k_eq) ? 1 : 0);
-    const int idx = pos + block_excl_scan(sel, wtot, &n_sel);
-    if (sel && idx < a.top_k) a.sel[static_cast<int64_t>(b) * a.top_k + idx] = t;
-    pos += n_sel;
-    eq_run += n_eq;
-  });
+  uint32_t key[kUnroll];
+  if (t0 < t1) load_group(a.scores, base, t0, t1, key);
+  if (c == 0 && tid == 0) a.n_sel[b] = min(L, a.top_k);
+  uint32_t thr = 0u;
+  int k_eq = 0, gt_run = t0, eq_run = 0;  // every token before the chunk is selected when all
+  if (!all) {  // uniform over the block
+    const Prefix pre = extend_prefix<P>(a, b, stored_prefix<P>(a, b));
+    thr = pre.bits;
+    k_eq = pre.k_rem;
+    // tokens of the chunks before this one above and equal to T (n_chunks <= kThreads)
+    const int d = static_cast<int>(thr & (kLastBins - 1));
+    int gt_j = 0, eq_j = 0;
+    if (tid < c) {
+      const int64_t row = static_cast<int64_t>(b) * a.n_chunks + tid;
+      const int s_d = a.chunk_suf[row * kLastBins + d];
+      const int s_up = d + 1 < kLastBins ? a.chunk_suf[row * kLastBins + d + 1] : 0;
+      gt_j = a.chunk_above[row] + s_up;
+      eq_j = s_d - s_up;
+    }
+    block_excl_scan(gt_j, wtot, &gt_run);
+    block_excl_scan(eq_j, wtot, &eq_run);
+  }
+  int32_t *out = a.sel + static_cast<int64_t>(b) * a.top_k;
+  for (int g = t0; g < t1; g += kGroup) {
+    if (g != t0) load_group(a.scores, base, g, t1, key);
+    const int t = g + kUnroll * tid;
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      n_gt += (t + u < t1 && (all || key[u] > thr)) ? 1 : 0;
+      n_eq += (t + u < t1 && !all && key[u] == thr) ? 1 : 0;
+    }
+    int tot;  // per group both counts are at most kGroup < 2^16: one packed scan
+    const int before = block_excl_scan(n_gt | (n_eq << 16), wtot, &tot);
+    int gb = gt_run + (before & 0xffff), eb = eq_run + (before >> 16);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (t + u >= t1) break;
+      if (all || key[u] > thr) {
+        const int idx = gb + min(eb, k_eq);  // eb = k_eq = 0 when all
+        if (idx < a.top_k) out[idx] = t + u;
+        ++gb;
+      } else if (key[u] == thr) {
+        if (eb < k_eq && gb + eb < a.top_k) out[gb + eb] = t + u;
+        ++eb;
+      }
+    }
+    gt_run += tot & 0xffff;
+    eq_run += tot >> 16;
+  }
 }
 
 }  // namespace
 
 int index_chunks() { return kThreads; }
+int index_hist_bins() { return kHistBins; }
+int index_passes() { return kPasses; }
+int index_last_bins() { return kLastBins; }
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   const dim3 chunks(a.B, a.n_chunks);
   {
     TimedLaunch tl("index_score", s);
+    index_clear_kernel<<<dim3(a.B, kPasses), kThreads, 0, s>>>(a);
     switch (a.d_idx) {
       case 64: index_score_kernel<64><<<chunks, kThreads, 0, s>>>(a); break;
       case 128: index_score_kernel<128><<<chunks, kThreads, 0, s>>>(a); break;
@@ -240,8 +347,8 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
     }
   }
   TimedLaunch tl("index_select", s);
-  for (int p = 0; p < kPasses; ++p) radix_pass_kernel<<<chunks, kThreads, 0, s>>>(a, p);
-  select_count_kernel<<<chunks, kThreads, 0, s>>>(a);
+  radix_pass_kernel<1><<<chunks, kThreads, 0, s>>>(a);
+  radix_pass_kernel<2><<<chunks, kThreads, 0, s>>>(a);
   select_write_kernel<<<chunks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }

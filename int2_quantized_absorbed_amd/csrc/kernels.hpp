@@ -54,6 +54,7 @@ struct DecodeArgs {
   float *part_ml;       // [max_items][M][2]  (m in log2 units, l)
   int32_t max_items;
   int32_t target_items;
+  int32_t min_chunk_tiles;  // smallest split-K item, in tiles
   int32_t tile;
   // sparse decode: token t of sequence b is cache slot seq_base[b] +
   // sel[b * sel_stride + t] (seq_len then holds the selected counts); dense
@@ -72,12 +73,18 @@ struct IndexArgs {
   const int32_t *seq_len;
   int32_t B, d_idx, top_k, n_chunks;
   float *scores;            // [capacity], by cache slot
-  uint32_t *hist;           // [4][B][256]
-  int32_t *counts;          // [B][n_chunks][2]: above / equal to the threshold
+  uint32_t *hist;           // [index_passes()][B][index_hist_bins()]
+  uint32_t *pfx_bits;       // [index_passes() - 1][B]: key prefix after passes 0..p
+  int32_t *pfx_rank;        // [index_passes() - 1][B]: rank still to find inside it
+  int32_t *chunk_above;     // [B][n_chunks]: keys above the last pass's prefix
+  int32_t *chunk_suf;       // [B][n_chunks][index_last_bins()]: suffix sums of the last digit
   int32_t *sel;             // [B][top_k]
   int32_t *n_sel;           // [B]
 };
 int index_chunks();
+int index_hist_bins();
+int index_passes();
+int index_last_bins();
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s);
 
 hipError_t launch_absorb_f32(const DecodeArgs &a, hipStream_t s);

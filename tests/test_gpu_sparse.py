@@ -4,7 +4,9 @@
   with the oracle's (``index_scores`` then ``index_topk``): integer output,
   so bit-exact.  Cases: ragged lengths across several selection chunks,
   sequences shorter than, equal to and just longer than top_k, an empty one,
-  top_k = 1, and duplicated key rows (equal scores: the lower index wins).
+  top_k = 1, duplicated key rows (equal scores: the lower index wins), chunks
+  longer than one scan group of the write pass, and keys drawn from a small
+  pool of rows (long runs of equal scores spanning many chunks).
 * ``mla_decode_sparse``: on the selection the GPU returned (itself checked
   above), outputs and lse against ``sparse_absorbed_attention`` to the decode
   tolerance, on the MFMA and on the vector-ALU kernel.
@@ -25,10 +27,12 @@ pytestmark = pytest.mark.gpu
 D_IDX = 64
 
 
-def _index_case(lens, seed, dup=0):
+def _index_case(lens, seed, dup=0, pool=0):
     rng = np.random.default_rng(seed)
     base, cap = S.contiguous_layout(lens, 5)
     keys = S.bf16_normal(rng, (cap, D_IDX))
+    if pool:
+        keys = keys[rng.integers(0, pool, size=cap)]
     if dup:
         # copy rows inside each sequence so that several tokens score equally
         for b, L in enumerate(lens):
@@ -54,17 +58,19 @@ def _run_topk(dims, lens, base, cap, keys, q, top_k):
 
 
 TOPK_CASES = [
-    ("ragged", [5000, 2049, 2048, 300, 0, 7000], 2048, 0),
-    ("k1", [17, 1, 999], 1, 0),
-    ("ties", [4096, 3000], 512, 400),
-    ("long", [40000], 2048, 50),
+    ("ragged", [5000, 2049, 2048, 300, 0, 7000], 2048, 0, 0),
+    ("k1", [17, 1, 999], 1, 0, 0),
+    ("ties", [4096, 3000], 512, 400, 0),
+    ("long", [40000], 2048, 50, 0),
+    ("multigroup", [600001, 3], 2048, 3000, 0),
+    ("pool", [20000, 1500], 3000, 0, 40),
 ]
 
 
-@pytest.mark.parametrize("name,lens,top_k,dup", TOPK_CASES)
-def test_index_topk_matches_oracle(name, lens, top_k, dup):
+@pytest.mark.parametrize("name,lens,top_k,dup,pool", TOPK_CASES)
+def test_index_topk_matches_oracle(name, lens, top_k, dup, pool):
     C.say(f"index top-k {name} lens={lens} top_k={top_k}")
-    base, cap, keys, q = _index_case(lens, 11, dup)
+    base, cap, keys, q = _index_case(lens, 11, dup, pool)
     sel, n_sel = _run_topk(_dims(), lens, base, cap, keys, q, top_k)
     for b, L in enumerate(lens):
         a = int(base[b])
