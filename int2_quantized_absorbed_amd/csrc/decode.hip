@@ -19,11 +19,11 @@ namespace mla {
 namespace {
 
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ seq_len, int B,
-                                                   int target, int tile, int max_items,
+                                                   int target, int tile, int min_k, int max_items,
                                                    WorkItem *__restrict__ items,
                                                    int32_t *__restrict__ item_begin,
                                                    int32_t *__restrict__ meta) {
-  plan_block(seq_len, B, target, tile, max_items, items, item_begin, meta);
+  plan_block(seq_len, B, target, tile, min_k, max_items, items, item_begin, meta);
 }
 
 // q~ in fp32, row-major [B*M][r + d_r] with M = Tq*H rows per sequence
@@ -342,8 +342,8 @@ __global__ __launch_bounds__(256) void upproj_valu_kernel(DecodeArgs a) {
 
 hipError_t launch_plan(const DecodeArgs &a, hipStream_t s) {
   TimedLaunch tl("decode_plan", s);
-  plan_kernel<<<1, 256, 0, s>>>(a.seq_len, a.B, a.target_items, a.tile, a.max_items, a.items,
-                                a.item_begin, a.meta);
+  plan_kernel<<<1, 256, 0, s>>>(a.seq_len, a.B, a.target_items, a.tile, a.min_chunk_tiles, a.max_items,
+                                a.items, a.item_begin, a.meta);
   return hipGetLastError();
 }
 

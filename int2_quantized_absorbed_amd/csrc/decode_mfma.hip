@@ -273,7 +273,8 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   };
 
   // ---- prologue: tile 0 scores summed in registers, tiles 0 and 1 in the
-  // Z buffers, tile 1 dequantised, tile 2 in flight ----
+  // Z buffers, tile 1 dequantised, tile 2 in flight (issued with tiles 0
+  // and 1, so the first iteration does not wait for it) ----
   f16x8 bz[KB];
   f32x16 sacc[2];
   const int zsw = 8 * ((l32 >> 3) & 1);  // chunk kb goes to kb ^ 1 in rows 8..15, 24..31
@@ -315,9 +316,11 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
             f32x4{acc[mt][4 * j], acc[mt][4 * j + 1], acc[mt][4 * j + 2], acc[mt][4 * j + 3]};
   };
   float s_next[8];
+  RawTile raw;
   {
     const RawTile r0 = load_tile<G>(a, tile_slot(0), w, hf);
     const RawTile r1 = load_tile<G>(a, tile_slot(1), w, hf);
+    raw = load_tile<G>(a, tile_slot(2), w, hf);
     dequant<G>(r0, bz);
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
@@ -330,7 +333,6 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     publish(sacc);
     dequant<G>(r1, bz);
   }
-  RawTile raw = load_tile<G>(a, tile_slot(2), w, hf);
   lds_barrier();
   read_scores(s_next);
 
@@ -365,6 +367,8 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     tmax = reduce4<true>(tmax);
     const bool need = tmax > m_run + kRescaleThreshold;   // true on the first visible tile
     const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
+    // a row's O is still zero until its first visible tile: no rescale then
+    const bool scale_o = need && m_run != -INFINITY;
     m_run = need ? tmax : m_run;
     const float m_sub = (m_run == -INFINITY) ? 0.0f : m_run;
     float psum = 0.0f;
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     // every lane stores (the quad's lanes and the wave's lanes store equal
     // values to one address), which keeps this block branch-free
     sm.alpha[s_row] = alpha;
-    sm.resc[w] = __any(need ? 1 : 0);
+    sm.resc[w] = __any(scale_o ? 1 : 0);
     lds_barrier();  // A: P, alpha and the rescale flags of tile i
 
 
@@ -434,18 +438,32 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
   }
 
   // ---- write the partial (O, m, l) of this work item ----
+  // Each 32x32 accumulator tile (rows 32 mt.., the 32 contiguous channels
+  // 128 w + 32 nt..) goes through this wave's own Z buffers (no other wave
+  // touches them) so that every lane then stores 16 contiguous bytes of one
+  // row.  Staged position of (row, col): rows in pairs of 64 floats, the half
+  // chosen by bit 0 xor bit 2 of the row, so the 4-row-apart halves a store
+  // writes and the adjacent rows a 16-lane read takes fall in disjoint banks.
+  auto stage_pos = [](int row, int col) { return (row >> 1) * 64 + 32 * ((row ^ (row >> 2)) & 1) + col; };
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int sl = 32 * nt + l32;  // slot of the wave's Z tile
-    const int ch = 128 * w + slot_channel(sl >> 6, (sl & 63) >> 3, sl & 7);
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int nt = 0; nt < 4; ++nt) {
+      float *st = reinterpret_cast<float *>(sm.z[nt & 1][w]);
+      const int sl = 32 * nt + l32;  // slot of the wave's Z tile
+      const int col = slot_channel(sl >> 6, (sl & 63) >> 3, sl & 7) - 32 * nt;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = rb * ROWS + 32 * mt + 8 * (v >> 2) + 4 * hf + (v & 3);
-        if (m < M) a.part_o[(static_cast<int64_t>(item) * M + m) * R + ch] = o[mt][nt][v];
+      for (int v = 0; v < 16; ++v) st[stage_pos(8 * (v >> 2) + 4 * hf + (v & 3), col)] = o[mt][nt][v];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 8 * j + (l >> 3), q = l & 7;
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(st + stage_pos(row, 4 * q));
+        const int m = rb * ROWS + 32 * mt + row;
+        if (m < M)  // streamed out (read once, by the combine kernel)
+          __builtin_nontemporal_store(
+              x, reinterpret_cast<f32x4 *>(a.part_o + (static_cast<int64_t>(item) * M + m) * R + 128 * w + 32 * nt + 4 * q));
       }
-  }
+    }
   if (s_k8 == 0 && s_m < M) {
     a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 0] = m_run;
     a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 1] = l_run;
@@ -474,7 +492,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_c
   // that column has nothing to do
   if (blockIdx.x == 0) {
     if (blockIdx.y == 0)
-      plan_block(a.seq_len, a.B, a.target_items, a.tile, a.max_items, a.items, a.item_begin, a.meta);
+      plan_block(a.seq_len, a.B, a.target_items, a.tile, a.min_chunk_tiles, a.max_items, a.items, a.item_begin,
+                 a.meta);
     return;
   }
   const int h = (blockIdx.x - 1) >> 2, cq = (blockIdx.x - 1) & 3, rt = blockIdx.y;

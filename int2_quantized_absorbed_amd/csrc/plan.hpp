@@ -20,7 +20,11 @@ __device__ inline int plan_wave_incl_scan(int x, int lane) {
 // The item count is non-increasing in C; the planner takes the smallest C
 // whose count fits `target` (the work-item slots that fill the GPU), so the
 // grid is as full as the lengths allow, or one item per sequence when even
-// that exceeds target.  max_items bounds the count and the item array.
+// that exceeds target.  C is at least min_k tiles (or the longest
+// sequence), so an item holds more than half of that, a sequence's last item
+// aside: an item has a fixed cost (its query rows in, its partial rows out)
+// that one or two tiles of tokens do not repay.  max_items bounds the count
+// and the item array.
 __device__ inline int plan_items_of(int L, int C, int tile, int *chunk_out) {
   if (L <= 0) {
     *chunk_out = 0;
@@ -34,7 +38,7 @@ __device__ inline int plan_items_of(int L, int C, int tile, int *chunk_out) {
 }
 
 __device__ inline void plan_block(const int32_t *__restrict__ seq_len, int B, int target, int tile,
-                                  int max_items, WorkItem *__restrict__ items,
+                                  int min_k, int max_items, WorkItem *__restrict__ items,
                                   int32_t *__restrict__ item_begin, int32_t *__restrict__ meta) {
   // called by one whole block of 256 threads
   __shared__ long long wsum[4];
@@ -88,6 +92,8 @@ __device__ inline void plan_block(const int32_t *__restrict__ seq_len, int B, in
     const long long per_lo = T * tile, per_hi = (T - nonempty) * tile;
     lo = static_cast<int>(min<long long>(khi, max<long long>(1, (total + per_lo - 1) / per_lo)));
     hi = static_cast<int>(min<long long>(khi, max<long long>(lo, (total + per_hi - 1) / per_hi)));
+    lo = max(lo, min(khi, min_k));
+    hi = max(hi, lo);
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (count(mid) <= target)
