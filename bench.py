@@ -197,7 +197,7 @@ def main():
         step(k)
     torch.cuda.synchronize()
     kernels = {}
-    for name in ("append_quant", "decode_plan", "absorb_q", "splitk_decode", "combine", "up_proj"):
+    for name in ("append_quant", "decode_plan", "absorb_q", "splitk_decode", "combine", "up_proj", "combine_up_proj"):
         ms, n = M.mla_timing_query(name)
         if n:
             kernels[name] = round(ms / n * 1e3, 3)
@@ -365,7 +365,7 @@ def sparse_bench(M, S, dev, args):
         step()
     torch.cuda.synchronize()
     k_us = {}
-    for name in ("index_score", "index_select", "absorb_q", "splitk_decode", "combine", "up_proj"):
+    for name in ("index_score", "index_select", "absorb_q", "splitk_decode", "combine", "up_proj", "combine_up_proj"):
         ms, cnt = M.mla_timing_query(name)
         if cnt:
             k_us[name] = round(ms / cnt * 1e3, 3)

@@ -155,7 +155,7 @@ int target_items(int rows, bool mfma) {
 // (query rows in, partial rows out, the combine reading them back) outweighs
 // spreading a short context over more compute units.
 #ifndef MLA_SPLIT_MIN_TOKENS
-#define MLA_SPLIT_MIN_TOKENS 32
+#define MLA_SPLIT_MIN_TOKENS 64
 #endif
 int min_chunk_tiles(int tile) { return (MLA_SPLIT_MIN_TOKENS + tile - 1) / tile; }
 
@@ -181,7 +181,7 @@ WsLayout layout(const mla_dims &d, int B, int Tq) {
   w.oz = off;
   off = align256(off + static_cast<size_t>(B) * M * r * sizeof(float));
   w.part_o = off;
-  off = align256(off + static_cast<size_t>(w.max_items) * M * r * sizeof(float));
+  off = align256(off + static_cast<size_t>(w.max_items) * M * r * sizeof(uint16_t));
   w.part_ml = off;
   off = align256(off + static_cast<size_t>(w.max_items) * M * 2 * sizeof(float));
   w.total = off;
@@ -563,7 +563,7 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
   a.meta = reinterpret_cast<int32_t *>(ws + w.meta);
   a.qbuf = ws + w.qbuf;
   a.oz = reinterpret_cast<float *>(ws + w.oz);
-  a.part_o = reinterpret_cast<float *>(ws + w.part_o);
+  a.part_o = reinterpret_cast<uint16_t *>(ws + w.part_o);
   a.part_ml = reinterpret_cast<float *>(ws + w.part_ml);
   a.max_items = w.max_items;
   a.target_items = target_items(M, use_mfma);

@@ -173,13 +173,18 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
       }
     }
   }
+  // partial O normalised by its row's l, in fp16
+  __syncthreads();  // the last tile's alpha reads are done
+  if (scorer && stok == 0) al_s[srow] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  __syncthreads();
+  f16 *po = reinterpret_cast<f16 *>(a.part_o);
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     if (i < na) {
       const int e = tid + 256 * i;
       const int row = e / r, j = e % r;
       const int m = row0 + row;
-      if (m < M) a.part_o[(static_cast<int64_t>(item) * M + m) * r + j] = acc[i];
+      if (m < M) po[(static_cast<int64_t>(item) * M + m) * r + j] = f32_to_f16(acc[i] * al_s[row]);
     }
   }
   if (scorer && stok == 0 && sm < M) {
@@ -190,7 +195,8 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
 
 // Log-sum-exp merge of the split-K partials of one query row (b, t, h):
 // m = max_i m_i, o_z = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i,
-// lse = ln 2 * (m + log2 sum_i 2^(m_i - m) l_i).  One block per row; thread
+// lse = ln 2 * (m + log2 sum_i 2^(m_i - m) l_i), with O_i = l_i * (the
+// stored fp16 O_i / l_i).  One block per row; thread
 // -> (item slice s, 4-channel chunk c).  Slice s folds items ib + s,
 // ib + s + S, ... into a running (max, sum, O) U items per round (addresses
 // clamped and weights zeroed past the end, so the U loads are issued
@@ -208,18 +214,18 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int chunks = r >> 2, S = 256 / chunks;
   const int tid = threadIdx.x, sl = tid / chunks, c = tid % chunks;
   const float *ml = a.part_ml + static_cast<int64_t>(m) * 2;
-  const float *po = a.part_o + static_cast<int64_t>(m) * r + 4 * c;
+  const f16 *po = reinterpret_cast<const f16 *>(a.part_o) + static_cast<int64_t>(m) * r + 4 * c;
   const int64_t ml_stride = static_cast<int64_t>(M) * 2, po_stride = static_cast<int64_t>(M) * r;
   float mrun = -INFINITY, lrun = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (sl < S) {
     for (int k0 = ib + sl; k0 < ie; k0 += U * S) {
-      f32x4 v[U];
+      f16x4 v[U];
       float2 st[U];
 #pragma unroll
       for (int e = 0; e < U; ++e) {
         const int k = min(k0 + e * S, ie - 1);
-        v[e] = *reinterpret_cast<const f32x4 *>(po + k * po_stride);
+        v[e] = *reinterpret_cast<const f16x4 *>(po + k * po_stride);
         st[e] = *reinterpret_cast<const float2 *>(ml + k * ml_stride);
         if (k0 + e * S >= ie) st[e].x = -INFINITY;
       }
@@ -232,8 +238,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
         lrun *= sc;
 #pragma unroll
         for (int e = 0; e < U; ++e) {
+          // item e: weight 2^(m_e - max) on l_e and on O_e = l_e * (its O / l)
           const float wgt = st[e].x == -INFINITY ? 0.0f : exp2f(st[e].x - rm);
-          acc += wgt * v[e];
+          acc += (wgt * st[e].y) * __builtin_convertvector(v[e], f32x4);
           lrun += wgt * st[e].y;
         }
         mrun = rm;
@@ -338,6 +345,156 @@ __global__ __launch_bounds__(256) void upproj_valu_kernel(DecodeArgs a) {
   }
 }
 
+// Combine and up-projection in one launch for r = 512, d_v = 128 and at most
+// kFuseMaxRows query rows per head.  Block = (head h, tile of RT query rows),
+// 512 threads, blocks of one head on one XCD (they share W~_UV[h] in L2).
+//  1. Merge: thread (slice s, row j, 4-channel chunk c) folds items ib + s,
+//     ib + s + S, ... (S = 4 / RT slices) of row j into a running (max, sum,
+//     O), kCombU items per round with their loads issued together; the
+//     slices are merged in slice order and o_z[j] = O / l goes to LDS (and
+//     lse out).
+//  2. Product: wave wv owns output columns 16 wv .. 16 wv + 15 and lane l
+//     latent channels 8 l .. 8 l + 7; the lane's slice of W~_UV[h] (16 rows x
+//     8 channels, fp16) is loaded at kernel start, so it is in flight during
+//     the merge.  Each lane forms RT x 16 eight-term fp32 partial sums; a
+//     butterfly reduce-scatter over the 64 lanes adds them up (lane l ends
+//     with the output l >> (6 - log2(16 RT)) in full).
+constexpr int kFuseR = 512, kFuseDv = 128, kFuseThreads = 512, kFuseMaxRows = 16, kCombU = 16;
+
+// p[0 .. N) summed over the lanes that differ in bits log2(D) .. log2(D) - log2(N) + 1:
+// at each step a lane keeps one half (the upper one if its bit D is set), adds the
+// partner's copy of that half, and passes the other half on.
+template <int N, int D>
+__device__ __forceinline__ void lane_reduce_scatter(float *p, int lane) {
+  if constexpr (N > 1) {
+    const bool up = (lane & D) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float keep = up ? p[N / 2 + i] : p[i];
+      const float give = up ? p[i] : p[N / 2 + i];
+      p[i] = keep + __shfl_xor(give, D);
+    }
+    lane_reduce_scatter<N / 2, D / 2>(p, lane);
+  }
+}
+
+template <int RT>
+__global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs a, int n_rt, int n_logical) {
+  constexpr int S = 4 / RT, CH = kFuseR / 4;
+  constexpr int V = 16 * RT, LOGV = RT == 1 ? 4 : (RT == 2 ? 5 : 6);
+  static_assert(S * RT * CH == kFuseThreads, "one (slice, row, chunk) per thread");
+  __shared__ f32x4 s_o[S][RT][CH];
+  __shared__ float s_m[S][RT], s_l[S][RT];
+  __shared__ __align__(16) float s_z[RT][kFuseR];
+  const int per_xcd = (n_logical + 7) / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (logical >= n_logical) return;
+  const int h = logical / n_rt, rt = logical % n_rt;
+  const int H = a.d.num_heads, M = H * a.Tq, nrows = a.B * a.Tq;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+  f16x8 wr[16];
+  {
+    const uint16_t *wp = a.w_uv_f + (static_cast<int64_t>(h) * kFuseDv + 16 * wv) * kFuseR + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wr[i] = *reinterpret_cast<const f16x8 *>(wp + i * kFuseR);
+  }
+
+  // ---- 1. merge the partials ----
+  {
+    const int c = tid % CH, j = (tid / CH) % RT, sl = tid / (CH * RT);
+    const int q = rt * RT + j;
+    float mrun = -INFINITY, lrun = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (q < nrows) {
+      const int b = q / a.Tq, m = (q % a.Tq) * H + h;
+      const int ib = a.item_begin[b], ie = a.item_begin[b + 1];
+      const float *ml = a.part_ml + static_cast<int64_t>(m) * 2;
+      const f16 *po = reinterpret_cast<const f16 *>(a.part_o) + static_cast<int64_t>(m) * kFuseR + 4 * c;
+      const int64_t ml_stride = static_cast<int64_t>(M) * 2, po_stride = static_cast<int64_t>(M) * kFuseR;
+      for (int k0 = ib + sl; k0 < ie; k0 += kCombU * S) {
+        f16x4 v[kCombU];
+        float2 st[kCombU];
+#pragma unroll
+        for (int e = 0; e < kCombU; ++e) {
+          const int k = min(k0 + e * S, ie - 1);
+          v[e] = *reinterpret_cast<const f16x4 *>(po + k * po_stride);
+          st[e] = *reinterpret_cast<const float2 *>(ml + k * ml_stride);
+          if (k0 + e * S >= ie) st[e].x = -INFINITY;
+        }
+        float rm = mrun;
+#pragma unroll
+        for (int e = 0; e < kCombU; ++e) rm = fmaxf(rm, st[e].x);
+        if (rm != -INFINITY) {
+          const float sc = exp2f(mrun - rm);  // 0 while nothing was folded in
+          acc *= sc;
+          lrun *= sc;
+#pragma unroll
+          for (int e = 0; e < kCombU; ++e) {
+            const float wgt = st[e].x == -INFINITY ? 0.0f : exp2f(st[e].x - rm);
+            acc += (wgt * st[e].y) * __builtin_convertvector(v[e], f32x4);
+            lrun += wgt * st[e].y;
+          }
+          mrun = rm;
+        }
+      }
+    }
+    s_o[sl][j][c] = acc;
+    if (c == 0) {  // every chunk thread of (slice, row) holds the same (max, sum)
+      s_m[sl][j] = mrun;
+      s_l[sl][j] = lrun;
+    }
+  }
+  __syncthreads();
+  if (tid < RT * CH) {
+    const int j = tid / CH, c = tid % CH;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sl = 0; sl < S; ++sl) mx = fmaxf(mx, s_m[sl][j]);
+    float den = 0.0f;
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int sl = 0; sl < S; ++sl) {
+        const float mj = s_m[sl][j];
+        if (mj == -INFINITY) continue;
+        const float wgt = exp2f(mj - mx);
+        den += wgt * s_l[sl][j];
+        o += wgt * s_o[sl][j][c];
+      }
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    *reinterpret_cast<f32x4 *>(&s_z[j][4 * c]) = o * inv;
+    const int q = rt * RT + j;
+    if (c == 0 && q < nrows && a.lse != nullptr)
+      a.lse[static_cast<int64_t>(q) * H + h] = den > 0.0f ? (mx + log2f(den)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+
+  // ---- 2. out = W~_UV[h] o_z ----
+  float part[V];
+#pragma unroll
+  for (int j = 0; j < RT; ++j) {
+    const f32x4 z0 = *reinterpret_cast<const f32x4 *>(&s_z[j][8 * lane]);
+    const f32x4 z1 = *reinterpret_cast<const f32x4 *>(&s_z[j][8 * lane + 4]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float t = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t = fmaf(static_cast<float>(wr[i][e]), z0[e], t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t = fmaf(static_cast<float>(wr[i][4 + e]), z1[e], t);
+      part[16 * j + i] = t;
+    }
+  }
+  lane_reduce_scatter<V, 32>(part, lane);
+#pragma unroll
+  for (int d = 32 >> LOGV; d > 0; d >>= 1) part[0] += __shfl_xor(part[0], d);
+  const int idx = lane >> (6 - LOGV), j = idx >> 4, q = rt * RT + j;
+  if ((lane & ((1 << (6 - LOGV)) - 1)) == 0 && q < nrows)
+    a.out[(static_cast<int64_t>(q) * H + h) * kFuseDv + 16 * wv + (idx & 15)] = part[0];
+}
+
 }  // namespace
 
 hipError_t launch_plan(const DecodeArgs &a, hipStream_t s) {
@@ -374,7 +531,27 @@ hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+static bool combine_upproj_fused(const DecodeArgs &a) {
+  return a.d.kv_lora_rank == kFuseR && a.d.v_head_dim == kFuseDv && a.B * a.Tq <= kFuseMaxRows;
+}
+
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
+  if (combine_upproj_fused(a)) {
+    TimedLaunch tl("combine_up_proj", s);
+    // the widest row tile that still gives every compute unit a block
+    const int nrows = a.B * a.Tq, H = a.d.num_heads, ncu = device_cu_count();
+    int rt = 4;
+    while (rt > 1 && H * ((nrows + rt - 1) / rt) < ncu) rt >>= 1;
+    const int n_rt = (nrows + rt - 1) / rt, n_logical = H * n_rt;
+    const unsigned grid = static_cast<unsigned>((n_logical + 7) / 8) * 8;
+    if (rt == 4)
+      combine_upproj_kernel<4><<<grid, kFuseThreads, 0, s>>>(a, n_rt, n_logical);
+    else if (rt == 2)
+      combine_upproj_kernel<2><<<grid, kFuseThreads, 0, s>>>(a, n_rt, n_logical);
+    else
+      combine_upproj_kernel<1><<<grid, kFuseThreads, 0, s>>>(a, n_rt, n_logical);
+    return hipGetLastError();
+  }
   TimedLaunch tl("combine", s);
   const int rows = a.B * a.Tq * a.d.num_heads;
   // items per sequence average (target + B) / B; rounds of 16 pay off once
@@ -389,6 +566,7 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_upproj(const DecodeArgs &a, hipStream_t s) {
+  if (combine_upproj_fused(a)) return hipSuccess;  // done by launch_combine
   TimedLaunch tl("up_proj", s);
   if (a.d.v_head_dim % 32 == 0) {
     const int nrows = a.B * a.Tq;

@@ -142,6 +142,7 @@ struct __align__(16) Smem {
   float sp[4][2][64][16];  // [wave][mt][lane][16 scores, 16-byte quads swizzled]
   f16 p[ROWS * PRSTRIDE];
   float alpha[ROWS];
+  float inv_l[ROWS];  // 1 / l of each row, for the normalised partial
   int resc[4];
 };
 
@@ -437,10 +438,12 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
     read_scores(s_next);
   }
 
-  // ---- write the partial (O, m, l) of this work item ----
+  // ---- write the partial (O / l in fp16, m, l) of this work item ----
+  if (s_k8 == 0) sm.inv_l[s_row] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  lds_barrier();
   // Each 32x32 accumulator tile (rows 32 mt.., the 32 contiguous channels
   // 128 w + 32 nt..) goes through this wave's own Z buffers (no other wave
-  // touches them) so that every lane then stores 16 contiguous bytes of one
+  // touches them) so that every lane then stores 4 contiguous channels of one
   // row.  Staged position of (row, col): rows in pairs of 64 floats, the half
   // chosen by bit 0 xor bit 2 of the row, so the 4-row-apart halves a store
   // writes and the adjacent rows a 16-lane read takes fall in disjoint banks.
@@ -458,10 +461,11 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
       for (int j = 0; j < 4; ++j) {
         const int row = 8 * j + (l >> 3), q = l & 7;
         const f32x4 x = *reinterpret_cast<const f32x4 *>(st + stage_pos(row, 4 * q));
+        const f16x4 y = __builtin_convertvector(x * sm.inv_l[32 * mt + row], f16x4);
         const int m = rb * ROWS + 32 * mt + row;
         if (m < M)  // streamed out (read once, by the combine kernel)
           __builtin_nontemporal_store(
-              x, reinterpret_cast<f32x4 *>(a.part_o + (static_cast<int64_t>(item) * M + m) * R + 128 * w + 32 * nt + 4 * q));
+              y, reinterpret_cast<f16x4 *>(a.part_o + (static_cast<int64_t>(item) * M + m) * R + 128 * w + 32 * nt + 4 * q));
       }
     }
   if (s_k8 == 0 && s_m < M) {

@@ -50,7 +50,8 @@ struct DecodeArgs {
   int32_t *meta;        // [0] = n_items, [1] = chunk tokens
   void *qbuf;           // absorbed queries
   float *oz;            // combined latent output [B*M][r]
-  float *part_o;        // [max_items][M][r]
+  uint16_t *part_o;     // [max_items][M][r] fp16: the item's O / l (a convex
+                        // combination of fp16 entries, so in fp16 range)
   float *part_ml;       // [max_items][M][2]  (m in log2 units, l)
   int32_t max_items;
   int32_t target_items;
