@@ -309,6 +309,128 @@ mla_status mla_decode_sparse(const mla_dims *dims, const uint16_t *q_nope,
                              void *stream);
 
 /* ------------------------------------------------------------------------
+ * OSCAR for full-attention (grouped-query) layers
+ *
+ * [OSCAR issue #10, "MLA model support (GLM-5.1 / DeepSeek-style)",
+ * maintainer reply, part "How the rotation adapts to the latent", first
+ * point]: on full-attention models the method fits two rotations per layer,
+ * each per KV head: one for K from the query covariance and one for V from a
+ * score-weighted value covariance.  Each KV head's K and V rows are rotated
+ * and INT2 group-quantised by the latent quantiser (mla_append_quant's
+ * arithmetic and entry format, without side keys), and decode runs on the
+ * rotated entries: each query is rotated once (q R_k), the merged output
+ * un-rotated once (o_z R_v^T).  The page gives no formulas; the readings
+ * implemented:
+ *  - the calibration data is one sequence of n_cal tokens under causal
+ *    self-attention (query i sees keys 0..i) with the given softmax scale;
+ *  - K rotation of head h: eigenvectors, by ascending eigenvalue, of
+ *    (M + 1e-8 I)^(-1/2) Sigma_k (M + 1e-8 I)^(-1/2), where Sigma_k is the
+ *    uncentred covariance of the head's keys and M the uncentred covariance
+ *    of the queries that read it (its G query heads, all positions) scaled
+ *    to mean eigenvalue 1: a key error e costs the score error q . e, whose
+ *    mean square is e^T M e;
+ *  - V rotation of head h: eigenvectors, by ascending eigenvalue, of
+ *    sum_t w_t v_t v_t^T / sum_t w_t, with w_t the attention mass key t
+ *    receives (summed over the head's query heads and the positions i >= t);
+ *  - signs as mla_calibrate_rotation.
+ * Layout: query head g reads KV head g / G, G = num_q_heads / num_kv_heads.
+ * ---------------------------------------------------------------------- */
+typedef struct gqa_dims {
+  int32_t head_dim;     /* d: a multiple of group_size and of 8, 16..256 */
+  int32_t num_q_heads;  /* H_q, a multiple of num_kv_heads, <= 4096 */
+  int32_t num_kv_heads; /* H_kv >= 1 */
+  int32_t group_size;   /* INT2 group along d: 16 or 32 */
+} gqa_dims;
+
+/* K and V entries per KV head in the latent entry format (codes packed four
+ * per byte, channel 4i + e in bits 2e..2e+1 of byte i; fp16 scale then zero
+ * per group).  Entry (h, slot) is row h * capacity + slot of
+ *   k_codes [H_kv * capacity][d/4] u8,  k_scale_zero [H_kv * capacity][d/G][2] fp16,
+ *   v_codes, v_scale_zero likewise.  Device memory, caller-owned. */
+typedef struct gqa_cache {
+  uint8_t *k_codes;
+  uint16_t *k_scale_zero;
+  uint8_t *v_codes;
+  uint16_t *v_scale_zero;
+  int64_t capacity; /* slots per KV head */
+} gqa_cache;
+
+/* gqa_calibrate — both rotations of every KV head.
+ *   q_cal [H_q][n_cal][d], k_cal and v_cal [H_kv][n_cal][d]: device bf16,
+ *     n_cal in 1..65536 (the attention masses cost n_cal^2 d per query head),
+ *     head-major (one calibration sequence, position-ordered)
+ *   softmax_scale: the layer's score scale (for the attention weights)
+ *   R_k, R_v: device [H_kv][d][d] fp32, per head laid out as
+ *     mla_calibrate_rotation's R (column j = eigenvector j)
+ *   eig_k, eig_v: host [H_kv][d] fp64 eigenvalues, ascending (may be NULL)
+ * The covariances, attention masses (fp64, two passes over the causal
+ * scores, no atomics) and weighted covariance run on the GPU; the d x d
+ * eigensolves on the host.  Synchronous; allocates device scratch.
+ * Errors: INVALID_ARG (dims, n_cal < 1, NULL or unaligned pointers,
+ * non-finite scale), NUMERIC (non-finite statistics, no convergence), HIP. */
+mla_status gqa_calibrate(const gqa_dims *dims, const uint16_t *q_cal,
+                         const uint16_t *k_cal, const uint16_t *v_cal,
+                         int64_t n_cal, float softmax_scale, float *R_k,
+                         float *R_v, double *eig_k, double *eig_v,
+                         void *stream);
+
+/* gqa_prepare_rotation — R_apply_t[h] = bf16(R[h])^T for every KV head
+ * (mla_prepare_rotation per head).  R device [H_kv][d][d] fp32, R_apply_t
+ * device [H_kv][d][d] bf16.  Asynchronous. */
+mla_status gqa_prepare_rotation(const gqa_dims *dims, const float *R,
+                                uint16_t *R_apply_t, void *stream);
+
+/* gqa_fit_clip — per-head, per-group clip ratios (mla_fit_clip per head).
+ *   x_cal [H_kv][n_cal][d] device bf16 (the calibration keys, or values)
+ *   R_apply_t [H_kv][d][d] device bf16 (of the same side)
+ *   alpha_grid host [n_grid] fp32 in (0, 1], 1 <= n_grid <= 64
+ *   alpha_out [H_kv][d/G] device fp32
+ * Synchronous; allocates device scratch. */
+mla_status gqa_fit_clip(const gqa_dims *dims, const uint16_t *x_cal,
+                        int64_t n_cal, const uint16_t *R_apply_t,
+                        const float *alpha_grid, int32_t n_grid,
+                        float *alpha_out, void *stream);
+
+/* gqa_append_quant — rotate, clip and quantise n new tokens' K and V rows.
+ *   k, v [n][H_kv][d] device bf16 (the projection output layout)
+ *   slot_mapping [n] int64 device: slot of token i (outside [0, capacity):
+ *     skipped)
+ *   Rk_apply_t, Rv_apply_t [H_kv][d][d] bf16; alpha_k, alpha_v [H_kv][d/G]
+ * Codes and scale/zero are those mla_append_quant writes for the head's
+ * rows with the head's rotation and ratios.  Asynchronous. */
+mla_status gqa_append_quant(const gqa_dims *dims, const uint16_t *k,
+                            const uint16_t *v, const int64_t *slot_mapping,
+                            int64_t n, const uint16_t *Rk_apply_t,
+                            const uint16_t *Rv_apply_t, const float *alpha_k,
+                            const float *alpha_v, const gqa_cache *cache,
+                            void *stream);
+
+/* Bytes of workspace gqa_decode needs (0 for invalid arguments). */
+size_t gqa_decode_workspace_size(const gqa_dims *dims, int32_t batch,
+                                 int32_t tq);
+
+/* gqa_decode — grouped-query decode over the INT2 K/V cache.
+ *   q [B][tq][H_q][d] device bf16; the tq queries are the last tq positions
+ *     of each sequence (causal: query t sees tokens 0 .. L - tq + t)
+ *   seq_base [B] int64, seq_len [B] int32 (device): sequence b is slots
+ *     seq_base[b] .. seq_base[b] + seq_len[b] - 1 of every KV head
+ *   out [B][tq][H_q][d] fp32 = softmax(scale q . k_hat) v_hat with k_hat =
+ *     z_k R_k,apply^T, v_hat = z_v R_v,apply^T the dequantised entries
+ *     un-rotated; lse [B][tq][H_q] fp32 natural-log log-sum-exp (may be NULL)
+ * An empty sequence gives out = 0, lse = -inf.  Runs as: query rotation,
+ * split-K attention over each (sequence, KV head) on the vector ALU,
+ * log-sum-exp merge, un-rotation.  Asynchronous; no host synchronisation.
+ * Errors: INVALID_ARG (dims, batch < 0, tq outside 1..64, causal not 0/1,
+ * NULL or unaligned pointers), WORKSPACE, HIP. */
+mla_status gqa_decode(const gqa_dims *dims, const uint16_t *q,
+                      const gqa_cache *cache, const uint16_t *Rk_apply_t,
+                      const uint16_t *Rv_apply_t, const int64_t *seq_base,
+                      const int32_t *seq_len, int32_t batch, int32_t tq,
+                      int32_t causal, float softmax_scale, void *workspace,
+                      size_t workspace_bytes, float *out, float *lse,
+                      void *stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics
  * ---------------------------------------------------------------------- */
 
@@ -327,8 +449,9 @@ mla_status mla_set_decode_variant(int32_t variant);
  * every kernel the library enqueues while enabled.  Names: "append_quant",
  * "decode_plan", "absorb_q" (on the MFMA path this kernel also plans the
  * split-K work, and "decode_plan" is not launched), "splitk_decode",
- * "combine", "up_proj",
- * "fold_weights", "prepare_rotation", "covariance", "clip_fit".
+ * "combine", "up_proj", "combine_up_proj" (the two in one launch where
+ * the shape allows), "index_score", "index_select", "gqa_rotate_q",
+ * "gqa_unrotate", "fold_weights", "prepare_rotation", "covariance", "clip_fit".
  * mla_timing_query waits for the recorded events and returns the summed
  * milliseconds and launch count since the last reset.  Process-wide; not
  * for use while another thread launches. */

@@ -42,6 +42,16 @@ class mla_cache(ctypes.Structure):
                 ("capacity", ctypes.c_int64)]
 
 
+class gqa_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("head_dim", "num_q_heads", "num_kv_heads", "group_size")]
+
+
+class gqa_cache(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_scale_zero", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_scale_zero", ctypes.c_void_p),
+                ("capacity", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _SIGS = {
     "mla_calibrate_rotation": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, ctypes.c_int, ctypes.c_int64, _P, _P, _P]),
@@ -63,6 +73,16 @@ _SIGS = {
     "mla_decode_sparse": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, _P, _P, _P, ctypes.POINTER(mla_cache),
                                          _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                          _P, ctypes.c_size_t, _P, _P, _P]),
+    "gqa_calibrate": (ctypes.c_int, [ctypes.POINTER(gqa_dims), _P, _P, _P, ctypes.c_int64, ctypes.c_float,
+                                     _P, _P, _P, _P, _P]),
+    "gqa_prepare_rotation": (ctypes.c_int, [ctypes.POINTER(gqa_dims), _P, _P, _P]),
+    "gqa_fit_clip": (ctypes.c_int, [ctypes.POINTER(gqa_dims), _P, ctypes.c_int64, _P, _P, ctypes.c_int32, _P, _P]),
+    "gqa_append_quant": (ctypes.c_int, [ctypes.POINTER(gqa_dims), _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
+                                        ctypes.POINTER(gqa_cache), _P]),
+    "gqa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(gqa_dims), ctypes.c_int32, ctypes.c_int32]),
+    "gqa_decode": (ctypes.c_int, [ctypes.POINTER(gqa_dims), _P, ctypes.POINTER(gqa_cache), _P, _P, _P, _P,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P,
+                                  ctypes.c_size_t, _P, _P, _P]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_abi_version": (ctypes.c_int32, []),
@@ -97,7 +117,7 @@ def header_functions() -> list:
     with open(HEADER_PATH) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:mla|gqa)_[a-z0-9_]+)\s*\(", text)))
 
 
 def _check(st: int, where: str):
@@ -180,6 +200,39 @@ class Cache:
     def c(self) -> mla_cache:
         return mla_cache(self.codes.data_ptr(), self.scale_zero.data_ptr(), self.k_rope.data_ptr(),
                          self.idx_key.data_ptr() if self.idx_key is not None else 0, self.capacity)
+
+
+@dataclass(frozen=True)
+class GqaDims:
+    head_dim: int
+    num_q_heads: int
+    num_kv_heads: int
+    group_size: int
+
+    def c(self) -> gqa_dims:
+        return gqa_dims(self.head_dim, self.num_q_heads, self.num_kv_heads, self.group_size)
+
+    @property
+    def n_groups(self):
+        return self.head_dim // self.group_size
+
+
+class GqaCache:
+    """Device tensors of the INT2 K/V cache of a grouped-query layer:
+    [H_kv, capacity, ...] per side (entry (h, slot) is row h * capacity + slot)."""
+
+    def __init__(self, dims: GqaDims, capacity: int, device="cuda"):
+        d, g, h = dims.head_dim, dims.group_size, dims.num_kv_heads
+        self.dims = dims
+        self.capacity = int(capacity)
+        self.k_codes = torch.zeros((h, capacity, d // 4), dtype=torch.uint8, device=device)
+        self.k_scale_zero = torch.zeros((h, capacity, d // g, 2), dtype=torch.float16, device=device)
+        self.v_codes = torch.zeros((h, capacity, d // 4), dtype=torch.uint8, device=device)
+        self.v_scale_zero = torch.zeros((h, capacity, d // g, 2), dtype=torch.float16, device=device)
+
+    def c(self) -> gqa_cache:
+        return gqa_cache(self.k_codes.data_ptr(), self.k_scale_zero.data_ptr(), self.v_codes.data_ptr(),
+                         self.v_scale_zero.data_ptr(), self.capacity)
 
 
 # ---------------------------------------------------------------------------
@@ -405,3 +458,104 @@ def mla_status_string(status: int) -> str:
 
 def mla_abi_version() -> int:
     return int(lib().mla_abi_version())
+
+
+# ---------------------------------------------------------------------------
+# grouped-query (OSCAR full-attention) layers
+# ---------------------------------------------------------------------------
+
+def gqa_calibrate(dims: GqaDims, q_cal, k_cal, v_cal, softmax_scale: float):
+    """q_cal [H_q, n, d], k_cal/v_cal [H_kv, n, d] bf16 -> (R_k, R_v [H_kv, d, d] fp32 device,
+    eig_k, eig_v float64 numpy [H_kv, d])."""
+    d, hq, hkv = dims.head_dim, dims.num_q_heads, dims.num_kv_heads
+    n = q_cal.shape[1] if q_cal.dim() == 3 else -1
+    _need(q_cal, "q_cal", torch.bfloat16, (hq, n, d))
+    _need(k_cal, "k_cal", torch.bfloat16, (hkv, n, d))
+    _need(v_cal, "v_cal", torch.bfloat16, (hkv, n, d))
+    rk = torch.empty((hkv, d, d), dtype=torch.float32, device=q_cal.device)
+    rv = torch.empty_like(rk)
+    ek = np.empty((hkv, d), dtype=np.float64)
+    ev = np.empty((hkv, d), dtype=np.float64)
+    g = dims.c()
+    st = lib().gqa_calibrate(ctypes.byref(g), _ptr(q_cal), _ptr(k_cal), _ptr(v_cal), n, float(softmax_scale),
+                             _ptr(rk), _ptr(rv), ek.ctypes.data_as(ctypes.c_void_p),
+                             ev.ctypes.data_as(ctypes.c_void_p), _stream())
+    _check(st, "gqa_calibrate")
+    return rk, rv, ek, ev
+
+
+def gqa_prepare_rotation(dims: GqaDims, R: torch.Tensor) -> torch.Tensor:
+    """R [H_kv, d, d] fp32 -> R_apply_t [H_kv, d, d] bf16, R_apply_t[h, j, i] = bf16(R[h, i, j])."""
+    d, hkv = dims.head_dim, dims.num_kv_heads
+    _need(R, "R", torch.float32, (hkv, d, d))
+    out = torch.empty((hkv, d, d), dtype=torch.bfloat16, device=R.device)
+    g = dims.c()
+    _check(lib().gqa_prepare_rotation(ctypes.byref(g), _ptr(R), _ptr(out), _stream()), "gqa_prepare_rotation")
+    return out
+
+
+def gqa_fit_clip(dims: GqaDims, x_cal, R_apply_t, grid):
+    """x_cal [H_kv, n, d] bf16 (keys or values) -> alpha [H_kv, d/G] fp32 device."""
+    d, hkv = dims.head_dim, dims.num_kv_heads
+    n = x_cal.shape[1] if x_cal.dim() == 3 else -1
+    _need(x_cal, "x_cal", torch.bfloat16, (hkv, n, d))
+    _need(R_apply_t, "R_apply_t", torch.bfloat16, (hkv, d, d))
+    gr = np.ascontiguousarray(np.asarray(grid, dtype=np.float32))
+    alpha = torch.empty((hkv, dims.n_groups), dtype=torch.float32, device=x_cal.device)
+    g = dims.c()
+    st = lib().gqa_fit_clip(ctypes.byref(g), _ptr(x_cal), n, _ptr(R_apply_t), gr.ctypes.data_as(ctypes.c_void_p),
+                            len(gr), _ptr(alpha), _stream())
+    _check(st, "gqa_fit_clip")
+    return alpha
+
+
+def gqa_append_quant(dims: GqaDims, k, v, slot_mapping, rk_apply_t, rv_apply_t, alpha_k, alpha_v,
+                     cache: GqaCache) -> None:
+    """k, v [n, H_kv, d] bf16; slot_mapping [n] int64."""
+    d, hkv = dims.head_dim, dims.num_kv_heads
+    n = k.shape[0]
+    _need(k, "k", torch.bfloat16, (n, hkv, d))
+    _need(v, "v", torch.bfloat16, (n, hkv, d))
+    _need(slot_mapping, "slot_mapping", torch.int64, (n,))
+    for t, name in ((rk_apply_t, "rk_apply_t"), (rv_apply_t, "rv_apply_t")):
+        _need(t, name, torch.bfloat16, (hkv, d, d))
+    for t, name in ((alpha_k, "alpha_k"), (alpha_v, "alpha_v")):
+        _need(t, name, torch.float32, (hkv, dims.n_groups))
+    g, c = dims.c(), cache.c()
+    st = lib().gqa_append_quant(ctypes.byref(g), _ptr(k), _ptr(v), _ptr(slot_mapping), n, _ptr(rk_apply_t),
+                                _ptr(rv_apply_t), _ptr(alpha_k), _ptr(alpha_v), ctypes.byref(c), _stream())
+    _check(st, "gqa_append_quant")
+
+
+def gqa_decode_workspace_size(dims: GqaDims, batch: int, tq: int) -> int:
+    g = dims.c()
+    return int(lib().gqa_decode_workspace_size(ctypes.byref(g), int(batch), int(tq)))
+
+
+def gqa_decode(dims: GqaDims, q, cache: GqaCache, rk_apply_t, rv_apply_t, seq_base, seq_len, tq: int,
+               causal: bool, softmax_scale: float, workspace=None, out=None, lse=None):
+    """q [B, tq, H_q, d] bf16 -> (out [B, tq, H_q, d] fp32, lse [B, tq, H_q] fp32)."""
+    d, hq, hkv = dims.head_dim, dims.num_q_heads, dims.num_kv_heads
+    B = seq_len.shape[0]
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, tq, hq, d))
+    for t, name in ((rk_apply_t, "rk_apply_t"), (rv_apply_t, "rv_apply_t")):
+        _need(t, name, torch.bfloat16, (hkv, d, d))
+    _need(seq_base, "seq_base", torch.int64, (B,))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    need = gqa_decode_workspace_size(dims, B, tq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((B, tq, hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, tq, hq), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, tq, hq, d))
+    _need(lse, "lse", torch.float32, (B, tq, hq))
+    g, c = dims.c(), cache.c()
+    st = lib().gqa_decode(ctypes.byref(g), _ptr(q), ctypes.byref(c), _ptr(rk_apply_t), _ptr(rv_apply_t),
+                          _ptr(seq_base), _ptr(seq_len), B, tq, int(bool(causal)), float(softmax_scale),
+                          _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream())
+    _check(st, "gqa_decode")
+    return out, lse

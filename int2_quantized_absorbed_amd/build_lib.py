@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 
-SOURCES = ["api.hip", "append.hip", "calib.hip", "decode.hip", "decode_mfma.hip", "index.hip"]
+SOURCES = ["api.hip", "append.hip", "calib.hip", "decode.hip", "decode_mfma.hip", "gqa.hip", "index.hip"]
 HOST_SOURCES = ["eigh.cpp"]
 
 ARCH = "gfx950"

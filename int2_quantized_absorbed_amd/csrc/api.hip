@@ -190,6 +190,111 @@ WsLayout layout(const mla_dims &d, int B, int Tq) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// sw = (M + ridge I)^(-1/2) Sigma (M + ridge I)^(-1/2), symmetrised, with M
+// the metric scaled to trace r (mean eigenvalue 1): Sigma seen in the metric
+// in which errors count.  The ridge keeps directions the metric ignores
+// finite (they get the largest weighted variance and the coarsest groups).
+// False if the metric is zero or not finite, or its eigensolve fails.
+constexpr double kMetricRidge = 1e-8;
+
+bool metric_whitened(int r, std::vector<double> metric, const std::vector<double> &sigma,
+                     std::vector<double> &sw) {
+  const size_t rr = static_cast<size_t>(r) * r;
+  double tr = 0.0;
+  for (int i = 0; i < r; ++i) tr += metric[static_cast<size_t>(i) * r + i];
+  if (!(tr > 0.0) || !std::isfinite(tr)) return false;
+  for (size_t i = 0; i < rr; ++i) metric[i] *= static_cast<double>(r) / tr;
+  std::vector<double> gv(r), gvec(rr), gh(rr, 0.0), tmp(rr, 0.0);
+  if (!eigh_ascending(r, metric.data(), gv.data(), gvec.data())) return false;
+  // (M + ridge I)^(-1/2) = V diag(1 / sqrt(max(lambda, 0) + ridge)) V^T
+  for (int k = 0; k < r; ++k) {
+    const double sq = 1.0 / std::sqrt(std::max(gv[k], 0.0) + kMetricRidge);
+    for (int i = 0; i < r; ++i) {
+      const double vik = gvec[static_cast<size_t>(i) * r + k] * sq;
+      if (vik == 0.0) continue;
+      double *row = gh.data() + static_cast<size_t>(i) * r;
+      for (int j = 0; j < r; ++j) row[j] += vik * gvec[static_cast<size_t>(j) * r + k];
+    }
+  }
+  auto matmul = [r](const std::vector<double> &a, const std::vector<double> &b, std::vector<double> &c) {
+    std::fill(c.begin(), c.end(), 0.0);
+    for (int i = 0; i < r; ++i)
+      for (int k = 0; k < r; ++k) {
+        const double aik = a[static_cast<size_t>(i) * r + k];
+        if (aik == 0.0) continue;
+        const double *brow = b.data() + static_cast<size_t>(k) * r;
+        double *crow = c.data() + static_cast<size_t>(i) * r;
+        for (int j = 0; j < r; ++j) crow[j] += aik * brow[j];
+      }
+  };
+  sw.assign(rr, 0.0);
+  matmul(gh, sigma, tmp);
+  matmul(tmp, gh, sw);
+  for (int i = 0; i < r; ++i)
+    for (int j = i + 1; j < r; ++j) {
+      const double m = 0.5 * (sw[static_cast<size_t>(i) * r + j] + sw[static_cast<size_t>(j) * r + i]);
+      sw[static_cast<size_t>(i) * r + j] = m;
+      sw[static_cast<size_t>(j) * r + i] = m;
+    }
+  return true;
+}
+
+// ---- grouped-query layers ----
+bool gqa_dims_valid(const gqa_dims *g, std::string *why) {
+  if (g == nullptr) {
+    *why = "dims is NULL";
+    return false;
+  }
+  if (g->group_size != 16 && g->group_size != 32) {
+    *why = "group_size must be 16 or 32";
+    return false;
+  }
+  if (g->head_dim < 16 || g->head_dim > 256 || g->head_dim % g->group_size != 0 || g->head_dim % 8 != 0) {
+    *why = "head_dim must be in 16..256 and a multiple of group_size and of 8";
+    return false;
+  }
+  if (g->num_kv_heads < 1 || g->num_q_heads < g->num_kv_heads || g->num_q_heads > 4096 ||
+      g->num_q_heads % g->num_kv_heads != 0) {
+    *why = "num_q_heads must be a multiple of num_kv_heads >= 1 and at most 4096";
+    return false;
+  }
+  return true;
+}
+
+// A KV head's K or V rows as a latent of width d with no side keys, and the
+// G query heads of one KV head as the decode's heads.
+mla_dims gqa_latent_dims(const gqa_dims &g) {
+  mla_dims d{};
+  d.kv_lora_rank = g.head_dim;
+  d.qk_rope_head_dim = 0;
+  d.qk_nope_head_dim = g.head_dim;
+  d.v_head_dim = g.head_dim;
+  d.num_heads = g.num_q_heads / g.num_kv_heads;
+  d.group_size = g.group_size;
+  d.index_head_dim = 0;
+  return d;
+}
+
+struct GqaWs {
+  WsLayout split;  // the shared decode workspace of B * H_kv pseudo-sequences
+  size_t base2 = 0, len2 = 0, lse2 = 0, total = 0;
+};
+
+GqaWs gqa_layout(const gqa_dims &g, int B, int Tq) {
+  GqaWs w;
+  const int Bp = B * g.num_kv_heads, G = g.num_q_heads / g.num_kv_heads;
+  w.split = layout(gqa_latent_dims(g), Bp, Tq);
+  size_t off = w.split.total;
+  w.base2 = off;
+  off = align256(off + sizeof(int64_t) * Bp);
+  w.len2 = off;
+  off = align256(off + sizeof(int32_t) * Bp);
+  w.lse2 = off;
+  off = align256(off + sizeof(float) * static_cast<size_t>(Bp) * Tq * G);
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 }  // namespace mla
 
@@ -327,50 +432,13 @@ mla_status mla_calibrate_rotation_weighted(const mla_dims *dims, const void *c_c
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   (void)hipFree(d_all);
   if (e != hipSuccess) return hip_fail(e, "mla_calibrate_rotation_weighted: covariances");
-  // G = sum_h W_UK[h]^T W_UK[h] + W_UV[h]^T W_UV[h], scaled to trace r
-  std::vector<double> g(rr);
-  double tr = 0.0;
+  // G = sum_h W_UK[h]^T W_UK[h] + W_UV[h]^T W_UV[h] (scaled to trace r by
+  // metric_whitened); Sigma_w = G^(-1/2) Sigma G^(-1/2)
+  std::vector<double> g(rr), sw;
   for (size_t i = 0; i < rr; ++i) g[i] = guk[i] * static_cast<double>(n_uk) + guv[i] * static_cast<double>(n_uv);
-  for (int i = 0; i < r; ++i) tr += g[static_cast<size_t>(i) * r + i];
-  if (!(tr > 0.0) || !std::isfinite(tr))
-    return fail(MLA_ERR_NUMERIC, "mla_calibrate_rotation_weighted: up-projection weights are zero or not finite");
-  for (size_t i = 0; i < rr; ++i) g[i] *= static_cast<double>(r) / tr;
-  // (G + ridge I)^(-1/2) = V diag(1 / sqrt(max(lambda, 0) + ridge)) V^T; the
-  // ridge keeps latent directions the up-projection ignores finite (they get
-  // the largest weighted variance and the coarsest groups)
-  constexpr double kMetricRidge = 1e-8;  // G has mean eigenvalue 1
-  std::vector<double> gv(r), gvec(rr), gh(rr, 0.0), tmp(rr, 0.0), sw(rr, 0.0);
-  if (!eigh_ascending(r, g.data(), gv.data(), gvec.data()))
-    return fail(MLA_ERR_NUMERIC, "mla_calibrate_rotation_weighted: eigensolver did not converge on the metric");
-  for (int k = 0; k < r; ++k) {
-    const double sq = 1.0 / std::sqrt(std::max(gv[k], 0.0) + kMetricRidge);
-    for (int i = 0; i < r; ++i) {
-      const double vik = gvec[static_cast<size_t>(i) * r + k] * sq;
-      if (vik == 0.0) continue;
-      double *row = gh.data() + static_cast<size_t>(i) * r;
-      for (int j = 0; j < r; ++j) row[j] += vik * gvec[static_cast<size_t>(j) * r + k];
-    }
-  }
-  // Sigma_w = G^(-1/2) Sigma G^(-1/2), symmetrised
-  auto matmul = [r](const std::vector<double> &a, const std::vector<double> &b, std::vector<double> &c) {
-    std::fill(c.begin(), c.end(), 0.0);
-    for (int i = 0; i < r; ++i)
-      for (int k = 0; k < r; ++k) {
-        const double aik = a[static_cast<size_t>(i) * r + k];
-        if (aik == 0.0) continue;
-        const double *brow = b.data() + static_cast<size_t>(k) * r;
-        double *crow = c.data() + static_cast<size_t>(i) * r;
-        for (int j = 0; j < r; ++j) crow[j] += aik * brow[j];
-      }
-  };
-  matmul(gh, sig, tmp);
-  matmul(tmp, gh, sw);
-  for (int i = 0; i < r; ++i)
-    for (int j = i + 1; j < r; ++j) {
-      const double m = 0.5 * (sw[static_cast<size_t>(i) * r + j] + sw[static_cast<size_t>(j) * r + i]);
-      sw[static_cast<size_t>(i) * r + j] = m;
-      sw[static_cast<size_t>(j) * r + i] = m;
-    }
+  if (!metric_whitened(r, g, sig, sw))
+    return fail(MLA_ERR_NUMERIC,
+                "mla_calibrate_rotation_weighted: up-projection weights are zero or not finite, or their eigensolve failed");
   std::vector<double> vals(r), vecs(rr);
   if (!eigh_ascending(r, sw.data(), vals.data(), vecs.data()))
     return fail(MLA_ERR_NUMERIC, "mla_calibrate_rotation_weighted: non-finite covariance or eigensolver did not converge");
@@ -542,7 +610,7 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
   const WsLayout w = layout(*dims, batch, tq);
   if (workspace_bytes < w.total)
     return fail(MLA_ERR_WORKSPACE, F + "workspace needs " + std::to_string(w.total) + " bytes");
-  DecodeArgs a;
+  DecodeArgs a{};
   a.d = *dims;
   a.q_nope = q_nope;
   a.q_rope = q_rope;
@@ -690,6 +758,261 @@ mla_status mla_decode_sparse(const mla_dims *dims, const uint16_t *q_nope, const
     return fail(MLA_ERR_INVALID_ARG, "mla_decode_sparse: device pointers must be 16-byte aligned");
   return decode_impl("mla_decode_sparse", dims, q_nope, q_rope, w_uk_f, w_uv_f, cache, seq_base, n_sel, sel, top_k,
                      batch, 1, 0, softmax_scale, workspace, workspace_bytes, out, lse, stream);
+}
+
+
+// ---------------------------------------------------------------------------
+// OSCAR for full-attention (grouped-query) layers
+mla_status gqa_calibrate(const gqa_dims *dims, const uint16_t *q_cal, const uint16_t *k_cal, const uint16_t *v_cal,
+                         int64_t n_cal, float softmax_scale, float *R_k, float *R_v, double *eig_k, double *eig_v,
+                         void *stream) {
+  std::string why;
+  if (!gqa_dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "gqa_calibrate: " + why);
+  if (!q_cal || !k_cal || !v_cal || !R_k || !R_v) return fail(MLA_ERR_INVALID_ARG, "gqa_calibrate: NULL device pointer");
+  const void *ptrs[] = {q_cal, k_cal, v_cal};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(MLA_ERR_INVALID_ARG, "gqa_calibrate: device pointers must be 16-byte aligned");
+  if (n_cal < 1 || n_cal > 65536) return fail(MLA_ERR_INVALID_ARG, "gqa_calibrate: n_cal must be in 1..65536");
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "gqa_calibrate: softmax_scale not finite");
+  const int d = dims->head_dim, Hq = dims->num_q_heads, Hkv = dims->num_kv_heads, G = Hq / Hkv;
+  const int n = static_cast<int>(n_cal);
+  const size_t dd = static_cast<size_t>(d) * d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // device scratch: Sigma_q, Sigma_k, Sigma_v [H_kv][d][d], row stats [H_q][n] x 2, masses [H_kv][n]
+  const size_t n_dbl = 3 * Hkv * dd + 2 * static_cast<size_t>(Hq) * n + static_cast<size_t>(Hkv) * n;
+  double *buf = nullptr;
+  MLA_HIP_CHECK(hipMalloc(&buf, n_dbl * sizeof(double)), "gqa_calibrate: hipMalloc");
+  double *sig_q = buf, *sig_k = sig_q + Hkv * dd, *sig_v = sig_k + Hkv * dd;
+  double *row_m = sig_v + Hkv * dd, *row_inv = row_m + static_cast<size_t>(Hq) * n;
+  double *mass = row_inv + static_cast<size_t>(Hq) * n;
+  hipError_t e = hipSuccess;
+  for (int h = 0; h < Hkv && e == hipSuccess; ++h) {
+    // the G query heads of KV head h are contiguous rows: [G * n][d]
+    e = launch_covariance(q_cal + static_cast<size_t>(h) * G * n * d, MLA_DTYPE_BF16, static_cast<int64_t>(G) * n, d,
+                          sig_q + h * dd, s);
+    if (e == hipSuccess)
+      e = launch_covariance(k_cal + static_cast<size_t>(h) * n * d, MLA_DTYPE_BF16, n, d, sig_k + h * dd, s);
+  }
+  if (e == hipSuccess)
+    e = launch_gqa_calib_stats(q_cal, k_cal, v_cal, n, d, Hq, Hkv, static_cast<double>(softmax_scale), row_m,
+                               row_inv, mass, sig_v, s);
+  std::vector<double> hq(Hkv * dd), hk(Hkv * dd), hv(Hkv * dd);
+  if (e == hipSuccess) e = hipMemcpyAsync(hq.data(), sig_q, Hkv * dd * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(hk.data(), sig_k, Hkv * dd * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(hv.data(), sig_v, Hkv * dd * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(buf);
+  if (e != hipSuccess) return hip_fail(e, "gqa_calibrate: statistics");
+  std::vector<float> rk(Hkv * dd), rv(Hkv * dd);
+  std::vector<double> vals(d), vecs(dd), sw;
+  for (int h = 0; h < Hkv; ++h) {
+    std::vector<double> sq(hq.begin() + h * dd, hq.begin() + (h + 1) * dd);
+    std::vector<double> sk(hk.begin() + h * dd, hk.begin() + (h + 1) * dd);
+    if (!metric_whitened(d, sq, sk, sw))
+      return fail(MLA_ERR_NUMERIC, "gqa_calibrate: query covariance is zero or not finite, or its eigensolve failed");
+    if (!eigh_ascending(d, sw.data(), vals.data(), vecs.data()))
+      return fail(MLA_ERR_NUMERIC, "gqa_calibrate: key statistics not finite or eigensolver did not converge");
+    for (size_t i = 0; i < dd; ++i) rk[h * dd + i] = static_cast<float>(vecs[i]);
+    if (eig_k != nullptr) std::memcpy(eig_k + static_cast<size_t>(h) * d, vals.data(), sizeof(double) * d);
+    if (!eigh_ascending(d, hv.data() + h * dd, vals.data(), vecs.data()))
+      return fail(MLA_ERR_NUMERIC, "gqa_calibrate: value statistics not finite or eigensolver did not converge");
+    for (size_t i = 0; i < dd; ++i) rv[h * dd + i] = static_cast<float>(vecs[i]);
+    if (eig_v != nullptr) std::memcpy(eig_v + static_cast<size_t>(h) * d, vals.data(), sizeof(double) * d);
+  }
+  MLA_HIP_CHECK(hipMemcpyAsync(R_k, rk.data(), rk.size() * sizeof(float), hipMemcpyHostToDevice, s),
+                "gqa_calibrate: copy R_k");
+  MLA_HIP_CHECK(hipMemcpyAsync(R_v, rv.data(), rv.size() * sizeof(float), hipMemcpyHostToDevice, s),
+                "gqa_calibrate: copy R_v");
+  MLA_HIP_CHECK(hipStreamSynchronize(s), "gqa_calibrate: synchronize");
+  clear_error();
+  return MLA_OK;
+}
+
+mla_status gqa_prepare_rotation(const gqa_dims *dims, const float *R, uint16_t *R_apply_t, void *stream) {
+  std::string why;
+  if (!gqa_dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "gqa_prepare_rotation: " + why);
+  if (R == nullptr || R_apply_t == nullptr) return fail(MLA_ERR_INVALID_ARG, "gqa_prepare_rotation: NULL device pointer");
+  const int d = dims->head_dim;
+  const size_t dd = static_cast<size_t>(d) * d;
+  hipError_t e = hipSuccess;
+  for (int h = 0; h < dims->num_kv_heads && e == hipSuccess; ++h)
+    e = launch_prepare_rotation(R + h * dd, d, R_apply_t + h * dd, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gqa_prepare_rotation");
+  clear_error();
+  return MLA_OK;
+}
+
+mla_status gqa_fit_clip(const gqa_dims *dims, const uint16_t *x_cal, int64_t n_cal, const uint16_t *R_apply_t,
+                        const float *alpha_grid, int32_t n_grid, float *alpha_out, void *stream) {
+  std::string why;
+  if (!gqa_dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "gqa_fit_clip: " + why);
+  if (!x_cal || !R_apply_t || !alpha_grid || !alpha_out) return fail(MLA_ERR_INVALID_ARG, "gqa_fit_clip: NULL pointer");
+  if (!aligned16(x_cal) || !aligned16(R_apply_t))
+    return fail(MLA_ERR_INVALID_ARG, "gqa_fit_clip: device pointers must be 16-byte aligned");
+  if (n_cal < 1) return fail(MLA_ERR_INVALID_ARG, "gqa_fit_clip: n_cal must be >= 1");
+  if (n_grid < 1 || n_grid > 64) return fail(MLA_ERR_INVALID_ARG, "gqa_fit_clip: n_grid must be in 1..64");
+  for (int i = 0; i < n_grid; ++i)
+    if (!(alpha_grid[i] > 0.0f && alpha_grid[i] <= 1.0f))
+      return fail(MLA_ERR_INVALID_ARG, "gqa_fit_clip: grid values must lie in (0, 1]");
+  const mla_dims dl = gqa_latent_dims(*dims);
+  const int d = dims->head_dim, G = dims->group_size, ng = d / G;
+  const size_t dd = static_cast<size_t>(d) * d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *z = nullptr, *grid_d = nullptr;
+  double *sse_d = nullptr;
+  MLA_HIP_CHECK(hipMalloc(&z, static_cast<size_t>(n_cal) * d * sizeof(float)), "gqa_fit_clip: hipMalloc");
+  hipError_t e = hipMalloc(&grid_d, sizeof(float) * n_grid);
+  if (e == hipSuccess) e = hipMalloc(&sse_d, sizeof(double) * ng * n_grid);
+  if (e == hipSuccess) e = hipMemcpyAsync(grid_d, alpha_grid, sizeof(float) * n_grid, hipMemcpyHostToDevice, s);
+  mla_cache none{};
+  for (int h = 0; h < dims->num_kv_heads && e == hipSuccess; ++h) {
+    // rotated rows of head h (the append arithmetic), then the per-group search
+    e = launch_append(dl, x_cal + static_cast<size_t>(h) * n_cal * d, MLA_DTYPE_BF16, nullptr, nullptr, nullptr,
+                      n_cal, R_apply_t + h * dd, nullptr, none, z, s);
+    if (e == hipSuccess) e = launch_group_sse(z, n_cal, d, G, grid_d, n_grid, sse_d, alpha_out + h * ng, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(z);
+  if (grid_d) (void)hipFree(grid_d);
+  if (sse_d) (void)hipFree(sse_d);
+  if (e != hipSuccess) return hip_fail(e, "gqa_fit_clip");
+  clear_error();
+  return MLA_OK;
+}
+
+mla_status gqa_append_quant(const gqa_dims *dims, const uint16_t *k, const uint16_t *v, const int64_t *slot_mapping,
+                            int64_t n, const uint16_t *Rk_apply_t, const uint16_t *Rv_apply_t, const float *alpha_k,
+                            const float *alpha_v, const gqa_cache *cache, void *stream) {
+  std::string why;
+  if (!gqa_dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "gqa_append_quant: " + why);
+  if (n < 0) return fail(MLA_ERR_INVALID_ARG, "gqa_append_quant: n must be >= 0");
+  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, "gqa_append_quant: cache is NULL");
+  if (n == 0) {
+    clear_error();
+    return MLA_OK;
+  }
+  if (!k || !v || !slot_mapping || !Rk_apply_t || !Rv_apply_t || !alpha_k || !alpha_v || !cache->k_codes ||
+      !cache->k_scale_zero || !cache->v_codes || !cache->v_scale_zero)
+    return fail(MLA_ERR_INVALID_ARG, "gqa_append_quant: NULL device pointer");
+  const void *ptrs[] = {k, v, Rk_apply_t, Rv_apply_t, cache->k_codes, cache->k_scale_zero, cache->v_codes,
+                        cache->v_scale_zero};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(MLA_ERR_INVALID_ARG, "gqa_append_quant: device pointers must be 16-byte aligned");
+  if (cache->capacity < 0) return fail(MLA_ERR_INVALID_ARG, "gqa_append_quant: capacity must be >= 0");
+  const mla_dims dl = gqa_latent_dims(*dims);
+  const int d = dims->head_dim, ng = d / dims->group_size, Hkv = dims->num_kv_heads;
+  const size_t dd = static_cast<size_t>(d) * d;
+  const int64_t cap = cache->capacity;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  for (int h = 0; h < Hkv && e == hipSuccess; ++h) {
+    for (int side = 0; side < 2 && e == hipSuccess; ++side) {
+      mla_cache c{};
+      c.codes = (side ? cache->v_codes : cache->k_codes) + static_cast<size_t>(h) * cap * (d / 4);
+      c.scale_zero = (side ? cache->v_scale_zero : cache->k_scale_zero) + static_cast<size_t>(h) * cap * ng * 2;
+      c.capacity = cap;
+      e = launch_append(dl, (side ? v : k) + static_cast<size_t>(h) * d, MLA_DTYPE_BF16, nullptr, nullptr,
+                        slot_mapping, n, (side ? Rv_apply_t : Rk_apply_t) + h * dd,
+                        (side ? alpha_v : alpha_k) + h * ng, c, nullptr, s, static_cast<int64_t>(Hkv) * d);
+    }
+  }
+  if (e != hipSuccess) return hip_fail(e, "gqa_append_quant");
+  clear_error();
+  return MLA_OK;
+}
+
+size_t gqa_decode_workspace_size(const gqa_dims *dims, int32_t batch, int32_t tq) {
+  std::string why;
+  if (!gqa_dims_valid(dims, &why) || batch < 0 || tq < 1 || tq > 64) return 0;
+  return gqa_layout(*dims, batch, tq).total;
+}
+
+mla_status gqa_decode(const gqa_dims *dims, const uint16_t *q, const gqa_cache *cache, const uint16_t *Rk_apply_t,
+                      const uint16_t *Rv_apply_t, const int64_t *seq_base, const int32_t *seq_len, int32_t batch,
+                      int32_t tq, int32_t causal, float softmax_scale, void *workspace, size_t workspace_bytes,
+                      float *out, float *lse, void *stream) {
+  std::string why;
+  if (!gqa_dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "gqa_decode: " + why);
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "gqa_decode: batch must be >= 0");
+  if (tq < 1 || tq > 64) return fail(MLA_ERR_INVALID_ARG, "gqa_decode: tq must be in 1..64");
+  if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "gqa_decode: causal must be 0 or 1");
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "gqa_decode: softmax_scale not finite");
+  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, "gqa_decode: cache is NULL");
+  if (batch == 0) {
+    clear_error();
+    return MLA_OK;
+  }
+  if (!q || !Rk_apply_t || !Rv_apply_t || !seq_base || !seq_len || !workspace || !out || !cache->k_codes ||
+      !cache->k_scale_zero || !cache->v_codes || !cache->v_scale_zero)
+    return fail(MLA_ERR_INVALID_ARG, "gqa_decode: NULL device pointer");
+  const void *ptrs[] = {q, Rk_apply_t, Rv_apply_t, seq_base, seq_len, workspace, out, lse,
+                        cache->k_codes, cache->k_scale_zero, cache->v_codes, cache->v_scale_zero};
+  for (const void *p : ptrs)
+    if (p != nullptr && !aligned16(p))
+      return fail(MLA_ERR_INVALID_ARG, "gqa_decode: device pointers must be 16-byte aligned");
+  const GqaWs w = gqa_layout(*dims, batch, tq);
+  if (workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE, "gqa_decode: workspace needs " + std::to_string(w.total) + " bytes");
+  const int Hkv = dims->num_kv_heads, G = dims->num_q_heads / Hkv;
+  const int Bp = batch * Hkv, M = G * tq;
+  char *ws = static_cast<char *>(workspace);
+  // the shared split-K stages over B * H_kv pseudo-sequences (sequence, KV
+  // head) of G query heads each, K and V from their own caches
+  DecodeArgs a{};
+  a.d = gqa_latent_dims(*dims);
+  a.cache.codes = cache->k_codes;
+  a.cache.scale_zero = cache->k_scale_zero;
+  a.cache.capacity = static_cast<int64_t>(Hkv) * cache->capacity;
+  a.vcache.codes = cache->v_codes;
+  a.vcache.scale_zero = cache->v_scale_zero;
+  a.vcache.capacity = a.cache.capacity;
+  a.seq_base = reinterpret_cast<int64_t *>(ws + w.base2);
+  a.seq_len = reinterpret_cast<int32_t *>(ws + w.len2);
+  a.B = Bp;
+  a.Tq = tq;
+  a.causal = causal;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.lse = reinterpret_cast<float *>(ws + w.lse2);
+  a.items = reinterpret_cast<WorkItem *>(ws + w.split.items);
+  a.item_begin = reinterpret_cast<int32_t *>(ws + w.split.item_begin);
+  a.meta = reinterpret_cast<int32_t *>(ws + w.split.meta);
+  a.qbuf = ws + w.split.qbuf;
+  a.oz = reinterpret_cast<float *>(ws + w.split.oz);
+  a.part_o = reinterpret_cast<uint16_t *>(ws + w.split.part_o);
+  a.part_ml = reinterpret_cast<float *>(ws + w.split.part_ml);
+  a.max_items = w.split.max_items;
+  a.target_items = target_items(M, false);
+  a.tile = 16;
+  a.min_chunk_tiles = min_chunk_tiles(a.tile);
+  GqaDecodeArgs g{};
+  g.q = q;
+  g.rk_t = Rk_apply_t;
+  g.rv_t = Rv_apply_t;
+  g.seq_base = seq_base;
+  g.seq_len = seq_len;
+  g.capacity = cache->capacity;
+  g.B = batch;
+  g.Tq = tq;
+  g.H_q = dims->num_q_heads;
+  g.H_kv = Hkv;
+  g.d = dims->head_dim;
+  g.scale_log2 = a.scale_log2;
+  g.qbuf = static_cast<float *>(a.qbuf);
+  g.base2 = const_cast<int64_t *>(a.seq_base);
+  g.len2 = const_cast<int32_t *>(a.seq_len);
+  g.oz = a.oz;
+  g.lse2 = a.lse;
+  g.out = out;
+  g.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_gqa_rotate_q(g, s);
+  if (e == hipSuccess) e = launch_plan(a, s);
+  if (e == hipSuccess) e = launch_splitk_valu(a, s);
+  if (e == hipSuccess) e = launch_combine(a, s);
+  if (e == hipSuccess) e = launch_gqa_unrotate(g, s);
+  if (e != hipSuccess) return hip_fail(e, "gqa_decode");
+  clear_error();
+  return MLA_OK;
 }
 
 }  // extern "C"

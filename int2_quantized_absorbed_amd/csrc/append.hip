@@ -99,6 +99,7 @@ struct AppendParams {
   const float *alpha;
   mla_cache cache;
   float *z_out;
+  int64_t lat_stride;  // elements from one token's latent row to the next
   int r, G, d_r, d_idx;
 };
 
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(1024) void append_valu_kernel(AppendParams p) {
     slot = p.slots[tok];
     if (slot < 0 || slot >= p.cache.capacity) return;  // uniform per block
   }
-  for (int i = j; i < r; i += blockDim.x) cs[i] = latent_f64<T>(lat, tok * r + i);
+  for (int i = j; i < r; i += blockDim.x) cs[i] = latent_f64<T>(lat, tok * p.lat_stride + i);
   __syncthreads();
   const uint16_t *row = p.Rt + static_cast<int64_t>(j) * r;
   double acc = 0.0;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void append_mfma_kernel(AppendParams p, i
   const int64_t wave_tok0 = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave;
   const int64_t tok = wave_tok0 + l32;
   const bool valid = tok < p.n;
-  const bf16x8 *brow = reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(p.latent) + (valid ? tok : 0) * R);
+  const bf16x8 *brow = reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(p.latent) + (valid ? tok : 0) * p.lat_stride);
   // epilogue inputs, fetched now so their latency hides under the GEMM
   constexpr int NGT = 32 / G;  // groups per M-tile: 1 (G=32) or 2 (G=16)
   int64_t slot = -1;
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(64) void append_skinny_kernel(AppendParams p) {
   const bool valid = tok < p.n;
   const bf16x8 *arow = reinterpret_cast<const bf16x8 *>(p.Rt + static_cast<int64_t>(32 * ct + l32) * R);
   const bf16x8 *brow =
-      reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(p.latent) + (valid ? tok : 0) * R);
+      reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(p.latent) + (valid ? tok : 0) * p.lat_stride);
   int64_t slot = -1;
   float alpha[NGT] = {};
   if (p.z_out == nullptr) {
@@ -459,7 +460,8 @@ bool append_uses_mfma(const mla_dims &d, mla_dtype dt) {
 
 hipError_t launch_append(const mla_dims &d, const void *latent, mla_dtype dt, const uint16_t *k_rope,
                          const uint16_t *idx_key, const int64_t *slots, int64_t n, const uint16_t *Rt,
-                         const float *alpha, const mla_cache &cache, float *z_out, hipStream_t s) {
+                         const float *alpha, const mla_cache &cache, float *z_out, hipStream_t s,
+                         int64_t lat_stride) {
   if (n <= 0) return hipSuccess;
   TimedLaunch tl("append_quant", s);
   AppendParams p;
@@ -472,6 +474,7 @@ hipError_t launch_append(const mla_dims &d, const void *latent, mla_dtype dt, co
   p.alpha = alpha;
   p.cache = cache;
   p.z_out = z_out;
+  p.lat_stride = lat_stride > 0 ? lat_stride : d.kv_lora_rank;
   p.r = d.kv_lora_rank;
   p.G = d.group_size;
   p.d_r = d.qk_rope_head_dim;

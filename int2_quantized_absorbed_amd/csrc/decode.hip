@@ -85,6 +85,8 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
   float *z_s = q_s + ROWS * KP;        // [TT][KP]
   float *p_s = z_s + TT * KP;          // [ROWS][TT]
   float *al_s = p_s + ROWS * TT;       // [ROWS]
+  const bool has_v = a.vcache.codes != nullptr;
+  float *v_s = has_v ? al_s + ROWS : z_s;  // [TT][KP] values (their own cache, or the latent)
   const int tid = threadIdx.x;
   const int row0 = rb * ROWS;
   const int L = a.seq_len[it.b];
@@ -111,24 +113,30 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
 #pragma unroll
   for (int i = 0; i < NA; ++i) acc[i] = 0.0f;
   const int na = ROWS * r / 256;
-  const uint32_t *sz32 = reinterpret_cast<const uint32_t *>(a.cache.scale_zero);
+  // dequantised entry (fp32) of channel j of cache slot `slot`
+  auto dequant = [&](const mla_cache &c, int64_t slot, int j) -> float {
+    const uint32_t byte = c.codes[slot * (r / 4) + j / 4];
+    const uint32_t code = (byte >> (2 * (j & 3))) & 3u;
+    const uint32_t sz = reinterpret_cast<const uint32_t *>(c.scale_zero)[slot * (r / G) + j / G];
+    const float sc = static_cast<float>(bits_f16(static_cast<uint16_t>(sz & 0xffffu)));
+    const float zr = static_cast<float>(bits_f16(static_cast<uint16_t>(sz >> 16)));
+    return fmaf(sc, static_cast<float>(code), zr);
+  };
   for (int t0 = it.t0; t0 < it.t1; t0 += TT) {
     __syncthreads();
-    // dequantise the tile into LDS (fp32), rope key appended
+    // dequantise the tile into LDS (fp32), rope key appended; values too
+    // when they have their own cache
     for (int e = tid; e < TT * r; e += 256) {
       const int tk = e / r, j = e % r;
       const int tau = t0 + tk;
-      float v = 0.0f;
+      float v = 0.0f, vv = 0.0f;
       if (tau < it.t1) {
         const int64_t slot = slot_of(tau);
-        const uint32_t byte = a.cache.codes[slot * (r / 4) + j / 4];
-        const uint32_t code = (byte >> (2 * (j & 3))) & 3u;
-        const uint32_t sz = sz32[slot * (r / G) + j / G];
-        const float sc = static_cast<float>(bits_f16(static_cast<uint16_t>(sz & 0xffffu)));
-        const float zr = static_cast<float>(bits_f16(static_cast<uint16_t>(sz >> 16)));
-        v = fmaf(sc, static_cast<float>(code), zr);
+        v = dequant(a.cache, slot, j);
+        if (has_v) vv = dequant(a.vcache, slot, j);
       }
       z_s[tk * KP + j] = v;
+      if (has_v) v_s[tk * KP + j] = vv;
     }
     for (int e = tid; e < TT * dr; e += 256) {
       const int tk = e / dr, k = e % dr;
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
         const int e = tid + 256 * i;
         const int row = e / r, j = e % r;
         float o = acc[i] * al_s[row];
-        for (int tk = 0; tk < TT; ++tk) o = fmaf(p_s[row * TT + tk], z_s[tk * KP + j], o);
+        for (int tk = 0; tk < TT; ++tk) o = fmaf(p_s[row * TT + tk], v_s[tk * KP + j], o);
         acc[i] = o;
       }
     }
@@ -511,18 +519,24 @@ hipError_t launch_absorb_f32(const DecodeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int valu_tile(const mla_dims &d) {
-  const int K = d.kv_lora_rank + d.qk_rope_head_dim;
-  return ((16 + 16) * (K + 1) + 16 * 16 + 16) * 4 <= 64 * 1024 ? 16 : 8;
+// LDS floats of splitk_valu_kernel at tile TT: queries, latent tile, P,
+// alpha, and a value tile when values have their own cache
+size_t valu_lds_floats(const mla_dims &d, int TT, bool has_v) {
+  const int KP = d.kv_lora_rank + d.qk_rope_head_dim + 1;
+  return static_cast<size_t>(16 + TT + (has_v ? TT : 0)) * KP + 16 * TT + 16;
+}
+
+int valu_tile(const mla_dims &d, bool has_v) {
+  return valu_lds_floats(d, 16, has_v) * 4 <= 64 * 1024 ? 16 : 8;
 }
 
 hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s) {
   TimedLaunch tl("splitk_decode", s);
   const int M = a.d.num_heads * a.Tq;
   const int row_blocks = (M + 15) / 16;
-  const int K = a.d.kv_lora_rank + a.d.qk_rope_head_dim;
-  const int TT = valu_tile(a.d);
-  const size_t lds = static_cast<size_t>((16 + TT) * (K + 1) + 16 * TT + 16) * sizeof(float);
+  const bool has_v = a.vcache.codes != nullptr;
+  const int TT = valu_tile(a.d, has_v);
+  const size_t lds = valu_lds_floats(a.d, TT, has_v) * sizeof(float);
   const unsigned grid = static_cast<unsigned>(a.max_items) * row_blocks;
   if (TT == 16)
     splitk_valu_kernel<16><<<grid, 256, lds, s>>>(a, row_blocks);

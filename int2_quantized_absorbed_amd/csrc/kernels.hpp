@@ -32,7 +32,8 @@ hipError_t launch_append(const mla_dims &d, const void *latent, mla_dtype dt,
                          const uint16_t *k_rope, const uint16_t *idx_key,
                          const int64_t *slots, int64_t n, const uint16_t *Rt,
                          const float *alpha, const mla_cache &cache,
-                         float *z_out, hipStream_t s);
+                         float *z_out, hipStream_t s, int64_t lat_stride = 0);
+// lat_stride: elements between consecutive tokens' latent rows (0: r)
 
 // ---- decode (decode.hip, decode_mfma.hip) ----
 struct DecodeArgs {
@@ -62,6 +63,9 @@ struct DecodeArgs {
   // decode: sel == nullptr and token t is slot seq_base[b] + t
   const int32_t *sel;
   int32_t sel_stride;
+  // grouped-query layers (vector-ALU kernel only): values come from their own
+  // INT2 cache, same slots; codes == nullptr: values are the latent itself
+  mla_cache vcache;
 };
 
 hipError_t launch_plan(const DecodeArgs &a, hipStream_t s);
@@ -92,6 +96,31 @@ hipError_t launch_absorb_f32(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_splitk_valu(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_upproj(const DecodeArgs &a, hipStream_t s);
+
+// ---- grouped-query (OSCAR full-attention) layers (gqa.hip) ----
+// Calibration statistics: causal row statistics, the attention mass w
+// [H_kv][n] of every calibration key and the score-weighted value covariance
+// sigma_v [H_kv][d][d] (scratch row_m, row_inv [H_q][n]).
+hipError_t launch_gqa_calib_stats(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n, int d, int H_q,
+                                  int H_kv, double scale, double *row_m, double *row_inv, double *w,
+                                  double *sigma_v, hipStream_t s);
+struct GqaDecodeArgs {
+  const uint16_t *q;               // [B][Tq][H_q][d] bf16
+  const uint16_t *rk_t, *rv_t;     // [H_kv][d][d] bf16, R_apply^T per KV head
+  const int64_t *seq_base;
+  const int32_t *seq_len;
+  int64_t capacity;                // slots per KV head
+  int32_t B, Tq, H_q, H_kv, d;
+  float scale_log2;                // softmax_scale * log2(e)
+  float *qbuf;                     // [B * H_kv][Tq * G][d] rotated queries
+  int64_t *base2;                  // [B * H_kv] pseudo-sequence slot bases
+  int32_t *len2;                   // [B * H_kv] pseudo-sequence lengths
+  const float *oz;                 // [B * H_kv * Tq * G][d] merged output (rotated basis)
+  const float *lse2;               // [B * H_kv * Tq * G]
+  float *out, *lse;                // [B][Tq][H_q][d], [B][Tq][H_q]
+};
+hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, hipStream_t s);
+hipError_t launch_gqa_unrotate(const GqaDecodeArgs &a, hipStream_t s);
 
 // MFMA split-K path (r = 512, d_r = 64): supported() says whether it applies.
 bool mfma_decode_supported(const mla_dims &d, int rows);

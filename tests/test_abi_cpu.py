@@ -171,3 +171,71 @@ def test_workspace_size_is_monotone():
     s3 = M.mla_decode_workspace_size(DS, 8, 8)
     assert 0 < s1 < s2 and s1 < s3
     assert M.mla_decode_workspace_size(DS, 8, 0) == 0
+
+
+def _gdims(**kw):
+    a = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, group_size=32)
+    a.update(kw)
+    return Bd.gqa_dims(a["head_dim"], a["num_q_heads"], a["num_kv_heads"], a["group_size"])
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=100), dict(head_dim=512), dict(group_size=8),
+                                 dict(num_q_heads=30), dict(num_kv_heads=0), dict(num_q_heads=4, num_kv_heads=8)])
+def test_gqa_dims_rejected(bad):
+    lib = M.lib()
+    d = _gdims(**bad)
+    P = ctypes.c_void_p(256)
+    assert lib.gqa_decode_workspace_size(ctypes.byref(d), 2, 1) == 0
+    assert lib.gqa_prepare_rotation(ctypes.byref(d), P, P, None) == Bd.MLA_ERR_INVALID_ARG
+    assert "gqa_prepare_rotation" in M.mla_last_error()
+
+
+def test_gqa_workspace_grows_with_batch():
+    lib = M.lib()
+    d = _gdims()
+    w1 = lib.gqa_decode_workspace_size(ctypes.byref(d), 1, 1)
+    w8 = lib.gqa_decode_workspace_size(ctypes.byref(d), 8, 1)
+    assert 0 < w1 < w8 and w8 % 256 == 0
+    assert lib.gqa_decode_workspace_size(ctypes.byref(d), 8, 0) == 0
+
+
+def test_gqa_decode_argument_checks():
+    lib = M.lib()
+    d = _gdims()
+    P = ctypes.c_void_p(256)
+    cache = Bd.gqa_cache(256, 256, 256, 256, 1000)
+    call = lambda **kw: lib.gqa_decode(
+        ctypes.byref(d), kw.get("q", P), ctypes.byref(kw.get("cache", cache)), P, P, P, P, kw.get("B", 2),
+        kw.get("tq", 1), kw.get("causal", 1), kw.get("scale", 0.09), P, kw.get("wsb", 1 << 40), P, P, None)
+    assert call(tq=0) == Bd.MLA_ERR_INVALID_ARG
+    assert call(causal=2) == Bd.MLA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == Bd.MLA_ERR_INVALID_ARG
+    assert call(B=-1) == Bd.MLA_ERR_INVALID_ARG
+    assert call(q=ctypes.c_void_p(0)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(q=ctypes.c_void_p(264)) == Bd.MLA_ERR_INVALID_ARG         # misaligned
+    assert call(cache=Bd.gqa_cache(256, 0, 256, 256, 1000)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(wsb=16) == Bd.MLA_ERR_WORKSPACE
+    assert "gqa_decode" in M.mla_last_error()
+    assert call(B=0) == Bd.MLA_OK
+
+
+def test_gqa_append_and_calibrate_argument_checks():
+    lib = M.lib()
+    d = _gdims()
+    P = ctypes.c_void_p(256)
+    cache = Bd.gqa_cache(256, 256, 256, 256, 1000)
+    app = lambda **kw: lib.gqa_append_quant(ctypes.byref(d), kw.get("k", P), P, P, kw.get("n", 8), P, P, P, P,
+                                            ctypes.byref(cache), None)
+    assert app(n=0) == Bd.MLA_OK
+    assert app(n=-1) == Bd.MLA_ERR_INVALID_ARG
+    assert app(k=ctypes.c_void_p(0)) == Bd.MLA_ERR_INVALID_ARG
+    assert app(k=ctypes.c_void_p(258)) == Bd.MLA_ERR_INVALID_ARG
+    cal = lambda **kw: lib.gqa_calibrate(ctypes.byref(d), P, P, P, kw.get("n", 64), kw.get("scale", 0.09), P, P,
+                                         None, None, None)
+    assert cal(n=0) == Bd.MLA_ERR_INVALID_ARG
+    assert cal(n=65537) == Bd.MLA_ERR_INVALID_ARG
+    assert cal(scale=float("inf")) == Bd.MLA_ERR_INVALID_ARG
+    grid = (ctypes.c_float * 2)(1.0, 0.0)
+    fit = lambda ng: lib.gqa_fit_clip(ctypes.byref(d), P, 64, P, grid, ng, P, None)
+    assert fit(0) == Bd.MLA_ERR_INVALID_ARG
+    assert fit(2) == Bd.MLA_ERR_INVALID_ARG                             # grid value 0 is outside (0, 1]
