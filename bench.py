@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=8, help="cache copies used in turn")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true",
+                    help="skip the grouped-query (OSCAR full-attention) decode measurement")
     ap.add_argument("--no-sparse", action="store_true",
                     help="skip the sparse (indexer top-k) decode measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -290,6 +292,12 @@ def main():
         torch.cuda.empty_cache()
         result["sparse_decode"] = sparse_bench(M, S, dev, args)
 
+    if not args.no_gqa:
+        if args.no_sparse:
+            del caches
+        torch.cuda.empty_cache()
+        result["gqa_decode"] = gqa_bench(M, S, dev, args)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, st, c_cal, lat_seed=1000 + w.wid, lens=lens, base=base,
                                               model=model, w_uk=w_uk, w_uv=w_uv, qn=qn, qr=qr, kr=kr,
@@ -385,6 +393,94 @@ def sparse_bench(M, S, dev, args):
             "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(score_bytes / (sc_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4) if sc_us else None,
             "algorithmic_bytes_per_launch": score_bytes},
+    }
+
+
+def gqa_bench(M, S, dev, args):
+    """OSCAR on a grouped-query layer: 32 query heads, 8 KV heads, head dim
+    128, INT2 groups of 32, the 16k-32k context draw of the main measurement
+    (8 sequences).  Calibration from 2048 synthetic tokens (anisotropic
+    channels), K/V appended through gqa_append_quant, then decode steps of one
+    query token per sequence."""
+    import torch
+    hq, hkv, hd, grp = 32, 8, 128, 32
+    gd = M.GqaDims(hd, hq, hkv, grp)
+    w2 = S.WORKLOADS[2]
+    lens = S.seq_lens(w2, S.streams(w2.wid))
+    base, cap = S.contiguous_layout(lens)
+    B = len(lens)
+    n_cal = 2048
+
+    def aniso(shape, seed):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        ax = torch.exp(torch.empty(shape[-1], device=dev).uniform_(np.log(0.1), np.log(3.0), generator=g))
+        return (torch.randn(shape, generator=g, device=dev) * ax).to(torch.bfloat16)
+
+    q_cal, k_cal, v_cal = aniso((hq, n_cal, hd), 11), aniso((hkv, n_cal, hd), 12), aniso((hkv, n_cal, hd), 13)
+    scale = float(np.float32(1.0 / np.sqrt(hd)))
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    rk, rv, _, _ = M.gqa_calibrate(gd, q_cal, k_cal, v_cal, scale)
+    calib_ms = (time.perf_counter() - t) * 1e3
+    rk_t, rv_t = M.gqa_prepare_rotation(gd, rk), M.gqa_prepare_rotation(gd, rv)
+    grid = [1.0 - 0.05 * k for k in range(11)]
+    alpha_k, alpha_v = M.gqa_fit_clip(gd, k_cal, rk_t, grid), M.gqa_fit_clip(gd, v_cal, rv_t, grid)
+    cache = M.GqaCache(gd, cap, dev)
+    piece = 1 << 16
+    for a in range(0, cap, piece):
+        n = min(piece, cap - a)
+        kn, vn = aniso((n, hkv, hd), 20000 + a), aniso((n, hkv, hd), 30000 + a)
+        M.gqa_append_quant(gd, kn, vn, torch.arange(a, a + n, dtype=torch.int64, device=dev), rk_t, rv_t,
+                           alpha_k, alpha_v, cache)
+        del kn, vn
+    q = S.torch_normal_bf16((B, 1, hq, hd), 40000, dev)
+    seq_base, seq_len = torch.from_numpy(base).to(dev), torch.from_numpy(lens).to(dev)
+    ws = torch.empty(M.gqa_decode_workspace_size(gd, B, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 1, hq, hd), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, 1, hq), dtype=torch.float32, device=dev)
+
+    def step():
+        M.gqa_decode(gd, q, cache, rk_t, rv_t, seq_base, seq_len, 1, True, scale, ws, out, lse)
+
+    n = max(args.steps // 2, 10)
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1e3 / n
+    M.mla_timing_enable(True)
+    M.mla_timing_reset()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    k_us = {}
+    for name in ("gqa_rotate_q", "decode_plan", "splitk_decode", "combine", "gqa_unrotate"):
+        c_ms, cnt = M.mla_timing_query(name)
+        if cnt:
+            k_us[name] = round(c_ms / cnt * 1e3, 3)
+    M.mla_timing_enable(False)
+    tokens = int(np.sum(lens))
+    entry = 2 * (hd // 4 + (hd // grp) * 4)          # K and V: codes + fp16 scale/zero per token and KV head
+    cache_bytes = tokens * hkv * entry
+    sk_us = k_us.get("splitk_decode")
+    return {
+        "workload": "gqa-layer-h32-kv8-d128-b8-ctx16k-32k", "batch": B, "context_tokens": tokens,
+        "q_heads": hq, "kv_heads": hkv, "head_dim": hd, "group_size": grp,
+        "cache_bytes_per_token": hkv * entry,
+        "ms_per_step": round(ms, 5),
+        "GB/s": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
+        "query_tokens_per_s": round(B / (ms * 1e-3), 1),
+        "kernel_us": k_us,
+        "calibration_ms": round(calib_ms, 1),
+        "splitk_roofline": {
+            "bound": "hbm", "achieved": round(cache_bytes / (sk_us * 1e-6) / 1e9, 1) if sk_us else None,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(cache_bytes / (sk_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4) if sk_us else None,
+            "algorithmic_bytes_per_launch": cache_bytes},
     }
 
 

@@ -159,13 +159,13 @@ int target_items(int rows, bool mfma) {
 #endif
 int min_chunk_tiles(int tile) { return (MLA_SPLIT_MIN_TOKENS + tile - 1) / tile; }
 
-WsLayout layout(const mla_dims &d, int B, int Tq) {
+WsLayout layout(const mla_dims &d, int B, int Tq, int min_items = 0) {
   WsLayout w;
   const int r = d.kv_lora_rank, K = r + d.qk_rope_head_dim;
   const int M = d.num_heads * Tq;
   // the planner emits at most max(target, number of sequences) items
   const int tgt = std::max(target_items(M, true), target_items(M, false));
-  w.max_items = std::max(tgt, B);
+  w.max_items = std::max(std::max(tgt, B), min_items);
   size_t off = 0;
   w.items = off;
   off = align256(off + sizeof(WorkItem) * w.max_items);
@@ -280,10 +280,25 @@ struct GqaWs {
   size_t base2 = 0, len2 = 0, lse2 = 0, total = 0;
 };
 
+// Work items of the grouped-query split-K: one wave per item on the MFMA
+// kernel, eight resident per CU (two waves per SIMD at its register count);
+// otherwise the vector-ALU kernel's own target.
+constexpr int kGqaWavesPerCu = 8;
+
+bool gqa_use_mfma(const gqa_dims &g, int Tq) {
+  const int rows = g.num_q_heads / g.num_kv_heads * Tq;
+  return g_decode_variant != 1 && gqa_mfma_supported(gqa_latent_dims(g), rows);
+}
+
+int gqa_target_items(const gqa_dims &g, int Tq) {
+  const int rows = g.num_q_heads / g.num_kv_heads * Tq;
+  return gqa_use_mfma(g, Tq) ? kGqaWavesPerCu * device_cu_count() : target_items(rows, false);
+}
+
 GqaWs gqa_layout(const gqa_dims &g, int B, int Tq) {
   GqaWs w;
   const int Bp = B * g.num_kv_heads, G = g.num_q_heads / g.num_kv_heads;
-  w.split = layout(gqa_latent_dims(g), Bp, Tq);
+  w.split = layout(gqa_latent_dims(g), Bp, Tq, gqa_target_items(g, Tq));
   size_t off = w.split.total;
   w.base2 = off;
   off = align256(off + sizeof(int64_t) * Bp);
@@ -981,8 +996,9 @@ mla_status gqa_decode(const gqa_dims *dims, const uint16_t *q, const gqa_cache *
   a.part_o = reinterpret_cast<uint16_t *>(ws + w.split.part_o);
   a.part_ml = reinterpret_cast<float *>(ws + w.split.part_ml);
   a.max_items = w.split.max_items;
-  a.target_items = target_items(M, false);
-  a.tile = 16;
+  const bool use_mfma = gqa_use_mfma(*dims, tq);
+  a.target_items = gqa_target_items(*dims, tq);
+  a.tile = use_mfma ? 32 : 16;
   a.min_chunk_tiles = min_chunk_tiles(a.tile);
   GqaDecodeArgs g{};
   g.q = q;
@@ -1007,7 +1023,7 @@ mla_status gqa_decode(const gqa_dims *dims, const uint16_t *q, const gqa_cache *
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_gqa_rotate_q(g, s);
   if (e == hipSuccess) e = launch_plan(a, s);
-  if (e == hipSuccess) e = launch_splitk_valu(a, s);
+  if (e == hipSuccess) e = use_mfma ? launch_gqa_splitk_mfma(a, s) : launch_splitk_valu(a, s);
   if (e == hipSuccess) e = launch_combine(a, s);
   if (e == hipSuccess) e = launch_gqa_unrotate(g, s);
   if (e != hipSuccess) return hip_fail(e, "gqa_decode");

@@ -578,6 +578,191 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_c
   }
 }
 
+// ---- grouped-query layers (head dim 128): one wave per work item ----
+// The same tile machinery for a KV head of a grouped-query layer, whose
+// head dim (128) is one wave's share of the latent above: a work item is a
+// token range of one (sequence, KV head) pseudo-sequence, its G * Tq query
+// rows (at most 32) are the N side of the score MFMA, and the K and V tiles
+// come from their own caches.  One wave per workgroup and no cross-wave
+// reduction, so the loop needs no barrier: per 32-token tile the wave
+// dequantises K into score operands and V into its LDS tile, takes the scores
+// (8 MFMAs), runs the online softmax (a row's 32 tokens on lanes l and l ^ 32),
+// stages P in LDS and accumulates O += P V_hat (8 MFMAs, V_hat through the
+// transposing load).  Channels travel in the slot order of the latent kernel;
+// the rotated queries are gathered into it and the partial un-permuted.
+constexpr int GQ_D = 128;
+constexpr int GQ_ROWS = 32;
+
+struct __align__(16) GqaSmem {
+  f16 z[TT * ZSTRIDE];         // dequantised V tile [token][slot]
+  f16 p[GQ_ROWS * PRSTRIDE];   // P [row][token]
+  float alpha[GQ_ROWS];
+  float inv_l[GQ_ROWS];
+};
+
+// o_settle for the four output accumulators of the grouped-query kernel.
+template <bool kAfterMfma>
+__device__ __forceinline__ void gqa_o_settle(f32x16 (&o)[4]) {
+  if (kAfterMfma)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+  else
+    asm volatile("s_nop 4" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+}
+
+template <int G>
+__device__ __forceinline__ RawTile gqa_load(const mla_cache &c, int64_t slot, int hf) {
+  RawTile t;
+  const uint32_t *codes32 = reinterpret_cast<const uint32_t *>(c.codes);
+  t.codes = *reinterpret_cast<const uint4 *>(codes32 + slot * (GQ_D / 16) + hf * 4);
+  if (G == 32) {
+    const uint2 s2 = *reinterpret_cast<const uint2 *>(c.scale_zero + (slot * (GQ_D / G) + 2 * hf) * 2);
+    t.sz = uint4{s2.x, s2.y, 0u, 0u};
+  } else {
+    t.sz = *reinterpret_cast<const uint4 *>(c.scale_zero + (slot * (GQ_D / G) + 4 * hf) * 2);
+  }
+  t.rope = uint4{0u, 0u, 0u, 0u};
+  return t;
+}
+
+template <int G>
+__global__ __launch_bounds__(64) void gqa_splitk_mfma_kernel(DecodeArgs a) {
+  __shared__ GqaSmem sm;
+  const int item = blockIdx.x;
+  if (item >= a.meta[0]) return;
+  const WorkItem it = a.items[item];
+  const int l = threadIdx.x, hf = l >> 5, l32 = l & 31;
+  const int Gq = a.d.num_heads;  // query heads per KV head
+  const int M = Gq * a.Tq;
+  const int L = a.seq_len[it.b];
+  const int64_t base = a.seq_base[it.b];
+  const int n_tiles = (it.t1 - it.t0 + TT - 1) / TT;
+
+  // rotated queries of row l32 as score B operands, gathered into slot order
+  f16x8 aq[KB];
+  {
+    const float *qr = static_cast<const float *>(a.qbuf) + (static_cast<int64_t>(it.b) * M + min(l32, M - 1)) * GQ_D;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) aq[kb][e] = static_cast<f16>(l32 < M ? qr[slot_channel(hf, kb, e)] : 0.0f);
+  }
+  // softmax ownership: row l32, tokens 8 j + 4 hf + i (j, i < 4) of each tile
+  const int vis = l32 < M ? (a.causal ? (L - a.Tq + l32 / Gq + 1) : L) : -1;
+  const int lim = min(it.t1, vis);  // tokens < lim are visible to this row
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 o[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) o[nt] = f32x16{};
+
+  const int g16 = l >> 4, s16 = l & 15;
+  const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);
+  const int pv_col = (16 * (g16 & 1) + 4 * (s16 & 3)) ^ (8 * ((g16 >> 1) & 1));
+  const int zsw = 8 * ((l32 >> 3) & 1);
+  auto tile_slot = [&](int i) -> int64_t {
+    const int t = min(it.t0 + min(i, n_tiles - 1) * TT + l32, it.t1 - 1);
+    return base + t;
+  };
+  RawTile rk = gqa_load<G>(a.cache, tile_slot(0), hf);
+  RawTile rv = gqa_load<G>(a.vcache, tile_slot(0), hf);
+  for (int i = 0; i < n_tiles; ++i) {
+    // K operands, the next K tile in flight, the scores; then V into the
+    // same registers, the next V tile in flight, V to LDS (short live ranges
+    // keep two waves per SIMD)
+    f32x16 sacc = f32x16{};
+    {
+      f16x8 bk[KB];
+      dequant<G>(rk, bk);
+      rk = gqa_load<G>(a.cache, tile_slot(i + 1), hf);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bk[kb], aq[kb], sacc, 0, 0, 0);
+    }
+    {
+      f16x8 bv[KB];
+      dequant<G>(rv, bv);
+      rv = gqa_load<G>(a.vcache, tile_slot(i + 1), hf);
+      // V tile to LDS (this wave's only), chunk kb ^ 1 in rows 8..15 and 24..31
+      f16 *zt = sm.z + l32 * ZSTRIDE + 64 * hf;
+      f16 *ze = zt + zsw, *zo = zt - zsw;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(((kb & 1) ? zo : ze) + 8 * kb) = bv[kb];
+    }
+    // online softmax of row l32 over this tile's tokens 8 j + 4 hf + i
+    const int t_first = it.t0 + i * TT + 4 * hf;
+    float s[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = (t_first + 8 * (v >> 2) + (v & 3) < lim) ? sacc[v] : -INFINITY;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const bool need = tmax > m_run + kRescaleThreshold;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;
+    const bool scale_o = need && m_run != -INFINITY;  // O is still zero before the first visible tile
+    m_run = need ? tmax : m_run;
+    const float m_sub = (m_run == -INFINITY) ? 0.0f : m_run;
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x4 pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(s[4 * j + e] - m_sub);
+        psum += pe;
+        pv[e] = static_cast<f16>(pe);
+      }
+      *reinterpret_cast<f16x4 *>(sm.p + l32 * PRSTRIDE + 8 * j + 4 * hf) = pv;
+    }
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    if (hf == 0) sm.alpha[l32] = alpha;
+    if (__any(scale_o ? 1 : 0)) {  // in place in the accumulator registers
+      gqa_o_settle<true>(o);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float al = sm.alpha[8 * (v >> 2) + 4 * hf + (v & 3)];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          float x = o[nt][v];
+          agpr_scale(x, al);
+          o[nt][v] = x;
+        }
+      }
+      gqa_o_settle<false>(o);
+    }
+    // O += P V_hat
+    const f16 *zb_base = sm.z + pv_krow * ZSTRIDE + pv_col;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const f16x8 pa = *reinterpret_cast<const f16x8 *>(sm.p + l32 * PRSTRIDE + 16 * ks + 8 * hf);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const f16 *z0 = zb_base + 16 * ks * ZSTRIDE + 32 * nt;
+        const f16x4 lo = ds_read_tr16(z0);
+        const f16x4 hi = ds_read_tr16(z0 + 4 * ZSTRIDE);
+        const f16x8 zb = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, zb, o[nt], 0, 0, 0);
+      }
+    }
+  }
+  // partial: O / l in fp16 (rows 8 (v / 4) + 4 hf + v % 4, slot 32 nt + l32), (m, l)
+  if (hf == 0) sm.inv_l[l32] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  f16 *po = reinterpret_cast<f16 *>(a.part_o);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int sl = 32 * nt + l32;
+    const int ch = slot_channel(sl >> 6, (sl & 63) >> 3, sl & 7);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 8 * (v >> 2) + 4 * hf + (v & 3);
+      if (m < M) po[(static_cast<int64_t>(item) * M + m) * GQ_D + ch] = static_cast<f16>(o[nt][v] * sm.inv_l[m]);
+    }
+  }
+  if (hf == 0 && l32 < M) {
+    a.part_ml[(static_cast<int64_t>(item) * M + l32) * 2 + 0] = m_run;
+    a.part_ml[(static_cast<int64_t>(item) * M + l32) * 2 + 1] = l_run;
+  }
+}
+
 }  // namespace
 
 bool mfma_absorb_supported(const mla_dims &d) { return d.qk_nope_head_dim % 16 == 0; }
@@ -608,6 +793,20 @@ hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
     splitk_mfma_kernel<32><<<grid, 256, 0, s>>>(a, rb_count, n_logical);
   else
     splitk_mfma_kernel<16><<<grid, 256, 0, s>>>(a, rb_count, n_logical);
+  return hipGetLastError();
+}
+
+bool gqa_mfma_supported(const mla_dims &d, int rows) {
+  return d.kv_lora_rank == GQ_D && d.qk_rope_head_dim == 0 && rows <= GQ_ROWS &&
+         (d.group_size == 16 || d.group_size == 32);
+}
+
+hipError_t launch_gqa_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
+  TimedLaunch tl("splitk_decode", s);
+  if (a.d.group_size == 32)
+    gqa_splitk_mfma_kernel<32><<<a.max_items, 64, 0, s>>>(a);
+  else
+    gqa_splitk_mfma_kernel<16><<<a.max_items, 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

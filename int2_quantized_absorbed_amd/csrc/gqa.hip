@@ -120,47 +120,89 @@ __global__ __launch_bounds__(kThreads) void gqa_weighted_cov_kernel(const uint16
   }
 }
 
+// Query heads of one KV head handled together by the rotation kernels: the
+// lane's row (or column) of the rotation is loaded once and applied to all
+// of them from LDS.
+constexpr int kHeadChunk = 8;
+
 // Rotated, scaled queries in the split-K kernel's layout (one pseudo-sequence
 // b' = b * H_kv + h per sequence and KV head, rows m = t * G + g):
 //   qbuf[b'][m][c] = scale * log2(e) * sum_n q[b][t][h G + g][n] R_k,apply[h][n][c]
 // and the pseudo-sequences' slots: KV head h's entries are cache slots
-// h * capacity + seq_base[b] ...  Grid (Tq, B * H_kv).
+// h * capacity + seq_base[b] ...  Grid (B * H_kv, Tq); thread c < d holds
+// row c of R_apply^T (the rotation's column c) and forms channel c of every
+// query head of the group.
 __global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a) {
-  const int t = blockIdx.x, bp = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, tid = threadIdx.x;
+  __shared__ float qs[kHeadChunk][256];
+  const int bp = blockIdx.x, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, c = threadIdx.x;
   const int G = a.H_q / a.H_kv, d = a.d;
-  if (t == 0 && tid == 0) {
+  if (t == 0 && c == 0) {
     a.base2[bp] = static_cast<int64_t>(h) * a.capacity + a.seq_base[b];
     a.len2[bp] = a.seq_len[b];
   }
-  for (int e = tid; e < G * d; e += kThreads) {
-    const int g = e / d, c = e % d;
-    const uint16_t *qr = a.q + ((static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G + g) * d;
-    const uint16_t *rr = a.rk_t + (static_cast<int64_t>(h) * d + c) * d;  // row c of R_apply^T
-    float acc = 0.0f;
-    for (int k = 0; k < d; ++k) acc = fmaf(bf16_to_f32(rr[k]), bf16_to_f32(qr[k]), acc);
-    a.qbuf[((static_cast<int64_t>(bp) * a.Tq + t) * G + g) * d + c] = acc * a.scale_log2;
+  const uint16_t *qbase = a.q + ((static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G) * d;
+  const uint16_t *rrow = a.rk_t + (static_cast<int64_t>(h) * d + min(c, d - 1)) * d;
+  for (int g0 = 0; g0 < G; g0 += kHeadChunk) {
+    const int ng = min(kHeadChunk, G - g0);
+    __syncthreads();  // qs is rewritten
+    for (int e = c; e < ng * d; e += blockDim.x) qs[e / d][e % d] = bf16_to_f32(qbase[static_cast<int64_t>(g0) * d + e]);
+    __syncthreads();
+    if (c >= d) continue;
+    float acc[kHeadChunk];
+#pragma unroll
+    for (int g = 0; g < kHeadChunk; ++g) acc[g] = 0.0f;
+    for (int n = 0; n < d; n += 8) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(rrow + n);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float r0 = __uint_as_float(ww[j] << 16), r1 = __uint_as_float(ww[j] & 0xffff0000u);
+#pragma unroll
+        for (int g = 0; g < kHeadChunk; ++g) {
+          acc[g] = fmaf(r0, qs[g][n + 2 * j], acc[g]);
+          acc[g] = fmaf(r1, qs[g][n + 2 * j + 1], acc[g]);
+        }
+      }
+    }
+    for (int g = 0; g < ng; ++g)
+      a.qbuf[((static_cast<int64_t>(bp) * a.Tq + t) * G + g0 + g) * d + c] = acc[g] * a.scale_log2;
   }
 }
 
 // out[b][t][h G + g][v] = sum_c R_v,apply[h][v][c] o_z[b'][t G + g][c] (the
 // merged attention output, still in KV head h's rotated basis), fp32; lse
-// copied into the output layout.  Grid (B * Tq * H_q).
+// copied into the output layout.  Grid (B * H_kv, Tq); R_apply^T of head h
+// is staged in LDS (all of its 16-byte loads in flight together), then
+// thread v < d walks column v of it for every query head of the group.
 __global__ __launch_bounds__(kThreads) void gqa_unrotate_kernel(GqaDecodeArgs a) {
-  __shared__ float oz[256];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  extern __shared__ uint16_t rs[];  // [d][d] R_apply^T of head h, then zs
+  const int bp = blockIdx.x, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, v = threadIdx.x;
   const int G = a.H_q / a.H_kv, d = a.d;
-  const int qh = row % a.H_q, t = (row / a.H_q) % a.Tq, b = row / (a.H_q * a.Tq);
-  const int h = qh / G, g = qh % G;
-  const int64_t row2 = (static_cast<int64_t>(b * a.H_kv + h) * a.Tq + t) * G + g;
-  for (int e = tid; e < d; e += kThreads) oz[e] = a.oz[row2 * d + e];
-  __syncthreads();
-  const uint16_t *rv = a.rv_t + static_cast<int64_t>(h) * d * d;  // rv[c][v] = R_v,apply[v][c]
-  for (int v = tid; v < d; v += kThreads) {
-    float acc = 0.0f;
-    for (int c = 0; c < d; ++c) acc = fmaf(bf16_to_f32(rv[static_cast<int64_t>(c) * d + v]), oz[c], acc);
-    a.out[static_cast<int64_t>(row) * d + v] = acc;
+  float(*zs)[256] = reinterpret_cast<float(*)[256]>(rs + d * d);
+  {
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.rv_t + static_cast<int64_t>(h) * d * d);
+    uint4 *dst = reinterpret_cast<uint4 *>(rs);
+    for (int e = v; e < d * d / 8; e += blockDim.x) dst[e] = src[e];
   }
-  if (tid == 0 && a.lse != nullptr) a.lse[row] = a.lse2[row2];
+  const int64_t row2 = (static_cast<int64_t>(bp) * a.Tq + t) * G;              // first merged row of the group
+  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G;    // first output row
+  for (int g0 = 0; g0 < G; g0 += kHeadChunk) {
+    const int ng = min(kHeadChunk, G - g0);
+    __syncthreads();  // zs is rewritten (and, the first time, rs is complete)
+    for (int e = v; e < ng * d; e += blockDim.x) zs[e / d][e % d] = a.oz[(row2 + g0) * d + e];
+    __syncthreads();
+    if (v < ng && a.lse != nullptr) a.lse[row + g0 + v] = a.lse2[row2 + g0 + v];
+    if (v >= d) continue;
+    float acc[kHeadChunk];
+#pragma unroll
+    for (int g = 0; g < kHeadChunk; ++g) acc[g] = 0.0f;
+    for (int c = 0; c < d; ++c) {
+      const float r = bf16_to_f32(rs[c * d + v]);  // R_v,apply[v][c]
+#pragma unroll
+      for (int g = 0; g < kHeadChunk; ++g) acc[g] = fmaf(r, zs[g][c], acc[g]);
+    }
+    for (int g = 0; g < ng; ++g) a.out[(row + g0 + g) * d + v] = acc[g];
+  }
 }
 
 }  // namespace
@@ -179,14 +221,17 @@ hipError_t launch_gqa_calib_stats(const uint16_t *q, const uint16_t *k, const ui
 hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, hipStream_t s) {
   if (a.d > 256) return hipErrorInvalidValue;
   TimedLaunch tl("gqa_rotate_q", s);
-  gqa_rotate_q_kernel<<<dim3(a.Tq, a.B * a.H_kv), kThreads, 0, s>>>(a);
+  const int threads = a.d <= 64 ? 64 : (a.d <= 128 ? 128 : 256);
+  gqa_rotate_q_kernel<<<dim3(a.B * a.H_kv, a.Tq), threads, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gqa_unrotate(const GqaDecodeArgs &a, hipStream_t s) {
   if (a.d > 256) return hipErrorInvalidValue;
   TimedLaunch tl("gqa_unrotate", s);
-  gqa_unrotate_kernel<<<a.B * a.Tq * a.H_q, kThreads, 0, s>>>(a);
+  const int threads = a.d <= 64 ? 64 : (a.d <= 128 ? 128 : 256);
+  const size_t lds = static_cast<size_t>(a.d) * a.d * sizeof(uint16_t) + kHeadChunk * 256 * sizeof(float);
+  gqa_unrotate_kernel<<<dim3(a.B * a.H_kv, a.Tq), threads, lds, s>>>(a);
   return hipGetLastError();
 }
 

@@ -128,5 +128,9 @@ bool mfma_absorb_supported(const mla_dims &d);
 int mfma_row_block();
 hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s);
+// grouped-query layers: head dim 128, at most 32 query rows per KV head,
+// one wave per work item (grid = max_items)
+bool gqa_mfma_supported(const mla_dims &d, int rows);
+hipError_t launch_gqa_splitk_mfma(const DecodeArgs &a, hipStream_t s);
 
 }  // namespace mla

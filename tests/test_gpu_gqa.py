@@ -10,10 +10,12 @@
   append rule (bit-exact outside the 1e-5 boundary band, fp16 midpoint
   excuse), slots outside the cache skipped.
 * ``gqa_decode``: outputs and lse against ``rotated_attention`` on the entries
-  the GPU cache holds, to the decode tolerance; ragged, empty and multi-query
-  (causal and not) cases, group sizes 1 (multi-head), 4 and 8, d = 64 and
-  128; and the full-size shape of the benchmark on its longest and shortest
-  sequences.
+  the GPU cache holds, to the decode tolerance, on the MFMA kernel (d = 128,
+  at most 32 query rows per KV head) and on the vector-ALU kernel; ragged,
+  empty, tile-edge and multi-query (causal and not) cases, group sizes 1
+  (multi-head), 4, 8 and 16 (32 rows at tq = 2), d = 64 and 128, INT2 groups
+  of 16 and 32; and the full-size shape of the benchmark on its longest and
+  shortest sequences.
 """
 import numpy as np
 import pytest
@@ -175,21 +177,29 @@ def _check_decode(dims, case, tq, causal, scale, out, lse, seqs=None):
 
 
 DECODE_CASES = [
-    # d, hq, hkv, G, lens, tq, causal
+    # d, hq, hkv, G, lens, tq, causal (d = 128 with at most 32 rows per KV head
+    # takes the MFMA kernel under variant 0; the rest, and variant 1, the vector ALU)
     (128, 32, 8, 32, [700, 0, 1500, 33], 1, True),
     (64, 8, 8, 16, [300, 1000], 4, True),
     (128, 16, 2, 32, [257, 1100], 3, False),
     (64, 32, 4, 16, [5, 64, 2049], 2, True),
+    (128, 8, 8, 16, [1, 31, 32, 33, 4000], 4, True),
+    (128, 32, 2, 32, [900, 77], 2, True),
 ]
 
 
+@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("d,hq,hkv,G,lens,tq,causal", DECODE_CASES)
-def test_gqa_decode_matches_oracle(d, hq, hkv, G, lens, tq, causal):
-    C.say(f"gqa decode d={d} hq={hq} hkv={hkv} G={G} lens={lens} tq={tq} causal={causal}")
+def test_gqa_decode_matches_oracle(d, hq, hkv, G, lens, tq, causal, variant):
+    C.say(f"gqa decode d={d} hq={hq} hkv={hkv} G={G} lens={lens} tq={tq} causal={causal} variant={variant}")
     dims = M.GqaDims(d, hq, hkv, G)
     case = _decode_case(dims, lens, tq, seed=51)
     scale = _scale(d)
-    out, lse = _run_decode(dims, case, tq, causal, scale)
+    M.mla_set_decode_variant(variant)
+    try:
+        out, lse = _run_decode(dims, case, tq, causal, scale)
+    finally:
+        M.mla_set_decode_variant(0)
     _check_decode(dims, case, tq, causal, scale, out, lse)
 
 
