@@ -458,7 +458,7 @@ def gqa_bench(M, S, dev, args):
         step()
     torch.cuda.synchronize()
     k_us = {}
-    for name in ("gqa_rotate_q", "decode_plan", "splitk_decode", "combine", "gqa_unrotate"):
+    for name in ("gqa_rotate_q", "decode_plan", "splitk_decode", "combine", "gqa_merge_unrotate"):
         c_ms, cnt = M.mla_timing_query(name)
         if cnt:
             k_us[name] = round(c_ms / cnt * 1e3, 3)

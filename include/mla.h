@@ -418,8 +418,10 @@ size_t gqa_decode_workspace_size(const gqa_dims *dims, int32_t batch,
  *     z_k R_k,apply^T, v_hat = z_v R_v,apply^T the dequantised entries
  *     un-rotated; lse [B][tq][H_q] fp32 natural-log log-sum-exp (may be NULL)
  * An empty sequence gives out = 0, lse = -inf.  Runs as: query rotation,
- * split-K attention over each (sequence, KV head) on the vector ALU,
- * log-sum-exp merge, un-rotation.  Asynchronous; no host synchronisation.
+ * split-K attention over each (sequence, KV head) (MFMA for head_dim 128
+ * with at most 32 query rows per KV head, G * tq; vector ALU otherwise),
+ * then the log-sum-exp merge and the un-rotation in one launch.
+ * Asynchronous; no host synchronisation.
  * Errors: INVALID_ARG (dims, batch < 0, tq outside 1..64, causal not 0/1,
  * NULL or unaligned pointers), WORKSPACE, HIP. */
 mla_status gqa_decode(const gqa_dims *dims, const uint16_t *q,
@@ -451,7 +453,8 @@ mla_status mla_set_decode_variant(int32_t variant);
  * split-K work, and "decode_plan" is not launched), "splitk_decode",
  * "combine", "up_proj", "combine_up_proj" (the two in one launch where
  * the shape allows), "index_score", "index_select", "gqa_rotate_q",
- * "gqa_unrotate", "fold_weights", "prepare_rotation", "covariance", "clip_fit".
+ * "gqa_merge_unrotate", "fold_weights", "prepare_rotation", "covariance",
+ * "clip_fit".
  * mla_timing_query waits for the recorded events and returns the summed
  * milliseconds and launch count since the last reset.  Process-wide; not
  * for use while another thread launches. */

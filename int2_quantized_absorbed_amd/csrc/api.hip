@@ -277,7 +277,7 @@ mla_dims gqa_latent_dims(const gqa_dims &g) {
 
 struct GqaWs {
   WsLayout split;  // the shared decode workspace of B * H_kv pseudo-sequences
-  size_t base2 = 0, len2 = 0, lse2 = 0, total = 0;
+  size_t base2 = 0, len2 = 0, total = 0;
 };
 
 // Work items of the grouped-query split-K: one wave per item on the MFMA
@@ -297,15 +297,13 @@ int gqa_target_items(const gqa_dims &g, int Tq) {
 
 GqaWs gqa_layout(const gqa_dims &g, int B, int Tq) {
   GqaWs w;
-  const int Bp = B * g.num_kv_heads, G = g.num_q_heads / g.num_kv_heads;
+  const int Bp = B * g.num_kv_heads;
   w.split = layout(gqa_latent_dims(g), Bp, Tq, gqa_target_items(g, Tq));
   size_t off = w.split.total;
   w.base2 = off;
   off = align256(off + sizeof(int64_t) * Bp);
   w.len2 = off;
   off = align256(off + sizeof(int32_t) * Bp);
-  w.lse2 = off;
-  off = align256(off + sizeof(float) * static_cast<size_t>(Bp) * Tq * G);
   w.total = off;
   return w;
 }
@@ -987,7 +985,6 @@ mla_status gqa_decode(const gqa_dims *dims, const uint16_t *q, const gqa_cache *
   a.Tq = tq;
   a.causal = causal;
   a.scale_log2 = softmax_scale * kLog2e;
-  a.lse = reinterpret_cast<float *>(ws + w.lse2);
   a.items = reinterpret_cast<WorkItem *>(ws + w.split.items);
   a.item_begin = reinterpret_cast<int32_t *>(ws + w.split.item_begin);
   a.meta = reinterpret_cast<int32_t *>(ws + w.split.meta);
@@ -1016,16 +1013,13 @@ mla_status gqa_decode(const gqa_dims *dims, const uint16_t *q, const gqa_cache *
   g.qbuf = static_cast<float *>(a.qbuf);
   g.base2 = const_cast<int64_t *>(a.seq_base);
   g.len2 = const_cast<int32_t *>(a.seq_len);
-  g.oz = a.oz;
-  g.lse2 = a.lse;
   g.out = out;
   g.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_gqa_rotate_q(g, s);
   if (e == hipSuccess) e = launch_plan(a, s);
   if (e == hipSuccess) e = use_mfma ? launch_gqa_splitk_mfma(a, s) : launch_splitk_valu(a, s);
-  if (e == hipSuccess) e = launch_combine(a, s);
-  if (e == hipSuccess) e = launch_gqa_unrotate(g, s);
+  if (e == hipSuccess) e = launch_gqa_merge_unrotate(g, a, s);
   if (e != hipSuccess) return hip_fail(e, "gqa_decode");
   clear_error();
   return MLA_OK;

@@ -1,6 +1,6 @@
 // OSCAR on full-attention (grouped-query) layers: the calibration statistics
-// of the two per-KV-head rotations, and the query rotation / output
-// un-rotation around the shared split-K decode.
+// of the two per-KV-head rotations, and the query rotation / partial merge
+// and output un-rotation around the split-K decode.
 //
 // [OSCAR issue #10, "MLA model support", maintainer reply, part "How the
 // rotation adapts to the latent", first point]: on full-attention models the
@@ -169,29 +169,72 @@ __global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a)
   }
 }
 
-// out[b][t][h G + g][v] = sum_c R_v,apply[h][v][c] o_z[b'][t G + g][c] (the
-// merged attention output, still in KV head h's rotated basis), fp32; lse
-// copied into the output layout.  Grid (B * H_kv, Tq); R_apply^T of head h
-// is staged in LDS (all of its 16-byte loads in flight together), then
-// thread v < d walks column v of it for every query head of the group.
-__global__ __launch_bounds__(kThreads) void gqa_unrotate_kernel(GqaDecodeArgs a) {
-  extern __shared__ uint16_t rs[];  // [d][d] R_apply^T of head h, then zs
-  const int bp = blockIdx.x, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, v = threadIdx.x;
-  const int G = a.H_q / a.H_kv, d = a.d;
+// Merge of the split-K partials and un-rotation in one launch.  Grid
+// (B * H_kv, Tq): the block takes the G query heads of one (sequence, KV
+// head, query position), kHeadChunk at a time.  R_apply^T of the head is
+// staged in LDS first (its loads in flight during the merge).  Thread (row,
+// 4-channel chunk) folds the items of the pseudo-sequence into a running
+// (max, sum, O), kMergeU at a time (O_k = l_k times the stored fp16 O_k / l_k):
+//   o_z = sum_k 2^(m_k - m) O_k / sum_k 2^(m_k - m) l_k,
+//   lse = ln 2 (m + log2 sum_k 2^(m_k - m) l_k);
+// then thread v forms out[v] = sum_c R_v,apply[v][c] o_z[c] for every row.
+constexpr int kMergeU = 16;
+
+__global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeArgs a, DecodeArgs sa) {
+  extern __shared__ uint16_t rs[];  // [d][d] R_apply^T of head h, then zs [kHeadChunk][256]
+  const int bp = blockIdx.x, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, tid = threadIdx.x;
+  const int G = a.H_q / a.H_kv, d = a.d, M = G * a.Tq, nch = d / 4;
   float(*zs)[256] = reinterpret_cast<float(*)[256]>(rs + d * d);
   {
     const uint4 *src = reinterpret_cast<const uint4 *>(a.rv_t + static_cast<int64_t>(h) * d * d);
     uint4 *dst = reinterpret_cast<uint4 *>(rs);
-    for (int e = v; e < d * d / 8; e += blockDim.x) dst[e] = src[e];
+    for (int e = tid; e < d * d / 8; e += blockDim.x) dst[e] = src[e];
   }
-  const int64_t row2 = (static_cast<int64_t>(bp) * a.Tq + t) * G;              // first merged row of the group
-  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G;    // first output row
+  const int ib = sa.item_begin[bp], ie = sa.item_begin[bp + 1];
+  const f16 *po = reinterpret_cast<const f16 *>(sa.part_o);
+  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G;  // first output row
   for (int g0 = 0; g0 < G; g0 += kHeadChunk) {
     const int ng = min(kHeadChunk, G - g0);
-    __syncthreads();  // zs is rewritten (and, the first time, rs is complete)
-    for (int e = v; e < ng * d; e += blockDim.x) zs[e / d][e % d] = a.oz[(row2 + g0) * d + e];
+    __syncthreads();  // zs is rewritten
+    for (int pr = tid; pr < ng * nch; pr += blockDim.x) {
+      const int g = pr / nch, c = pr % nch, m = t * G + g0 + g;
+      const float *ml = sa.part_ml + static_cast<int64_t>(m) * 2;
+      const f16 *pp = po + static_cast<int64_t>(m) * d + 4 * c;
+      const int64_t ml_stride = static_cast<int64_t>(M) * 2, po_stride = static_cast<int64_t>(M) * d;
+      float mrun = -INFINITY, lrun = 0.0f;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k0 = ib; k0 < ie; k0 += kMergeU) {
+        f16x4 v[kMergeU];
+        float2 st[kMergeU];
+#pragma unroll
+        for (int e = 0; e < kMergeU; ++e) {
+          const int k = min(k0 + e, ie - 1);
+          v[e] = *reinterpret_cast<const f16x4 *>(pp + k * po_stride);
+          st[e] = *reinterpret_cast<const float2 *>(ml + k * ml_stride);
+          if (k0 + e >= ie) st[e].x = -INFINITY;
+        }
+        float rm = mrun;
+#pragma unroll
+        for (int e = 0; e < kMergeU; ++e) rm = fmaxf(rm, st[e].x);
+        if (rm != -INFINITY) {
+          const float sc = exp2f(mrun - rm);  // 0 while nothing was folded in
+          acc *= sc;
+          lrun *= sc;
+#pragma unroll
+          for (int e = 0; e < kMergeU; ++e) {
+            const float wgt = st[e].x == -INFINITY ? 0.0f : exp2f(st[e].x - rm);
+            acc += (wgt * st[e].y) * __builtin_convertvector(v[e], f32x4);
+            lrun += wgt * st[e].y;
+          }
+          mrun = rm;
+        }
+      }
+      const float inv = lrun > 0.0f ? 1.0f / lrun : 0.0f;
+      *reinterpret_cast<f32x4 *>(&zs[g][4 * c]) = acc * inv;
+      if (c == 0 && a.lse != nullptr) a.lse[row + g0 + g] = lrun > 0.0f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
+    }
     __syncthreads();
-    if (v < ng && a.lse != nullptr) a.lse[row + g0 + v] = a.lse2[row2 + g0 + v];
+    const int v = tid;
     if (v >= d) continue;
     float acc[kHeadChunk];
 #pragma unroll
@@ -226,12 +269,11 @@ hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gqa_unrotate(const GqaDecodeArgs &a, hipStream_t s) {
-  if (a.d > 256) return hipErrorInvalidValue;
-  TimedLaunch tl("gqa_unrotate", s);
-  const int threads = a.d <= 64 ? 64 : (a.d <= 128 ? 128 : 256);
+hipError_t launch_gqa_merge_unrotate(const GqaDecodeArgs &a, const DecodeArgs &sa, hipStream_t s) {
+  if (a.d > 256 || a.d % 4 != 0) return hipErrorInvalidValue;
+  TimedLaunch tl("gqa_merge_unrotate", s);
   const size_t lds = static_cast<size_t>(a.d) * a.d * sizeof(uint16_t) + kHeadChunk * 256 * sizeof(float);
-  gqa_unrotate_kernel<<<dim3(a.B * a.H_kv, a.Tq), threads, lds, s>>>(a);
+  gqa_merge_unrotate_kernel<<<dim3(a.B * a.H_kv, a.Tq), kThreads, lds, s>>>(a, sa);
   return hipGetLastError();
 }
 

@@ -115,12 +115,12 @@ struct GqaDecodeArgs {
   float *qbuf;                     // [B * H_kv][Tq * G][d] rotated queries
   int64_t *base2;                  // [B * H_kv] pseudo-sequence slot bases
   int32_t *len2;                   // [B * H_kv] pseudo-sequence lengths
-  const float *oz;                 // [B * H_kv * Tq * G][d] merged output (rotated basis)
-  const float *lse2;               // [B * H_kv * Tq * G]
   float *out, *lse;                // [B][Tq][H_q][d], [B][Tq][H_q]
 };
 hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, hipStream_t s);
-hipError_t launch_gqa_unrotate(const GqaDecodeArgs &a, hipStream_t s);
+// the merge of the split-K partials (sa's items and partials) and the
+// un-rotation in one launch
+hipError_t launch_gqa_merge_unrotate(const GqaDecodeArgs &a, const DecodeArgs &sa, hipStream_t s);
 
 // MFMA split-K path (r = 512, d_r = 64): supported() says whether it applies.
 bool mfma_decode_supported(const mla_dims &d, int rows);
