@@ -1016,8 +1016,7 @@ mla_status gqa_decode(const gqa_dims *dims, const uint16_t *q, const gqa_cache *
   g.out = out;
   g.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_gqa_rotate_q(g, s);
-  if (e == hipSuccess) e = launch_plan(a, s);
+  hipError_t e = launch_gqa_rotate_q(g, a, s);  // also plans the split-K items
   if (e == hipSuccess) e = use_mfma ? launch_gqa_splitk_mfma(a, s) : launch_splitk_valu(a, s);
   if (e == hipSuccess) e = launch_gqa_merge_unrotate(g, a, s);
   if (e != hipSuccess) return hip_fail(e, "gqa_decode");

@@ -14,6 +14,7 @@
 // KV head g / G.  Calibration inputs are head-major bf16: q [H_q][n][d],
 // k and v [H_kv][n][d].
 #include "kernels.hpp"
+#include "plan.hpp"
 
 namespace mla {
 namespace {
@@ -129,11 +130,19 @@ constexpr int kHeadChunk = 8;
 // b' = b * H_kv + h per sequence and KV head, rows m = t * G + g):
 //   qbuf[b'][m][c] = scale * log2(e) * sum_n q[b][t][h G + g][n] R_k,apply[h][n][c]
 // and the pseudo-sequences' slots: KV head h's entries are cache slots
-// h * capacity + seq_base[b] ...  Grid (B * H_kv, Tq); thread c < d holds
-// row c of R_apply^T (the rotation's column c) and forms channel c of every
-// query head of the group.
-__global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a) {
+// h * capacity + seq_base[b] ...  Grid (B * H_kv + 1, Tq); thread c < d
+// holds row c of R_apply^T (the rotation's column c) and forms channel c of
+// every query head of the group.  One extra block plans the split-K items
+// from seq_len alongside (each sequence counted once per KV head), which
+// saves a launch.
+__global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a, DecodeArgs sa) {
   __shared__ float qs[kHeadChunk][256];
+  if (blockIdx.x == a.B * a.H_kv) {  // the extra block column: block (B * H_kv, 0) plans the split-K work
+    if (blockIdx.y == 0)
+      plan_block(a.seq_len, sa.B, sa.target_items, sa.tile, sa.min_chunk_tiles, sa.max_items, sa.items,
+                 sa.item_begin, sa.meta, a.H_kv);
+    return;
+  }
   const int bp = blockIdx.x, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, c = threadIdx.x;
   const int G = a.H_q / a.H_kv, d = a.d;
   if (t == 0 && c == 0) {
@@ -180,6 +189,7 @@ __global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a)
 // then thread v forms out[v] = sum_c R_v,apply[v][c] o_z[c] for every row.
 constexpr int kMergeU = 16;
 
+template <int GC>  // query heads per pass: min(G, kHeadChunk) rounded up to a power of two
 __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeArgs a, DecodeArgs sa) {
   extern __shared__ uint16_t rs[];  // [d][d] R_apply^T of head h, then zs [kHeadChunk][256]
   const int bp = blockIdx.x, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, tid = threadIdx.x;
@@ -193,8 +203,8 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeA
   const int ib = sa.item_begin[bp], ie = sa.item_begin[bp + 1];
   const f16 *po = reinterpret_cast<const f16 *>(sa.part_o);
   const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G;  // first output row
-  for (int g0 = 0; g0 < G; g0 += kHeadChunk) {
-    const int ng = min(kHeadChunk, G - g0);
+  for (int g0 = 0; g0 < G; g0 += GC) {
+    const int ng = min(GC, G - g0);
     __syncthreads();  // zs is rewritten
     for (int pr = tid; pr < ng * nch; pr += blockDim.x) {
       const int g = pr / nch, c = pr % nch, m = t * G + g0 + g;
@@ -236,13 +246,19 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeA
     __syncthreads();
     const int v = tid;
     if (v >= d) continue;
-    float acc[kHeadChunk];
+    float acc[GC];
 #pragma unroll
-    for (int g = 0; g < kHeadChunk; ++g) acc[g] = 0.0f;
-    for (int c = 0; c < d; ++c) {
-      const float r = bf16_to_f32(rs[c * d + v]);  // R_v,apply[v][c]
+    for (int g = 0; g < GC; ++g) acc[g] = 0.0f;
+    for (int c = 0; c < d; c += 4) {  // four channels per step: 16-byte reads of the merged rows
+      float r[4];
 #pragma unroll
-      for (int g = 0; g < kHeadChunk; ++g) acc[g] = fmaf(r, zs[g][c], acc[g]);
+      for (int j = 0; j < 4; ++j) r[j] = bf16_to_f32(rs[(c + j) * d + v]);  // R_v,apply[v][c + j]
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        const f32x4 z = *reinterpret_cast<const f32x4 *>(&zs[g][c]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[g] = fmaf(r[j], z[j], acc[g]);
+      }
     }
     for (int g = 0; g < ng; ++g) a.out[(row + g0 + g) * d + v] = acc[g];
   }
@@ -261,11 +277,11 @@ hipError_t launch_gqa_calib_stats(const uint16_t *q, const uint16_t *k, const ui
   return hipGetLastError();
 }
 
-hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, hipStream_t s) {
+hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, const DecodeArgs &sa, hipStream_t s) {
   if (a.d > 256) return hipErrorInvalidValue;
   TimedLaunch tl("gqa_rotate_q", s);
-  const int threads = a.d <= 64 ? 64 : (a.d <= 128 ? 128 : 256);
-  gqa_rotate_q_kernel<<<dim3(a.B * a.H_kv, a.Tq), threads, 0, s>>>(a);
+  // 256 threads: the planner block needs all of them
+  gqa_rotate_q_kernel<<<dim3(a.B * a.H_kv + 1, a.Tq), kThreads, 0, s>>>(a, sa);
   return hipGetLastError();
 }
 
@@ -273,7 +289,16 @@ hipError_t launch_gqa_merge_unrotate(const GqaDecodeArgs &a, const DecodeArgs &s
   if (a.d > 256 || a.d % 4 != 0) return hipErrorInvalidValue;
   TimedLaunch tl("gqa_merge_unrotate", s);
   const size_t lds = static_cast<size_t>(a.d) * a.d * sizeof(uint16_t) + kHeadChunk * 256 * sizeof(float);
-  gqa_merge_unrotate_kernel<<<dim3(a.B * a.H_kv, a.Tq), kThreads, lds, s>>>(a, sa);
+  const dim3 grid(a.B * a.H_kv, a.Tq);
+  const int G = a.H_q / a.H_kv;
+  if (G >= 8)
+    gqa_merge_unrotate_kernel<8><<<grid, kThreads, lds, s>>>(a, sa);
+  else if (G >= 4)
+    gqa_merge_unrotate_kernel<4><<<grid, kThreads, lds, s>>>(a, sa);
+  else if (G >= 2)
+    gqa_merge_unrotate_kernel<2><<<grid, kThreads, lds, s>>>(a, sa);
+  else
+    gqa_merge_unrotate_kernel<1><<<grid, kThreads, lds, s>>>(a, sa);
   return hipGetLastError();
 }
 

@@ -117,7 +117,8 @@ struct GqaDecodeArgs {
   int32_t *len2;                   // [B * H_kv] pseudo-sequence lengths
   float *out, *lse;                // [B][Tq][H_q][d], [B][Tq][H_q]
 };
-hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, hipStream_t s);
+// query rotation, plus the split-K plan of sa (one extra block)
+hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, const DecodeArgs &sa, hipStream_t s);
 // the merge of the split-K partials (sa's items and partials) and the
 // un-rotation in one launch
 hipError_t launch_gqa_merge_unrotate(const GqaDecodeArgs &a, const DecodeArgs &sa, hipStream_t s);

@@ -37,16 +37,18 @@ __device__ inline int plan_items_of(int L, int C, int tile, int *chunk_out) {
   return (L + chunk - 1) / chunk;
 }
 
+// rep > 1: B pseudo-sequences, pseudo-sequence b having the length of
+// sequence b / rep (a sequence's KV heads in grouped-query decode).
 __device__ inline void plan_block(const int32_t *__restrict__ seq_len, int B, int target, int tile,
                                   int min_k, int max_items, WorkItem *__restrict__ items,
-                                  int32_t *__restrict__ item_begin, int32_t *__restrict__ meta) {
+                                  int32_t *__restrict__ item_begin, int32_t *__restrict__ meta, int rep = 1) {
   // called by one whole block of 256 threads
   __shared__ long long wsum[4];
   __shared__ int32_t wne[4], wmax[4], wred[4];
   __shared__ int32_t wtot[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int L0 = tid < B ? seq_len[tid] : 0;
-  auto len_of = [&](int b) -> int { return b < 256 ? L0 : seq_len[b]; };
+  const int L0 = tid < B ? seq_len[tid / rep] : 0;
+  auto len_of = [&](int b) -> int { return b < 256 ? L0 : seq_len[b / rep]; };
   // totals: tokens, non-empty sequences, longest sequence (one barrier pair)
   long long tot = 0;
   int ne = 0, lmax = 0;
