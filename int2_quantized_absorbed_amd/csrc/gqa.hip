@@ -135,6 +135,7 @@ constexpr int kHeadChunk = 8;
 // every query head of the group.  One extra block plans the split-K items
 // from seq_len alongside (each sequence counted once per KV head), which
 // saves a launch.
+template <int DMAX>  // head dim bound: the lane's rotation row is loaded whole, all loads in flight together
 __global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a, DecodeArgs sa) {
   __shared__ float qs[kHeadChunk][256];
   if (blockIdx.x == a.B * a.H_kv) {  // the extra block column: block (B * H_kv, 0) plans the split-K work
@@ -150,7 +151,12 @@ __global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a,
     a.len2[bp] = a.seq_len[b];
   }
   const uint16_t *qbase = a.q + ((static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G) * d;
-  const uint16_t *rrow = a.rk_t + (static_cast<int64_t>(h) * d + min(c, d - 1)) * d;
+  uint4 rw[DMAX / 8];  // row min(c, d-1) of R_apply^T, i.e. column c of the rotation
+  {
+    const uint4 *rrow = reinterpret_cast<const uint4 *>(a.rk_t + (static_cast<int64_t>(h) * d + min(c, d - 1)) * d);
+#pragma unroll
+    for (int i = 0; i < DMAX / 8; ++i) rw[i] = 8 * i < d ? rrow[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
   for (int g0 = 0; g0 < G; g0 += kHeadChunk) {
     const int ng = min(kHeadChunk, G - g0);
     __syncthreads();  // qs is rewritten
@@ -160,21 +166,25 @@ __global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a,
     float acc[kHeadChunk];
 #pragma unroll
     for (int g = 0; g < kHeadChunk; ++g) acc[g] = 0.0f;
-    for (int n = 0; n < d; n += 8) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(rrow + n);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float r0 = __uint_as_float(ww[j] << 16), r1 = __uint_as_float(ww[j] & 0xffff0000u);
+    for (int n = 0; n < DMAX; n += 8) {
+      if (n < d) {  // uniform; rw stays statically indexed
+        const uint4 w = rw[n / 8];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int g = 0; g < kHeadChunk; ++g) {
-          acc[g] = fmaf(r0, qs[g][n + 2 * j], acc[g]);
-          acc[g] = fmaf(r1, qs[g][n + 2 * j + 1], acc[g]);
+        for (int j = 0; j < 4; ++j) {
+          const float r0 = __uint_as_float(ww[j] << 16), r1 = __uint_as_float(ww[j] & 0xffff0000u);
+#pragma unroll
+          for (int g = 0; g < kHeadChunk; ++g) {
+            acc[g] = fmaf(r0, qs[g][n + 2 * j], acc[g]);
+            acc[g] = fmaf(r1, qs[g][n + 2 * j + 1], acc[g]);
+          }
         }
       }
     }
-    for (int g = 0; g < ng; ++g)
-      a.qbuf[((static_cast<int64_t>(bp) * a.Tq + t) * G + g0 + g) * d + c] = acc[g] * a.scale_log2;
+#pragma unroll
+    for (int g = 0; g < kHeadChunk; ++g)
+      if (g < ng) a.qbuf[((static_cast<int64_t>(bp) * a.Tq + t) * G + g0 + g) * d + c] = acc[g] * a.scale_log2;
   }
 }
 
@@ -198,7 +208,16 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeA
   {
     const uint4 *src = reinterpret_cast<const uint4 *>(a.rv_t + static_cast<int64_t>(h) * d * d);
     uint4 *dst = reinterpret_cast<uint4 *>(rs);
-    for (int e = tid; e < d * d / 8; e += blockDim.x) dst[e] = src[e];
+    for (int e0 = 0; e0 < d * d / 8; e0 += 8 * kThreads) {  // eight loads in flight per thread
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = src[min(e0 + j * kThreads + tid, d * d / 8 - 1)];  // clamped: always defined
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = e0 + j * kThreads + tid;
+        if (e < d * d / 8) dst[e] = v[j];
+      }
+    }
   }
   const int ib = sa.item_begin[bp], ie = sa.item_begin[bp + 1];
   const f16 *po = reinterpret_cast<const f16 *>(sa.part_o);
@@ -260,7 +279,9 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeA
         for (int j = 0; j < 4; ++j) acc[g] = fmaf(r[j], z[j], acc[g]);
       }
     }
-    for (int g = 0; g < ng; ++g) a.out[(row + g0 + g) * d + v] = acc[g];
+#pragma unroll
+    for (int g = 0; g < GC; ++g)
+      if (g < ng) a.out[(row + g0 + g) * d + v] = acc[g];
   }
 }
 
@@ -281,7 +302,13 @@ hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, const DecodeArgs &sa, hip
   if (a.d > 256) return hipErrorInvalidValue;
   TimedLaunch tl("gqa_rotate_q", s);
   // 256 threads: the planner block needs all of them
-  gqa_rotate_q_kernel<<<dim3(a.B * a.H_kv + 1, a.Tq), kThreads, 0, s>>>(a, sa);
+  const dim3 grid(a.B * a.H_kv + 1, a.Tq);
+  if (a.d <= 64)
+    gqa_rotate_q_kernel<64><<<grid, kThreads, 0, s>>>(a, sa);
+  else if (a.d <= 128)
+    gqa_rotate_q_kernel<128><<<grid, kThreads, 0, s>>>(a, sa);
+  else
+    gqa_rotate_q_kernel<256><<<grid, kThreads, 0, s>>>(a, sa);
   return hipGetLastError();
 }
 
