@@ -11,13 +11,14 @@
 // Kernels, chosen by input dtype and shape; for bf16 latents the token count
 // only picks between two kernels that give bit-identical results, so one
 // layer always quantises a token the same way:
-//  * append_mfma_kernel: bf16 latents, r in {128, 256, 384, 512}.  The
-//    rotation z^T = R_apply^T c^T is a bf16 MFMA GEMM (32x32x16, fp32
-//    accumulate) with channels as the M dimension: each lane then holds 16
-//    channels of one token, so a 32-channel group is two lanes (one cross-lane
-//    exchange for min/max) and the 2-bit codes of 4 consecutive channels form
-//    one byte in-lane.  The R_apply^T slice (128 channels x r) stays in LDS;
-//    latents stream from HBM straight into MFMA B operands.
+//  * append_staged_kernel: bf16 latents, r in {128, 256, 384, 512}, more
+//    than 1024 tokens.  The rotation z^T = R_apply^T c^T is a bf16 MFMA GEMM
+//    (32x32x16, fp32 accumulate) with channels as the M dimension: each lane
+//    then holds 16 channels of one token, so a 32-channel group is two lanes
+//    (one cross-lane exchange for min/max) and the 2-bit codes of 4
+//    consecutive channels form one byte in-lane.  The R_apply^T slice (128
+//    channels x r) stays in LDS; latents arrive with coalesced loads and pass
+//    through a per-wave LDS buffer into the MFMA B operands.
 //  * append_skinny_kernel: the same shapes for appends of at most 1024 tokens
 //    (a decode step's new tokens): one wave per 32-channel x 32-token tile,
 //    operands straight from memory, the same MFMA sequence per accumulator.
@@ -157,15 +158,9 @@ __global__ __launch_bounds__(1024) void append_valu_kernel(AppendParams p) {
 // ---------------------------------------------------------------------------
 // MFMA path
 // ---------------------------------------------------------------------------
-constexpr int kSlice = 128;       // channels per block (4 M-tiles of 32)
-constexpr int kWaves = 8;         // two waves per SIMD
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTokPerWave = 32;   // one N-tile of 32 tokens
-constexpr int kTokPerBlock = kWaves * kTokPerWave;
+constexpr int kSlice = 128;             // channels per block of the staged kernel (4 M-tiles of 32)
+constexpr int kTokPerBlock = 256;       // tokens per block of the staged kernel
 constexpr int kSkinnyMaxTokens = 1024;  // appends of at most this many tokens use append_skinny_kernel
-
-template <int R>
-constexpr int lds_stride() { return R + 8; }  // +16 B per row: rows rotate banks
 
 // Epilogue of one 32-channel x 32-token rotation tile in MFMA C layout (lane
 // l holds channels ch0 + 8q + 4hf + s, v = 4q + s, of token tok): the fp32
@@ -199,28 +194,35 @@ __device__ __forceinline__ void tile_epilogue(const AppendParams &p, const f32x1
     mn = fminf(mn, __shfl_xor(mn, 32));
     qp[g] = quant_params(mx, mn, alpha[g]);
   }
-  // quotient estimates for all 16 values; the exact division runs only
-  // when some value of the wave lies next to a code boundary
-  float xs[16], us[16];
-  bool near = false;
+  // quotient estimates u for all 16 values and their nearest integers; the
+  // exact division runs only where some estimate of this lane lies within
+  // 2e-6 of a half-integer (a code boundary, or one the clamp makes
+  // harmless).  A NaN or infinite estimate gives the same code either way.
+  float xs[16], rs[16];
+  float dmin = 1.0f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const QuantParams &qq = qp[v / VPG];
     xs[v] = __fsub_rn(z[v], qq.zero_f);
-    us[v] = quant_u_estimate(xs[v], qq);
-    near |= qq.scale_f != 0.0f && quant_u_near_boundary(us[v]);
+    const float u = quant_u_estimate(xs[v], qq);
+    rs[v] = rintf(u);
+    dmin = fminf(dmin, 0.5f - fabsf(u - rs[v]));
   }
-  if (near) {
+  if (!(dmin > 2e-6f)) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (quant_u_near_boundary(us[v])) us[v] = __fdiv_rn(xs[v], qp[v / VPG].scale_f);
+    for (int v = 0; v < 16; ++v) {
+      const QuantParams &qq = qp[v / VPG];
+      const float u = quant_u_estimate(xs[v], qq);
+      if (!(0.5f - fabsf(u - rs[v]) > 2e-6f)) rs[v] = rintf(__fdiv_rn(xs[v], qq.scale_f));
+    }
   }
   uint32_t dword = 0;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const uint32_t code = qp[v / VPG].scale_f == 0.0f ? 0u : quant_code_from_u(us[v]);
-    dword |= code << (2 * v);
-  }
+  for (int v = 0; v < 16; ++v) dword |= static_cast<uint32_t>(fminf(fmaxf(rs[v], 0.0f), 3.0f)) << (2 * v);
+  // a group with scale 0 (all values equal) gets code 0 throughout
+#pragma unroll
+  for (int g = 0; g < NGT; ++g)
+    if (qp[g].scale_f == 0.0f) dword &= VPG == 16 ? 0u : ~(0xffffu << (16 * g));
   // lane hf=0 holds bytes 0,2,4,6 of the tile's 8 code bytes, hf=1 holds 1,3,5,7
   const uint32_t partner = __shfl_xor(dword, 32);
   const uint32_t packed = __builtin_amdgcn_perm(partner, dword, hf ? 0x03070206u : 0x05010400u);
@@ -233,20 +235,59 @@ __device__ __forceinline__ void tile_epilogue(const AppendParams &p, const f32x1
         reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G] = sz;
       }
     } else {
-      const QuantParams &qh = qp[hf & (NGT - 1)];
-      const uint32_t sz = static_cast<uint32_t>(f16_bits(qh.scale)) |
-                          (static_cast<uint32_t>(f16_bits(qh.zero)) << 16);
+      // lane half hf stores group hf's side info (selects, not a lane-indexed array)
+      const uint32_t sz0 = static_cast<uint32_t>(f16_bits(qp[0].scale)) |
+                           (static_cast<uint32_t>(f16_bits(qp[0].zero)) << 16);
+      const uint32_t sz1 = static_cast<uint32_t>(f16_bits(qp[NGT - 1].scale)) |
+                           (static_cast<uint32_t>(f16_bits(qp[NGT - 1].zero)) << 16);
+      const uint32_t sz = hf ? sz1 : sz0;
       reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G + hf] = sz;
     }
   }
 }
 
-template <int R, int G, int NACC>
-__global__ __launch_bounds__(kThreads) void append_mfma_kernel(AppendParams p, int n_logical) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t rt_s[];
-  constexpr int KS = R / 16;
-  constexpr int NSLICE = R / kSlice;
-  constexpr int LS = lds_stride<R>();
+// Appends of more than kSkinnyMaxTokens tokens.  A block owns one 128-channel
+// slice of R_apply^T, which stays in LDS for the whole block, and kTokPerBlock
+// tokens.  Each of its WAVES waves owns 32 * NT tokens and computes all four
+// 32-channel M-tiles of the slice for its NT token tiles, so an A operand
+// read from LDS feeds NT products.  Latents reach the MFMA B operands through
+// a per-wave LDS buffer, one K-chunk (64 values, 128 bytes of a token row) at
+// a time: a chunk is fetched with fully coalesced 16-byte loads (8 lanes per
+// token row), PF chunks ahead of the one being multiplied, and read back in
+// operand order.  Both LDS regions are XOR-swizzled rather than padded, so
+// the 16-byte operand reads of 16 consecutive lanes hit 64 distinct banks.
+// Accumulation order per output: K-steps in order into even/odd partial sums
+// added at the end, the same as append_skinny_kernel.
+template <int R, int WAVES, int NT>
+struct StagedCfg {
+  static constexpr int KS = R / 16;           // MFMA K-steps
+  static constexpr int KC = 4;                // K-steps per staged chunk
+  static constexpr int NCH = KS / KC;         // chunks per token row
+  static constexpr int TOKW = 32 * NT;        // tokens per wave
+  static constexpr int NLD = TOKW / 8;        // 16-byte loads per lane per chunk
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr size_t RT_BYTES = static_cast<size_t>(kSlice) * R * 2;
+  static constexpr size_t LDS = RT_BYTES + static_cast<size_t>(WAVES) * TOKW * 128;
+  static_assert(WAVES * TOKW == kTokPerBlock, "a block covers one token tile");
+};
+
+// element offset of 16-byte chunk c of row `row` in the swizzled R_apply^T slice
+template <int R>
+__device__ __forceinline__ int rt_off(int row, int c) {
+  return row * R + ((c ^ (row & 15)) << 3);
+}
+// byte offset of 16-byte piece j (0..7) of token t's row in a wave's chunk buffer
+__device__ __forceinline__ int lat_off(int t, int j) {
+  return t * 128 + ((j ^ ((t >> 1) & 7)) << 4);
+}
+
+template <int R, int G, int WAVES, int NT, int PF>
+__global__ __launch_bounds__(64 * WAVES) void append_staged_kernel(AppendParams p,
+                                                                                        int n_logical) {
+  using C = StagedCfg<R, WAVES, NT>;
+  constexpr int KS = C::KS, KC = C::KC, NCH = C::NCH, TOKW = C::TOKW, NLD = C::NLD, NSLICE = R / kSlice;
+  static_assert(PF >= 1 && PF <= NCH, "prefetch depth within the row");
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   // XCD-aware order: blocks b, b + 8, ... run on one XCD (one L2); give them
   // consecutive logical indices, so the NSLICE channel-slice blocks of a
   // token tile read its latents through the same L2
@@ -257,95 +298,50 @@ __global__ __launch_bounds__(kThreads) void append_mfma_kernel(AppendParams p, i
   const int tb = logical / NSLICE;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, hf = l >> 5, l32 = l & 31;
+  uint16_t *rt_s = smem;
+  uint8_t *lat_s = reinterpret_cast<uint8_t *>(smem) + C::RT_BYTES + static_cast<size_t>(w) * TOKW * 128;
+  const int64_t wave_tok0 = static_cast<int64_t>(tb) * kTokPerBlock + w * TOKW;
+  const uint16_t *lat = static_cast<const uint16_t *>(p.latent);
 
-  // this wave's 32 tokens; lanes of tokens past the end read token 0's row
-  // (their output columns are never stored), so every load is unconditional
-  const int64_t wave_tok0 = static_cast<int64_t>(tb) * kTokPerBlock + w * kTokPerWave;
-  const int64_t tok = wave_tok0 + l32;
-  const bool valid = tok < p.n;
-  const bf16x8 *brow = reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(p.latent) + (valid ? tok : 0) * p.lat_stride);
+  // chunk loads: load i of a chunk brings 16 bytes (piece l & 7) of the
+  // chunk's 128 bytes of token wave_tok0 + 8i + (l >> 3); tokens past the end
+  // read the last token's row (their outputs are never stored)
+  const uint16_t *rowp[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int64_t t = min<int64_t>(wave_tok0 + 8 * i + (l >> 3), p.n - 1);
+    rowp[i] = lat + t * p.lat_stride + (l & 7) * 8;
+  }
+  uint4 buf[PF][NLD];
+#pragma unroll
+  for (int c = 0; c < PF; ++c)
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) buf[c][i] = *reinterpret_cast<const uint4 *>(rowp[i] + c * 64);
+
   // epilogue inputs, fetched now so their latency hides under the GEMM
   constexpr int NGT = 32 / G;  // groups per M-tile: 1 (G=32) or 2 (G=16)
-  int64_t slot = -1;
+  int64_t slot[NT];
   float alpha_of[4][NGT] = {};  // (the rotation-only launch, z_out != nullptr, has no alpha)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) slot[nt] = -1;
   if (p.z_out == nullptr) {
-    if (valid) slot = p.slots[tok];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t tok = wave_tok0 + nt * 32 + l32;
+      if (tok < p.n) slot[nt] = p.slots[tok];
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int g = 0; g < NGT; ++g) alpha_of[mt][g] = p.alpha[(cs * kSlice + mt * 32) / G + g];
   }
-  const bool live = wave_tok0 < p.n;  // a wave with no token in range skips the products
 
-  f32x16 acc[NACC][4];
-#pragma unroll
-  for (int a = 0; a < NACC; ++a)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[a][mt] = f32x16{};
-
-  // latent operands stream from HBM in chunks of PD K-steps, double-buffered:
-  // chunk c + 1 is in flight while chunk c is multiplied
-  constexpr int PD = 8;
-  static_assert(KS % PD == 0, "K-steps come in whole chunks");
-  bf16x8 bq[2][PD];
-#pragma unroll
-  for (int j = 0; j < PD; ++j) bq[0][j] = brow[2 * j + hf];
-  // stage R_apply^T rows [cs*128, +128) into LDS (16-byte chunks, several
-  // loads in flight per thread) while the first latent chunk is in flight
-  {
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.Rt + static_cast<int64_t>(cs) * kSlice * R);
-    constexpr int CPR = R / 8;  // chunks per row
-    constexpr int TOTAL = kSlice * CPR;
-    constexpr int SU = TOTAL % (kThreads * 16) == 0 ? 16 : (TOTAL % (kThreads * 8) == 0 ? 8 : 4);
-    static_assert(TOTAL % (kThreads * SU) == 0, "staging loop has no tail");
-    for (int e0 = tid; e0 < TOTAL; e0 += kThreads * SU) {
-      uint4 v[SU];
-#pragma unroll
-      for (int j = 0; j < SU; ++j) v[j] = src[e0 + kThreads * j];
-#pragma unroll
-      for (int j = 0; j < SU; ++j) {
-        const int e = e0 + kThreads * j, row = e / CPR, c = e % CPR;
-        *reinterpret_cast<uint4 *>(rt_s + row * LS + c * 8) = v[j];
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < KS / PD; ++c) {
-    if (!live) break;
-    const int cur = c & 1;
-    if (c + 1 < KS / PD) {
-#pragma unroll
-      for (int j = 0; j < PD; ++j) bq[cur ^ 1][j] = brow[2 * ((c + 1) * PD + j) + hf];
-    }
-#pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int ks = c * PD + j;
-      bf16x8 a[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        a[mt] = *reinterpret_cast<const bf16x8 *>(rt_s + (mt * 32 + l32) * LS + ks * 16 + hf * 8);
-      const int par = ks % NACC;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[par][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], bq[cur][j], acc[par][mt], 0, 0, 0);
-    }
-  }
-
-  // epilogue: lane holds channels 32mt + 8q + 4hf + s (v = 4q + s) of token tok
-  const bool write = valid && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    f32x16 z = acc[0][mt];
-#pragma unroll
-    for (int a = 1; a < NACC; ++a) z += acc[a][mt];
-    tile_epilogue<R, G>(p, z, tok, write, slot, cs * kSlice + mt * 32, alpha_of[mt], hf);
-  }
-  // side keys: channel-slice block cs copies its share of this 256-token
-  // tile (ceil(256 / NSLICE) tokens), an eighth of that per wave, every lane
+  // side keys first (their loads and stores overlap the prologue):
+  // channel-slice block cs copies its share of this token tile
+  // (ceil(kTokPerBlock / NSLICE) tokens), split over the waves, every lane
   // moving 16-byte pieces
   if (p.z_out == nullptr) {
-    constexpr int PB = (kTokPerBlock + NSLICE - 1) / NSLICE, PW = (PB + kWaves - 1) / kWaves;
+    constexpr int PB = (kTokPerBlock + NSLICE - 1) / NSLICE, PW = (PB + WAVES - 1) / WAVES;
     const int64_t tile_end = min<int64_t>(static_cast<int64_t>(tb + 1) * kTokPerBlock, p.n);
     const int64_t t0 = static_cast<int64_t>(tb) * kTokPerBlock + cs * PB + w * PW;
     const int64_t t1 = min<int64_t>(min<int64_t>(t0 + PW, static_cast<int64_t>(tb) * kTokPerBlock + (cs + 1) * PB), tile_end);
@@ -355,18 +351,156 @@ __global__ __launch_bounds__(kThreads) void append_mfma_kernel(AppendParams p, i
       if (p.d_idx > 0) copy_side_keys(p.cache.idx_key, p.idx_key, p.d_idx, p.slots, t0, cnt, p.cache.capacity, l);
     }
   }
+
+  // stage R_apply^T rows [cs*128, +128) into LDS, 16 loads in flight per thread
+  {
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.Rt + static_cast<int64_t>(cs) * kSlice * R);
+    constexpr int CPR = R / 8;  // 16-byte chunks per row
+    constexpr int TOTAL = kSlice * CPR;
+    constexpr int PER = TOTAL / C::THREADS;  // chunks per thread
+    constexpr int SU = PER % 16 == 0 ? 16 : (PER % 8 == 0 ? 8 : (PER % 4 == 0 ? 4 : 1));
+    static_assert(TOTAL % (C::THREADS * SU) == 0, "staging loop has no tail");
+    for (int e0 = tid; e0 < TOTAL; e0 += C::THREADS * SU) {
+      uint4 v[SU];
+#pragma unroll
+      for (int j = 0; j < SU; ++j) v[j] = src[e0 + C::THREADS * j];
+#pragma unroll
+      for (int j = 0; j < SU; ++j) {
+        const int e = e0 + C::THREADS * j;
+        *reinterpret_cast<uint4 *>(rt_s + rt_off<R>(e / CPR, e % CPR)) = v[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  f32x16 acc[2][4][NT];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[a][mt][nt] = f32x16{};
+
+  // a wave with no token in range skips the products
+  if (wave_tok0 < p.n) {
+    // A chunk goes registers -> this wave's LDS buffer, then the chunk PF
+    // places further on is requested into the freed registers (the chunks in
+    // flight move down one slot, so every register index is static).  LDS
+    // instructions of one wave execute in order: a chunk's writes land after
+    // the previous chunk's operand reads, and its operand reads after its
+    // writes; the wave barriers only keep the compiler from moving LDS
+    // accesses across them.  Software pipeline: the operands of a K-step are
+    // requested before the products of the previous K-step issue (scheduling
+    // fences keep that order), so LDS latency hides under the MFMAs.
+    bf16x8 opa0[4], opb0[NT], opa1[4], opb1[NT];  // even / odd K-step operands
+    static_assert(KC % 2 == 0, "K-steps come in even/odd pairs within a chunk");
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) {
+      if (ks == 0) {
+        // chunk 0: registers -> LDS, chunk PF requested into the freed
+        // registers, then the operands of K-step 0
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          *reinterpret_cast<uint4 *>(lat_s + lat_off(8 * i + (l >> 3), l & 7)) = buf[0][i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int f = 0; f + 1 < PF; ++f)
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) buf[f][i] = buf[f + 1][i];
+        if (PF < NCH) {
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) buf[PF - 1][i] = *reinterpret_cast<const uint4 *>(rowp[i] + PF * 64);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          opa0[mt] = *reinterpret_cast<const bf16x8 *>(rt_s + rt_off<R>(mt * 32 + l32, hf));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          opb0[nt] = *reinterpret_cast<const bf16x8 *>(lat_s + lat_off(nt * 32 + l32, hf));
+      }
+      // odd K-step ks + 1 (same chunk)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        opa1[mt] = *reinterpret_cast<const bf16x8 *>(rt_s + rt_off<R>(mt * 32 + l32, 2 * (ks + 1) + hf));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        opb1[nt] = *reinterpret_cast<const bf16x8 *>(lat_s + lat_off(nt * 32 + l32, 2 * ((ks + 1) % KC) + hf));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[0][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa0[mt], opb0[nt], acc[0][mt][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // even K-step ks + 2, unless it starts a new chunk (then it is read
+      // right after that chunk is staged)
+      if (ks + 2 < KS && (ks + 2) % KC != 0) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          opa0[mt] = *reinterpret_cast<const bf16x8 *>(rt_s + rt_off<R>(mt * 32 + l32, 2 * (ks + 2) + hf));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          opb0[nt] = *reinterpret_cast<const bf16x8 *>(lat_s + lat_off(nt * 32 + l32, 2 * ((ks + 2) % KC) + hf));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[1][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa1[mt], opb1[nt], acc[1][mt][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 2 < KS && (ks + 2) % KC == 0) {
+        // the next chunk's first K-step: stage it now, then read its operands
+        // while the odd products above run
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          *reinterpret_cast<uint4 *>(lat_s + lat_off(8 * i + (l >> 3), l & 7)) = buf[0][i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int f = 0; f + 1 < PF; ++f)
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) buf[f][i] = buf[f + 1][i];
+        if ((ks + 2) / KC + PF < NCH) {
+#pragma unroll
+          for (int i = 0; i < NLD; ++i)
+            buf[PF - 1][i] = *reinterpret_cast<const uint4 *>(rowp[i] + ((ks + 2) / KC + PF) * 64);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          opa0[mt] = *reinterpret_cast<const bf16x8 *>(rt_s + rt_off<R>(mt * 32 + l32, 2 * (ks + 2) + hf));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          opb0[nt] = *reinterpret_cast<const bf16x8 *>(lat_s + lat_off(nt * 32 + l32, hf));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // epilogue: lane holds channels 32mt + 8q + 4hf + s (v = 4q + s) of token
+  // wave_tok0 + 32nt + l32
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t tok = wave_tok0 + nt * 32 + l32;
+    const bool write = tok < p.n && (p.z_out != nullptr || (slot[nt] >= 0 && slot[nt] < p.cache.capacity));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x16 z = acc[0][mt][nt] + acc[1][mt][nt];
+      tile_epilogue<R, G>(p, z, tok, write, slot[nt], cs * kSlice + mt * 32, alpha_of[mt], hf);
+    }
+  }
 }
 
 // Small appends (a decode step's few new tokens): one wave per (32-channel
 // tile, 32-token tile).  R_apply^T rows and latents go straight from memory
-// into the MFMA operands (8 K-steps per double-buffered chunk), and every
-// accumulator sees the same MFMA sequence as in append_mfma_kernel (K-steps
+// into the MFMA operands, all K-steps requested at once, and every
+// accumulator sees the same MFMA sequence as in append_staged_kernel (K-steps
 // in order, even/odd partial sums added at the end), so a token gets
 // bit-identical codes whichever kernel appends it.
 template <int R, int G, int NACC>
 __global__ __launch_bounds__(64) void append_skinny_kernel(AppendParams p) {
-  constexpr int KS = R / 16, PD = 8;
-  static_assert(KS % PD == 0, "K-steps come in whole chunks");
+  constexpr int KS = R / 16;
   constexpr int NGT = 32 / G;
   const int ct = blockIdx.x;  // channels [32 ct, 32 ct + 32)
   const int l = threadIdx.x, hf = l >> 5, l32 = l & 31;
@@ -382,33 +516,22 @@ __global__ __launch_bounds__(64) void append_skinny_kernel(AppendParams p) {
 #pragma unroll
     for (int g = 0; g < NGT; ++g) alpha[g] = p.alpha[(32 * ct) / G + g];
   }
-  // lanes of tokens past the end read token 0's row (their columns are never
-  // stored), so the loads carry no branches
-  bf16x8 aq[2][PD], bq[2][PD];
+  // every operand of the tile is requested at once (one memory round trip;
+  // at most 2 x 32 loads per lane); lanes of tokens past the end read token
+  // 0's row (their columns are never stored), so the loads carry no branches
+  bf16x8 aq[KS], bq[KS];
 #pragma unroll
-  for (int j = 0; j < PD; ++j) {
-    aq[0][j] = arow[2 * j + hf];
-    bq[0][j] = brow[2 * j + hf];
+  for (int ks = 0; ks < KS; ++ks) {
+    aq[ks] = arow[2 * ks + hf];
+    bq[ks] = brow[2 * ks + hf];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
   f32x16 acc[NACC];
 #pragma unroll
   for (int a = 0; a < NACC; ++a) acc[a] = f32x16{};
 #pragma unroll
-  for (int c = 0; c < KS / PD; ++c) {
-    const int cur = c & 1;
-    if (c + 1 < KS / PD) {
-#pragma unroll
-      for (int j = 0; j < PD; ++j) {
-        aq[cur ^ 1][j] = arow[2 * ((c + 1) * PD + j) + hf];
-        bq[cur ^ 1][j] = brow[2 * ((c + 1) * PD + j) + hf];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int ks = c * PD + j;
-      acc[ks % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[cur][j], bq[cur][j], acc[ks % NACC], 0, 0, 0);
-    }
-  }
+  for (int ks = 0; ks < KS; ++ks)
+    acc[ks % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], bq[ks], acc[ks % NACC], 0, 0, 0);
   f32x16 z = acc[0];
 #pragma unroll
   for (int a = 1; a < NACC; ++a) z += acc[a];
@@ -423,6 +546,25 @@ __global__ __launch_bounds__(64) void append_skinny_kernel(AppendParams p) {
   }
 }
 
+template <int R, int G, int WAVES, int NT, int PF>
+hipError_t launch_staged(const AppendParams &p, hipStream_t s) {
+  using C = StagedCfg<R, WAVES, NT>;
+  constexpr int PFC = PF < C::NCH ? PF : C::NCH;
+  const void *fn = reinterpret_cast<const void *>(&append_staged_kernel<R, G, WAVES, NT, PFC>);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(C::LDS));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t blocks = ((p.n + kTokPerBlock - 1) / kTokPerBlock) * (R / kSlice);
+  if (blocks > (int64_t{1} << 30)) return hipErrorInvalidValue;
+  const int64_t grid = (blocks + 7) / 8 * 8;  // a multiple of 8 (XCD-aware order)
+  append_staged_kernel<R, G, WAVES, NT, PFC>
+      <<<static_cast<unsigned>(grid), C::THREADS, C::LDS, s>>>(p, static_cast<int>(blocks));
+  return hipGetLastError();
+}
+
 template <int R, int G>
 hipError_t launch_mfma_rg(const AppendParams &p, hipStream_t s) {
   constexpr int NACC = 2;
@@ -431,19 +573,8 @@ hipError_t launch_mfma_rg(const AppendParams &p, hipStream_t s) {
     append_skinny_kernel<R, G, NACC><<<grid, 64, 0, s>>>(p);
     return hipGetLastError();
   }
-  const size_t lds = static_cast<size_t>(kSlice) * lds_stride<R>() * sizeof(uint16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&append_mfma_kernel<R, G, NACC>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int64_t blocks = ((p.n + kTokPerBlock - 1) / kTokPerBlock) * (R / kSlice);
-  if (blocks > (int64_t{1} << 30)) return hipErrorInvalidValue;
-  const int64_t grid = (blocks + 7) / 8 * 8;  // a multiple of 8 (XCD-aware order)
-  append_mfma_kernel<R, G, NACC><<<static_cast<unsigned>(grid), kThreads, lds, s>>>(p, static_cast<int>(blocks));
-  return hipGetLastError();
+  // eight waves (two per SIMD), one 32-token tile each, three chunks in flight
+  return launch_staged<R, G, 8, 1, 3>(p, s);
 }
 
 template <int R>
