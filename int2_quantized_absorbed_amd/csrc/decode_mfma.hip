@@ -490,6 +490,10 @@ constexpr int QTSTRIDE = 136;  // halves per staged row (128 channels + pad)
 
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_count) {
   __shared__ __align__(16) f16 qt[32 * QTSTRIDE];
+  // the quarter's 128 W~_UK rows, 128 values of the contraction at a time;
+  // 16-byte piece p of row j sits at piece p ^ (j & 15) (conflict-free
+  // operand reads by 16 consecutive lanes)
+  __shared__ __align__(16) u32x4 wk[128 * 16];
   const int H = a.d.num_heads, dn = a.d.qk_nope_head_dim;
   // the extra first block column: block (0, 0) plans the split-K work in
   // parallel with the absorb blocks (and is dispatched first), the rest of
@@ -508,30 +512,46 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_c
   const int q = rt * 32 + l32;
   const bool q_ok = q < nrows;
   const uint16_t *arow = a.q_nope + (static_cast<int64_t>(q_ok ? q : 0) * H + h) * dn;
-  const int j = 128 * cq + 32 * w + l32;  // this lane's B column = latent channel
-  const uint16_t *brow = a.w_uk_f + (static_cast<int64_t>(h) * R + j) * dn;
+  // coalesced weight rows: thread tid moves piece tid & 15 of rows (tid >> 4) + 16i
+  const uint16_t *wbase = a.w_uk_f + (static_cast<int64_t>(h) * R + 128 * cq) * dn;
+  const int wp = tid & 15, wr0 = tid >> 4;
+  const int brow = 32 * w + l32;  // this lane's B column = latent channel 128cq + brow
   f32x16 acc = {};
   for (int k0 = 0; k0 < dn; k0 += 128) {
-    uint4 raw[8];
-    f16x8 bv[8];
+    const int kc = min(128, dn - k0);  // a multiple of 16
+    u32x4 wv[8];
+    u32x4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      wv[i] = *reinterpret_cast<const u32x4 *>(wbase + static_cast<int64_t>(wr0 + 16 * i) * dn + k0 + 8 * min(wp, kc / 8 - 1));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int kk = min(k0 + 16 * e, dn - 16) + 8 * hf;
-      raw[e] = *reinterpret_cast<const uint4 *>(arow + kk);  // row 0 stands in for q >= nrows
-      bv[e] = *reinterpret_cast<const f16x8 *>(brow + kk);
+      const int kk = k0 + min(16 * e, kc - 16) + 8 * hf;
+      raw[e] = *reinterpret_cast<const u32x4 *>(arow + kk);  // row 0 stands in for q >= nrows
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
+    if (k0 > 0) __syncthreads();  // the previous chunk's operand reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = wr0 + 16 * i;
+      wk[j * 16 + (wp ^ (j & 15))] = wv[i];
+    }
+    __syncthreads();
+    // K-steps past the chunk (kc < 128) repeat its last step with a zero
+    // query operand, so every step reads written, finite weights
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (k0 + 16 * e >= dn) break;
-      const uint32_t rr[4] = {raw[e].x, raw[e].y, raw[e].z, raw[e].w};
+      const int ee = min(e, kc / 16 - 1);
+      const bool use = q_ok && e == ee;
+      const u32x4 bw = wk[brow * 16 + ((2 * ee + hf) ^ (brow & 15))];
+      const f16x8 bv = __builtin_bit_cast(f16x8, bw);
+      const u32x4 rr = raw[e];
       f16x8 av;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        av[2 * j] = q_ok ? static_cast<f16>(__uint_as_float(rr[j] << 16)) : f16(0.0f);
-        av[2 * j + 1] = q_ok ? static_cast<f16>(__uint_as_float(rr[j] & 0xffff0000u)) : f16(0.0f);
+        av[2 * j] = use ? static_cast<f16>(__uint_as_float(rr[j] << 16)) : f16(0.0f);
+        av[2 * j + 1] = use ? static_cast<f16>(__uint_as_float(rr[j] & 0xffff0000u)) : f16(0.0f);
       }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv[e], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
     }
   }
   // C layout: column = channel 32w + l32 of the quarter, rows 8(v/4) + 4hf + v%4
