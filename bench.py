@@ -177,9 +177,12 @@ def main():
     del lat
 
     def step(k):
+        # one decode step: the new tokens are quantised into the cache, then
+        # every query attends over it (one call; the small append runs in
+        # the query-absorb launch)
         c = caches[k % len(caches)]
-        M.mla_append_quant(d, step_lat, step_kr, step_idx, step_slots, Rt, alpha, c)
-        M.mla_decode_absorbed(d, qn, qr, uk_f, uv_f, c, seq_base, seq_len, tq, w.causal, scale, ws, out, lse)
+        M.mla_decode_step(d, step_lat, step_kr, step_idx, step_slots, Rt, alpha, qn, qr, uk_f, uv_f, c, seq_base,
+                          seq_len, tq, w.causal, scale, ws, out, lse)
 
     for k in range(args.warmup):
         step(k)
@@ -199,7 +202,8 @@ def main():
         step(k)
     torch.cuda.synchronize()
     kernels = {}
-    for name in ("append_quant", "decode_plan", "absorb_q", "splitk_decode", "combine", "up_proj", "combine_up_proj"):
+    for name in ("append_quant", "append_absorb_q", "decode_plan", "absorb_q", "splitk_decode", "combine", "up_proj",
+                 "combine_up_proj"):
         ms, n = M.mla_timing_query(name)
         if n:
             kernels[name] = round(ms / n * 1e3, 3)

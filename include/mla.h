@@ -257,6 +257,34 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope,
                                void *stream);
 
 /* ------------------------------------------------------------------------
+ * mla_decode_step — one decode step: quantise-on-append of the step's new
+ * tokens, then absorbed decode over the cache that now holds them
+ * [OSCAR-MLA; SHARD-MLA absorb form]
+ *
+ * The result (cache bytes, out, lse) is exactly that of mla_append_quant(dims,
+ * latent, dtype, k_rope, idx_key, slot_mapping, n, R_apply_t, alpha, cache)
+ * followed by mla_decode_absorbed(dims, q_nope, ..., lse) on the same stream;
+ * the arguments mean what they mean there.  When the decode takes its MFMA
+ * path and the append is small (bf16 latents, kv_lora_rank 512, n <= 1024)
+ * the append runs in the query-absorb launch, next to the absorb blocks;
+ * otherwise the two run one after the other.  n == 0 skips the append;
+ * batch == 0 skips the decode.  All arguments are checked before anything
+ * is launched.  Asynchronous.
+ * ---------------------------------------------------------------------- */
+mla_status mla_decode_step(const mla_dims *dims, const void *latent,
+                           mla_dtype dtype, const uint16_t *k_rope,
+                           const uint16_t *idx_key,
+                           const int64_t *slot_mapping, int64_t n,
+                           const uint16_t *R_apply_t, const float *alpha,
+                           const uint16_t *q_nope, const uint16_t *q_rope,
+                           const uint16_t *w_uk_f, const uint16_t *w_uv_f,
+                           const mla_cache *cache, const int64_t *seq_base,
+                           const int32_t *seq_len, int32_t batch, int32_t tq,
+                           int32_t causal, float softmax_scale,
+                           void *workspace, size_t workspace_bytes,
+                           float *out, float *lse, void *stream);
+
+/* ------------------------------------------------------------------------
  * Sparse decode through the cached indexer key
  * [LLMH-SIZE: GLM-5.3-Flash's latent layers carry a sparse-attention indexer
  * and cache its key]

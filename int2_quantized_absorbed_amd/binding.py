@@ -67,6 +67,10 @@ _SIGS = {
     "mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, _P, _P, _P, ctypes.POINTER(mla_cache),
                                            _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                            _P, ctypes.c_size_t, _P, _P, _P]),
+    "mla_decode_step": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, ctypes.c_int, _P, _P, _P, ctypes.c_int64,
+                                       _P, _P, _P, _P, _P, _P, ctypes.POINTER(mla_cache), _P, _P, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, ctypes.c_size_t, _P, _P,
+                                       _P]),
     "mla_index_topk_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(mla_dims), ctypes.c_int32, ctypes.c_int64]),
     "mla_index_topk": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, ctypes.POINTER(mla_cache), _P, _P,
                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P, _P, _P]),
@@ -366,6 +370,50 @@ def mla_decode_absorbed(dims: Dims, q_nope, q_rope, w_uk_f, w_uv_f, cache: Cache
                                    float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
                                    _stream())
     _check(st, "mla_decode_absorbed")
+    return out, lse
+
+
+def mla_decode_step(dims: Dims, latent, k_rope, idx_key, slot_mapping, R_apply_t, alpha, q_nope, q_rope, w_uk_f,
+                    w_uv_f, cache: Cache, seq_base, seq_len, tq: int, causal: bool, softmax_scale: float,
+                    workspace=None, out=None, lse=None):
+    """mla_append_quant of the step's new tokens, then mla_decode_absorbed over
+    the cache that holds them, in one call; returns (out, lse)."""
+    H, r = dims.num_heads, dims.kv_lora_rank
+    B = seq_len.shape[0]
+    dev = q_nope.device
+    _need(latent, "latent", (torch.bfloat16, torch.float32))
+    n = latent.shape[0]
+    if latent.dim() != 2 or latent.shape[1] != r:
+        raise ValueError("latent must be [n, kv_lora_rank]")
+    _need(k_rope, "k_rope", torch.bfloat16, (n, dims.qk_rope_head_dim))
+    if dims.index_head_dim:
+        _need(idx_key, "idx_key", torch.bfloat16, (n, dims.index_head_dim))
+    _need(slot_mapping, "slot_mapping", torch.int64, (n,))
+    _need(R_apply_t, "R_apply_t", torch.bfloat16, (r, r))
+    _need(alpha, "alpha", torch.float32, (dims.n_groups,))
+    _need(q_nope, "q_nope", torch.bfloat16, (B, tq, H, dims.qk_nope_head_dim))
+    _need(q_rope, "q_rope", torch.bfloat16, (B, tq, H, dims.qk_rope_head_dim))
+    _need(w_uk_f, "w_uk_f", torch.float16, (H, r, dims.qk_nope_head_dim))
+    _need(w_uv_f, "w_uv_f", torch.float16, (H, dims.v_head_dim, r))
+    _need(seq_base, "seq_base", torch.int64, (B,))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    need = mla_decode_workspace_size(dims, B, tq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((B, tq, H, dims.v_head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, tq, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, tq, H, dims.v_head_dim))
+    _need(lse, "lse", torch.float32, (B, tq, H))
+    d, c = dims.c(), cache.c()
+    st = lib().mla_decode_step(ctypes.byref(d), _ptr(latent), _dtype_code(latent), _ptr(k_rope), _ptr(idx_key),
+                               _ptr(slot_mapping), n, _ptr(R_apply_t), _ptr(alpha), _ptr(q_nope), _ptr(q_rope),
+                               _ptr(w_uk_f), _ptr(w_uv_f), ctypes.byref(c), _ptr(seq_base), _ptr(seq_len), B, tq,
+                               int(bool(causal)), float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out),
+                               _ptr(lse), _stream())
+    _check(st, "mla_decode_step")
     return out, lse
 
 

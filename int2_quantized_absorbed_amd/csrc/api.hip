@@ -533,35 +533,53 @@ mla_status mla_fold_absorb_weights(const mla_dims *dims, const uint16_t *w_uk, c
   return MLA_OK;
 }
 
-mla_status mla_append_quant(const mla_dims *dims, const void *latent, mla_dtype dtype,
-                            const uint16_t *k_rope, const uint16_t *idx_key, const int64_t *slot_mapping,
-                            int64_t n, const uint16_t *R_apply_t, const float *alpha, const mla_cache *cache,
-                            void *stream) {
+}  // extern "C"
+
+namespace {
+// Host-side checks of a quantise-on-append call (no side effects); F names
+// the entry point in the message.
+mla_status append_check(const std::string &F, const mla_dims *dims, const void *latent, mla_dtype dtype,
+                        const uint16_t *k_rope, const uint16_t *idx_key, const int64_t *slot_mapping, int64_t n,
+                        const uint16_t *R_apply_t, const float *alpha, const mla_cache *cache) {
   std::string why;
-  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "mla_append_quant: " + why);
+  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, F + why);
   if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_FP32)
-    return fail(MLA_ERR_INVALID_ARG, "mla_append_quant: dtype must be bf16 or fp32");
-  if (n < 0) return fail(MLA_ERR_INVALID_ARG, "mla_append_quant: n must be >= 0");
-  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, "mla_append_quant: cache is NULL");
-  if (n == 0) {
-    clear_error();
-    return MLA_OK;
-  }
+    return fail(MLA_ERR_INVALID_ARG, F + "dtype must be bf16 or fp32");
+  if (n < 0) return fail(MLA_ERR_INVALID_ARG, F + "n must be >= 0");
+  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, F + "cache is NULL");
+  if (n == 0) return MLA_OK;
   if (!latent || !k_rope || !slot_mapping || !R_apply_t || !alpha || !cache->codes || !cache->scale_zero ||
       !cache->k_rope)
-    return fail(MLA_ERR_INVALID_ARG, "mla_append_quant: NULL device pointer");
+    return fail(MLA_ERR_INVALID_ARG, F + "NULL device pointer");
   if ((dims->index_head_dim > 0) != (idx_key != nullptr) ||
       (dims->index_head_dim > 0 && cache->idx_key == nullptr))
-    return fail(MLA_ERR_INVALID_ARG, "mla_append_quant: idx_key and cache.idx_key must be given iff index_head_dim > 0");
-  if (cache->capacity < 0) return fail(MLA_ERR_INVALID_ARG, "mla_append_quant: negative capacity");
+    return fail(MLA_ERR_INVALID_ARG, F + "idx_key and cache.idx_key must be given iff index_head_dim > 0");
+  if (cache->capacity < 0) return fail(MLA_ERR_INVALID_ARG, F + "negative capacity");
   if (dims->kv_lora_rank > 1024 && !append_uses_mfma(*dims, dtype))
-    return fail(MLA_ERR_UNSUPPORTED, "mla_append_quant: kv_lora_rank > 1024");
-  if (n > (int64_t{1} << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "mla_append_quant: n >= 2^31");
+    return fail(MLA_ERR_UNSUPPORTED, F + "kv_lora_rank > 1024");
+  if (n > (int64_t{1} << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, F + "n >= 2^31");
   const void *ptrs[] = {latent, k_rope, idx_key, slot_mapping, R_apply_t, alpha, cache->codes,
                         cache->scale_zero, cache->k_rope, cache->idx_key};
   for (const void *p : ptrs)
     if (p != nullptr && !aligned16(p))
-      return fail(MLA_ERR_INVALID_ARG, "mla_append_quant: device pointers must be 16-byte aligned");
+      return fail(MLA_ERR_INVALID_ARG, F + "device pointers must be 16-byte aligned");
+  return MLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+mla_status mla_append_quant(const mla_dims *dims, const void *latent, mla_dtype dtype,
+                            const uint16_t *k_rope, const uint16_t *idx_key, const int64_t *slot_mapping,
+                            int64_t n, const uint16_t *R_apply_t, const float *alpha, const mla_cache *cache,
+                            void *stream) {
+  const mla_status st = append_check("mla_append_quant: ", dims, latent, dtype, k_rope, idx_key, slot_mapping, n,
+                                     R_apply_t, alpha, cache);
+  if (st != MLA_OK) return st;
+  if (n == 0) {
+    clear_error();
+    return MLA_OK;
+  }
   hipError_t e = launch_append(*dims, latent, dtype, k_rope, idx_key, slot_mapping, n, R_apply_t, alpha, *cache,
                                nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mla_append_quant");
@@ -586,7 +604,8 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
                        const uint16_t *w_uk_f, const uint16_t *w_uv_f, const mla_cache *cache,
                        const int64_t *seq_base, const int32_t *seq_len, const int32_t *sel, int32_t sel_stride,
                        int32_t batch, int32_t tq, int32_t causal, float softmax_scale, void *workspace,
-                       size_t workspace_bytes, float *out, float *lse, void *stream) {
+                       size_t workspace_bytes, float *out, float *lse, void *stream,
+                       const AppendJob *job = nullptr, mla_dtype job_dtype = MLA_DTYPE_BF16) {
   const std::string F = std::string(fn) + ": ";
   std::string why;
   if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, F + "" + why);
@@ -596,6 +615,11 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
   if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, F + "softmax_scale not finite");
   if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, F + "cache is NULL");
   if (batch == 0) {
+    if (job != nullptr) {  // the step's append still runs
+      const hipError_t e = launch_append(*dims, job->latent, job_dtype, job->k_rope, job->idx_key, job->slots, job->n,
+                                         job->Rt, job->alpha, *cache, nullptr, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, fn);
+    }
     clear_error();
     return MLA_OK;
   }
@@ -653,8 +677,14 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
   a.sel = sel;
   a.sel_stride = sel_stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // the MFMA absorb kernel also runs the planner
-  hipError_t e = use_mfma ? launch_absorb_mfma_layout(a, s) : launch_plan(a, s);
+  // the MFMA absorb kernel also runs the planner, and takes a step's small
+  // append as extra blocks; any other append runs first on its own
+  const bool fuse = job != nullptr && use_mfma && append_fusable(*dims, job_dtype, job->n);
+  hipError_t e = hipSuccess;
+  if (job != nullptr && !fuse)
+    e = launch_append(*dims, job->latent, job_dtype, job->k_rope, job->idx_key, job->slots, job->n, job->Rt,
+                      job->alpha, *cache, nullptr, s);
+  if (e == hipSuccess) e = use_mfma ? launch_absorb_mfma_layout(a, s, fuse ? job : nullptr) : launch_plan(a, s);
   if (e == hipSuccess && !use_mfma) e = launch_absorb_f32(a, s);
   if (e == hipSuccess) e = use_mfma ? launch_splitk_mfma(a, s) : launch_splitk_valu(a, s);
   if (e == hipSuccess) e = launch_combine(a, s);
@@ -675,6 +705,22 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
                                float *out, float *lse, void *stream) {
   return decode_impl("mla_decode_absorbed", dims, q_nope, q_rope, w_uk_f, w_uv_f, cache, seq_base, seq_len,
                      nullptr, 0, batch, tq, causal, softmax_scale, workspace, workspace_bytes, out, lse, stream);
+}
+
+mla_status mla_decode_step(const mla_dims *dims, const void *latent, mla_dtype dtype, const uint16_t *k_rope,
+                           const uint16_t *idx_key, const int64_t *slot_mapping, int64_t n,
+                           const uint16_t *R_apply_t, const float *alpha, const uint16_t *q_nope,
+                           const uint16_t *q_rope, const uint16_t *w_uk_f, const uint16_t *w_uv_f,
+                           const mla_cache *cache, const int64_t *seq_base, const int32_t *seq_len, int32_t batch,
+                           int32_t tq, int32_t causal, float softmax_scale, void *workspace,
+                           size_t workspace_bytes, float *out, float *lse, void *stream) {
+  const mla_status st = append_check("mla_decode_step: ", dims, latent, dtype, k_rope, idx_key, slot_mapping, n,
+                                     R_apply_t, alpha, cache);
+  if (st != MLA_OK) return st;
+  AppendJob job{latent, k_rope, idx_key, slot_mapping, n, R_apply_t, alpha};
+  return decode_impl("mla_decode_step", dims, q_nope, q_rope, w_uk_f, w_uv_f, cache, seq_base, seq_len, nullptr,
+                     0, batch, tq, causal, softmax_scale, workspace, workspace_bytes, out, lse, stream,
+                     n > 0 ? &job : nullptr, dtype);
 }
 
 namespace {

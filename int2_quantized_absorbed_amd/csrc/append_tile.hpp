@@ -1,0 +1,230 @@
+// Device pieces of the quantise-on-append path shared by the append kernels
+// and by the decode-step launch that runs a small append next to the query
+// absorb: the argument block, the side-key copy, the quantiser epilogue of
+// one 32-channel x 32-token rotation tile, and the one-wave small-append tile.
+//
+// [OSCAR issue #10, maintainer reply, "How the rotation adapts to the
+// latent"]: the cache holds the rotated, INT2-quantised latent; low-variance
+// eigen-directions (the first channels of z, ascending order) share groups.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int kSkinnyMaxTokens = 1024;  // appends of at most this many tokens use the small-append tile
+
+// Copy the bf16 side keys (width values each) of tokens [t0, t0 + cnt) into
+// their cache slots, one wave, all lanes moving 16-byte pieces (4-byte pieces
+// when width is not a multiple of 8); slots outside the cache are skipped.
+__device__ __forceinline__ void copy_side_keys(uint16_t *__restrict__ dst, const uint16_t *__restrict__ src,
+                                               int width, const int64_t *__restrict__ slots, int64_t t0,
+                                               int cnt, int64_t capacity, int lane) {
+  if ((width & 7) == 0) {
+    const int per = width / 8, total = cnt * per;
+    for (int e0 = lane; e0 < total; e0 += 64 * 4) {
+      uint4 v[4];
+      int64_t sl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = min(e0 + 64 * j, total - 1), t = e / per;
+        sl[j] = slots[t0 + t];
+        v[j] = reinterpret_cast<const uint4 *>(src + (t0 + t) * width)[e % per];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 64 * j;
+        if (e < total && sl[j] >= 0 && sl[j] < capacity)
+          reinterpret_cast<uint4 *>(dst + sl[j] * width)[e % per] = v[j];
+      }
+    }
+  } else {
+    const int per = width / 2, total = cnt * per;
+    for (int e = lane; e < total; e += 64) {
+      const int t = e / per;
+      const int64_t sl = slots[t0 + t];
+      if (sl >= 0 && sl < capacity)
+        reinterpret_cast<uint32_t *>(dst + sl * width)[e % per] =
+            reinterpret_cast<const uint32_t *>(src + (t0 + t) * width)[e % per];
+    }
+  }
+}
+
+struct AppendParams {
+  const void *latent;
+  const uint16_t *k_rope;
+  const uint16_t *idx_key;
+  const int64_t *slots;
+  int64_t n;
+  const uint16_t *Rt;
+  const float *alpha;
+  mla_cache cache;
+  float *z_out;
+  int64_t lat_stride;  // elements from one token's latent row to the next
+  int r, G, d_r, d_idx;
+};
+
+// Epilogue of one 32-channel x 32-token rotation tile in MFMA C layout (lane
+// l holds channels ch0 + 8q + 4hf + s, v = 4q + s, of token tok): the fp32
+// rotated latent for a rotation-only launch, else the group min/max
+// (exchanged with the partner lane l ^ 32), fp16 scale/zero, INT2 codes and
+// their stores into the token's cache slot.
+template <int R, int G>
+__device__ __forceinline__ void tile_epilogue(const AppendParams &p, const f32x16 &z, int64_t tok, bool write,
+                                              int64_t slot, int ch0, const float (&alpha)[32 / G], int hf) {
+  constexpr int NGT = 32 / G;    // groups per tile: 1 (G=32) or 2 (G=16)
+  constexpr int VPG = 16 / NGT;  // values per lane per group
+  if (p.z_out != nullptr) {
+    if (write) {
+      float *dst = p.z_out + tok * R + ch0 + 4 * hf;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4 *>(dst + 8 * q) = f32x4{z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+    }
+    return;
+  }
+  QuantParams qp[NGT];
+#pragma unroll
+  for (int g = 0; g < NGT; ++g) {
+    float mx = z[g * VPG], mn = z[g * VPG];
+#pragma unroll
+    for (int v = 1; v < VPG; ++v) {
+      mx = fmaxf(mx, z[g * VPG + v]);
+      mn = fminf(mn, z[g * VPG + v]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    qp[g] = quant_params(mx, mn, alpha[g]);
+  }
+  // quotient estimates u for all 16 values and their nearest integers; the
+  // exact division runs only where some estimate of this lane lies within
+  // 2e-6 of a half-integer (a code boundary, or one the clamp makes
+  // harmless).  A NaN or infinite estimate gives the same code either way.
+  float xs[16], rs[16];
+  float dmin = 1.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const QuantParams &qq = qp[v / VPG];
+    xs[v] = __fsub_rn(z[v], qq.zero_f);
+    const float u = quant_u_estimate(xs[v], qq);
+    rs[v] = rintf(u);
+    dmin = fminf(dmin, 0.5f - fabsf(u - rs[v]));
+  }
+  if (!(dmin > 2e-6f)) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const QuantParams &qq = qp[v / VPG];
+      const float u = quant_u_estimate(xs[v], qq);
+      if (!(0.5f - fabsf(u - rs[v]) > 2e-6f)) rs[v] = rintf(__fdiv_rn(xs[v], qq.scale_f));
+    }
+  }
+  uint32_t dword = 0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) dword |= static_cast<uint32_t>(fminf(fmaxf(rs[v], 0.0f), 3.0f)) << (2 * v);
+  // a group with scale 0 (all values equal) gets code 0 throughout
+#pragma unroll
+  for (int g = 0; g < NGT; ++g)
+    if (qp[g].scale_f == 0.0f) dword &= VPG == 16 ? 0u : ~(0xffffu << (16 * g));
+  // lane hf=0 holds bytes 0,2,4,6 of the tile's 8 code bytes, hf=1 holds 1,3,5,7
+  const uint32_t partner = __shfl_xor(dword, 32);
+  const uint32_t packed = __builtin_amdgcn_perm(partner, dword, hf ? 0x03070206u : 0x05010400u);
+  if (write) {
+    reinterpret_cast<uint32_t *>(p.cache.codes + slot * (R / 4) + ch0 / 4)[hf] = packed;
+    if (NGT == 1) {
+      if (hf == 0) {
+        const uint32_t sz = static_cast<uint32_t>(f16_bits(qp[0].scale)) |
+                            (static_cast<uint32_t>(f16_bits(qp[0].zero)) << 16);
+        reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G] = sz;
+      }
+    } else {
+      // lane half hf stores group hf's side info (selects, not a lane-indexed array)
+      const uint32_t sz0 = static_cast<uint32_t>(f16_bits(qp[0].scale)) |
+                           (static_cast<uint32_t>(f16_bits(qp[0].zero)) << 16);
+      const uint32_t sz1 = static_cast<uint32_t>(f16_bits(qp[NGT - 1].scale)) |
+                           (static_cast<uint32_t>(f16_bits(qp[NGT - 1].zero)) << 16);
+      const uint32_t sz = hf ? sz1 : sz0;
+      reinterpret_cast<uint32_t *>(p.cache.scale_zero)[slot * (R / G) + ch0 / G + hf] = sz;
+    }
+  }
+}
+
+// One 32-channel x 32-token tile of a small append (a decode step's few new
+// tokens) by one wave: R_apply^T rows and latents go straight from memory
+// into the MFMA operands, all at once (ALL) or in double-buffered chunks.
+// Every accumulator sees the same MFMA sequence as in the LDS-staged kernel
+// (K-steps in order, even/odd partial sums added at the end), so a token
+// gets bit-identical codes whichever kernel appends it.
+template <int R, int G, int NACC, bool ALL>
+__device__ __forceinline__ void skinny_tile(const AppendParams &p, int ct, int ty, int l) {
+  constexpr int KS = R / 16;
+  constexpr int NGT = 32 / G;
+  const int hf = l >> 5, l32 = l & 31;  // channels [32 ct, 32 ct + 32), tokens [32 ty, 32 ty + 32)
+  const int64_t tok = static_cast<int64_t>(ty) * 32 + l32;
+  const bool valid = tok < p.n;
+  const bf16x8 *arow = reinterpret_cast<const bf16x8 *>(p.Rt + static_cast<int64_t>(32 * ct + l32) * R);
+  const bf16x8 *brow =
+      reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(p.latent) + (valid ? tok : 0) * p.lat_stride);
+  int64_t slot = -1;
+  float alpha[NGT] = {};
+  if (p.z_out == nullptr) {
+    if (valid) slot = p.slots[tok];
+#pragma unroll
+    for (int g = 0; g < NGT; ++g) alpha[g] = p.alpha[(32 * ct) / G + g];
+  }
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) acc[a] = f32x16{};
+  // lanes of tokens past the end read token 0's row (their columns are never
+  // stored), so the loads carry no branches
+  if constexpr (ALL) {
+    // every operand of the tile requested at once (one memory round trip;
+    // 2 x KS loads per lane)
+    bf16x8 aq[KS], bq[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      aq[ks] = arow[2 * ks + hf];
+      bq[ks] = brow[2 * ks + hf];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc[ks % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], bq[ks], acc[ks % NACC], 0, 0, 0);
+  } else {
+    // operands in chunks of 16 K-steps, one chunk of registers (for a wave
+    // that shares its workgroup's register budget with other work): a
+    // chunk's loads are issued as soon as the previous chunk's products are
+    constexpr int PD = KS < 16 ? KS : 16;
+    static_assert(KS % PD == 0, "K-steps come in whole chunks");
+#pragma unroll
+    for (int c = 0; c < KS / PD; ++c) {
+      bf16x8 aq[PD], bq[PD];
+#pragma unroll
+      for (int j = 0; j < PD; ++j) {
+        aq[j] = arow[2 * (c * PD + j) + hf];
+        bq[j] = brow[2 * (c * PD + j) + hf];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < PD; ++j) {
+        const int ks = c * PD + j;
+        acc[ks % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[j], bq[j], acc[ks % NACC], 0, 0, 0);
+      }
+    }
+  }
+  f32x16 z = acc[0];
+#pragma unroll
+  for (int a = 1; a < NACC; ++a) z += acc[a];
+  const bool write = valid && (p.z_out != nullptr || (slot >= 0 && slot < p.cache.capacity));
+  tile_epilogue<R, G>(p, z, tok, write, slot, 32 * ct, alpha, hf);
+  // side keys: the first channel tile copies its 32 tokens' keys
+  if (ct == 0 && p.z_out == nullptr) {
+    const int64_t t0 = static_cast<int64_t>(ty) * 32;
+    const int cnt = static_cast<int>(min<int64_t>(32, p.n - t0));
+    copy_side_keys(p.cache.k_rope, p.k_rope, p.d_r, p.slots, t0, cnt, p.cache.capacity, l);
+    if (p.d_idx > 0) copy_side_keys(p.cache.idx_key, p.idx_key, p.d_idx, p.slots, t0, cnt, p.cache.capacity, l);
+  }
+}
+
+}  // namespace
+}  // namespace mla

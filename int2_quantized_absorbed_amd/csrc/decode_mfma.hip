@@ -29,7 +29,7 @@
 // The running max is only moved when a tile's max exceeds it by more than
 // 8 (log2 units); otherwise p = 2^(s - m) <= 256 stays exact enough in fp16
 // and O needs no rescaling.
-#include "kernels.hpp"
+#include "append_tile.hpp"
 #include "plan.hpp"
 
 namespace mla {
@@ -488,7 +488,15 @@ __device__ __forceinline__ int64_t qpos(int rb_count, int b, int m, int w, int h
 
 constexpr int QTSTRIDE = 136;  // halves per staged row (128 channels + pad)
 
-__global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_count) {
+// Query absorb (q~ = W~_UK^T q_nope per head, in split-K operand order), the
+// split-K planner (block (0, 0)), and optionally a decode step's small append
+// (columns 1 .. x0 - 1, dispatched right after the planner so its memory
+// round trips overlap the absorb: each 4-wave block appends four 32-channel
+// tiles of one 32-token tile, with the same tile code as the stand-alone
+// small-append kernel, so the cache bytes are identical).  The absorb blocks
+// are the columns from x0 on.
+template <int G>  // INT2 group size of the fused append (0: no append)
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_count, AppendParams ap, int x0) {
   __shared__ __align__(16) f16 qt[32 * QTSTRIDE];
   // the quarter's 128 W~_UK rows, 128 values of the contraction at a time;
   // 16-byte piece p of row j sits at piece p ^ (j & 15) (conflict-free
@@ -504,7 +512,16 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_c
                  a.meta);
     return;
   }
-  const int h = (blockIdx.x - 1) >> 2, cq = (blockIdx.x - 1) & 3, rt = blockIdx.y;
+  if constexpr (G != 0) {
+    if (static_cast<int>(blockIdx.x) < x0) {
+      // append block: tiles (ct = 4 (blk % (R / 128)) + wave, ty = blk / (R / 128))
+      const int blk = (blockIdx.x - 1) * gridDim.y + blockIdx.y;
+      const int ty = blk / (R / 128), ct = 4 * (blk % (R / 128)) + (threadIdx.x >> 6);
+      if (static_cast<int64_t>(ty) * 32 < ap.n) skinny_tile<R, G, 2, false>(ap, ct, ty, threadIdx.x & 63);
+      return;
+    }
+  }
+  const int h = (blockIdx.x - x0) >> 2, cq = (blockIdx.x - x0) & 3, rt = blockIdx.y;
   const int M = H * a.Tq;
   const int nrows = a.B * a.Tq;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, hf = l >> 5, l32 = l & 31;
@@ -794,12 +811,39 @@ bool mfma_decode_supported(const mla_dims &d, int rows) {
 
 int mfma_row_block() { return ROWS; }
 
-hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s) {
-  TimedLaunch tl("absorb_q", s);
+hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s, const AppendJob *job) {
+  TimedLaunch tl(job != nullptr ? "append_absorb_q" : "absorb_q", s);
   const int M = a.d.num_heads * a.Tq;
   const int rb_count = (M + ROWS - 1) / ROWS;
   const int nrows = a.B * a.Tq;
-  absorb_mfma_kernel<<<dim3(a.d.num_heads * 4 + 1, (nrows + 31) / 32), 256, 0, s>>>(a, rb_count);
+  const int gy = (nrows + 31) / 32;
+  const int absorb_cols = a.d.num_heads * 4;
+  if (job == nullptr) {
+    absorb_mfma_kernel<0><<<dim3(1 + absorb_cols, gy), 256, 0, s>>>(a, rb_count, AppendParams{}, 1);
+    return hipGetLastError();
+  }
+  AppendParams ap{};
+  ap.latent = job->latent;
+  ap.k_rope = job->k_rope;
+  ap.idx_key = job->idx_key;
+  ap.slots = job->slots;
+  ap.n = job->n;
+  ap.Rt = job->Rt;
+  ap.alpha = job->alpha;
+  ap.cache = a.cache;
+  ap.z_out = nullptr;
+  ap.lat_stride = R;
+  ap.r = R;
+  ap.G = a.d.group_size;
+  ap.d_r = a.d.qk_rope_head_dim;
+  ap.d_idx = a.d.index_head_dim;
+  const int blocks = (R / 128) * static_cast<int>((job->n + 31) / 32);  // four 32-channel tiles per block
+  const int cols = (blocks + gy - 1) / gy;
+  const int x0 = 1 + cols;  // first absorb column
+  if (a.d.group_size == 32)
+    absorb_mfma_kernel<32><<<dim3(x0 + absorb_cols, gy), 256, 0, s>>>(a, rb_count, ap, x0);
+  else
+    absorb_mfma_kernel<16><<<dim3(x0 + absorb_cols, gy), 256, 0, s>>>(a, rb_count, ap, x0);
   return hipGetLastError();
 }
 

@@ -127,7 +127,19 @@ hipError_t launch_gqa_merge_unrotate(const GqaDecodeArgs &a, const DecodeArgs &s
 bool mfma_decode_supported(const mla_dims &d, int rows);
 bool mfma_absorb_supported(const mla_dims &d);
 int mfma_row_block();
-hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s);
+// A decode step's new tokens (bf16 latent rows of kv_lora_rank values),
+// appended by blocks of the query-absorb launch.
+struct AppendJob {
+  const void *latent;
+  const uint16_t *k_rope, *idx_key;
+  const int64_t *slots;
+  int64_t n;
+  const uint16_t *Rt;
+  const float *alpha;
+};
+// true when launch_absorb_mfma_layout can take the append of n tokens
+bool append_fusable(const mla_dims &d, mla_dtype dt, int64_t n);
+hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s, const AppendJob *job = nullptr);
 hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s);
 // grouped-query layers: head dim 128, at most 32 query rows per KV head,
 // one wave per work item (grid = max_items)

@@ -146,6 +146,30 @@ def test_append_argument_checks():
     assert call(cache=Bd.mla_cache(256, 256, 256, 0, -1)) == Bd.MLA_ERR_INVALID_ARG
 
 
+def test_decode_step_argument_checks():
+    """Every argument of the combined step is checked before anything is
+    launched: with no GPU here a launch would report MLA_ERR_HIP, so a
+    check error (or MLA_OK with nothing to do) shows nothing ran."""
+    lib = M.lib()
+    d = _dims()
+    P = ctypes.c_void_p(256)
+    cache = Bd.mla_cache(256, 256, 256, 0, 1000)
+    call = lambda **kw: lib.mla_decode_step(
+        ctypes.byref(d), kw.get("lat", P), kw.get("dt", 0), P, kw.get("idx", None), P, kw.get("n", 8), P, P,
+        kw.get("qn", P), P, P, P, ctypes.byref(cache), P, P, kw.get("B", 2), kw.get("tq", 1), 1, 0.07, P,
+        kw.get("wsb", 1 << 40), P, P, None)
+    assert call(n=-1) == Bd.MLA_ERR_INVALID_ARG
+    assert call(dt=7) == Bd.MLA_ERR_INVALID_ARG
+    assert call(lat=ctypes.c_void_p(0)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(idx=P) == Bd.MLA_ERR_INVALID_ARG           # idx key without index_head_dim
+    assert "mla_decode_step" in M.mla_last_error()
+    # valid append, invalid decode: rejected before the append is launched
+    assert call(tq=0) == Bd.MLA_ERR_INVALID_ARG
+    assert call(qn=ctypes.c_void_p(258)) == Bd.MLA_ERR_INVALID_ARG
+    assert call(wsb=16) == Bd.MLA_ERR_WORKSPACE
+    assert call(n=0, B=0) == Bd.MLA_OK                     # nothing to do
+
+
 def test_calibration_argument_checks():
     lib = M.lib()
     d = _dims()
