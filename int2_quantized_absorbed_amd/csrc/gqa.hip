@@ -121,111 +121,120 @@ __global__ __launch_bounds__(kThreads) void gqa_weighted_cov_kernel(const uint16
   }
 }
 
-// Query heads of one KV head handled together by the rotation kernels: the
-// lane's row (or column) of the rotation is loaded once and applied to all
-// of them from LDS.
-constexpr int kHeadChunk = 8;
+// The rotation kernels work on column slices of CW output channels (32, or
+// 16 when the head dim is not a multiple of 32): a block stages its slice
+// of the rotation into LDS with coalesced loads (rows padded by 16 bytes, so
+// the 16-byte reads of 16 consecutive rows hit distinct banks), and thread
+// (g, c) forms output channel c of query head g as a dot product over the
+// head dim, 256 / CW query heads per pass.
+__host__ __device__ __forceinline__ int rot_cw(int d) { return d % 32 == 0 ? 32 : 16; }
+
+// dot product of a staged bf16 row (d values) with a staged fp32 row
+__device__ __forceinline__ float dot_row(const uint16_t *mrow, const float *x, int d) {
+  float acc = 0.0f;
+  for (int n = 0; n < d; n += 8) {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(mrow + n);
+    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(x + n);
+    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(x + n + 4);
+    acc = fmaf(__uint_as_float(w[0] << 16), x0[0], acc);
+    acc = fmaf(__uint_as_float(w[0] & 0xffff0000u), x0[1], acc);
+    acc = fmaf(__uint_as_float(w[1] << 16), x0[2], acc);
+    acc = fmaf(__uint_as_float(w[1] & 0xffff0000u), x0[3], acc);
+    acc = fmaf(__uint_as_float(w[2] << 16), x1[0], acc);
+    acc = fmaf(__uint_as_float(w[2] & 0xffff0000u), x1[1], acc);
+    acc = fmaf(__uint_as_float(w[3] << 16), x1[2], acc);
+    acc = fmaf(__uint_as_float(w[3] & 0xffff0000u), x1[3], acc);
+  }
+  return acc;
+}
 
 // Rotated, scaled queries in the split-K kernel's layout (one pseudo-sequence
 // b' = b * H_kv + h per sequence and KV head, rows m = t * G + g):
 //   qbuf[b'][m][c] = scale * log2(e) * sum_n q[b][t][h G + g][n] R_k,apply[h][n][c]
 // and the pseudo-sequences' slots: KV head h's entries are cache slots
-// h * capacity + seq_base[b] ...  Grid (B * H_kv + 1, Tq); thread c < d
-// holds row c of R_apply^T (the rotation's column c) and forms channel c of
-// every query head of the group.  One extra block plans the split-K items
-// from seq_len alongside (each sequence counted once per KV head), which
-// saves a launch.
-template <int DMAX>  // head dim bound: the lane's rotation row is loaded whole, all loads in flight together
+// h * capacity + seq_base[b] ...  Grid (B * H_kv * (d / CW) + 1, Tq): block
+// (b', slice) stages rows [CW slice, +CW) of R_apply^T (rotation columns).
+// The last block plans the split-K items from seq_len alongside (each
+// sequence counted once per KV head), which saves a launch.
+template <int CW>
 __global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a, DecodeArgs sa) {
-  __shared__ float qs[kHeadChunk][256];
-  if (blockIdx.x == a.B * a.H_kv) {  // the extra block column: block (B * H_kv, 0) plans the split-K work
+  __shared__ __align__(16) uint16_t rsm[CW * (256 + 8)];
+  __shared__ __align__(16) float qs[kThreads / CW][256];
+  const int d = a.d, G = a.H_q / a.H_kv, ncs = d / CW, rst = d + 8;
+  if (static_cast<int>(blockIdx.x) == a.B * a.H_kv * ncs) {  // the planner block
     if (blockIdx.y == 0)
       plan_block(a.seq_len, sa.B, sa.target_items, sa.tile, sa.min_chunk_tiles, sa.max_items, sa.items,
                  sa.item_begin, sa.meta, a.H_kv);
     return;
   }
-  const int bp = blockIdx.x, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, c = threadIdx.x;
-  const int G = a.H_q / a.H_kv, d = a.d;
-  if (t == 0 && c == 0) {
+  const int bp = blockIdx.x / ncs, cs = blockIdx.x % ncs, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv;
+  const int tid = threadIdx.x;
+  if (t == 0 && cs == 0 && tid == 0) {
     a.base2[bp] = static_cast<int64_t>(h) * a.capacity + a.seq_base[b];
     a.len2[bp] = a.seq_len[b];
   }
-  const uint16_t *qbase = a.q + ((static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G) * d;
-  uint4 rw[DMAX / 8];  // row min(c, d-1) of R_apply^T, i.e. column c of the rotation
+  // rows [CW cs, +CW) of R_apply^T[h] are CW * d contiguous values
   {
-    const uint4 *rrow = reinterpret_cast<const uint4 *>(a.rk_t + (static_cast<int64_t>(h) * d + min(c, d - 1)) * d);
-#pragma unroll
-    for (int i = 0; i < DMAX / 8; ++i) rw[i] = 8 * i < d ? rrow[i] : make_uint4(0u, 0u, 0u, 0u);
+    const uint16_t *src = a.rk_t + (static_cast<int64_t>(h) * d + CW * cs) * d;
+    const int np = d / 8, total = CW * np;
+    for (int e = tid; e < total; e += kThreads)
+      *reinterpret_cast<u32x4 *>(rsm + (e / np) * rst + 8 * (e % np)) = reinterpret_cast<const u32x4 *>(src)[e];
   }
-  for (int g0 = 0; g0 < G; g0 += kHeadChunk) {
-    const int ng = min(kHeadChunk, G - g0);
-    __syncthreads();  // qs is rewritten
-    for (int e = c; e < ng * d; e += blockDim.x) qs[e / d][e % d] = bf16_to_f32(qbase[static_cast<int64_t>(g0) * d + e]);
+  const uint16_t *qbase = a.q + ((static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G) * d;
+  const int c = tid % CW, gl = tid / CW;
+  constexpr int GP = kThreads / CW;  // query heads per pass
+  for (int g0 = 0; g0 < G; g0 += GP) {
+    const int ng = min(GP, G - g0);
+    __syncthreads();  // qs is rewritten (and, the first time, the rotation is staged)
+    for (int e = tid; e < ng * d; e += kThreads) qs[e / d][e % d] = bf16_to_f32(qbase[static_cast<int64_t>(g0) * d + e]);
     __syncthreads();
-    if (c >= d) continue;
-    float acc[kHeadChunk];
-#pragma unroll
-    for (int g = 0; g < kHeadChunk; ++g) acc[g] = 0.0f;
-#pragma unroll
-    for (int n = 0; n < DMAX; n += 8) {
-      if (n < d) {  // uniform; rw stays statically indexed
-        const uint4 w = rw[n / 8];
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float r0 = __uint_as_float(ww[j] << 16), r1 = __uint_as_float(ww[j] & 0xffff0000u);
-#pragma unroll
-          for (int g = 0; g < kHeadChunk; ++g) {
-            acc[g] = fmaf(r0, qs[g][n + 2 * j], acc[g]);
-            acc[g] = fmaf(r1, qs[g][n + 2 * j + 1], acc[g]);
-          }
-        }
-      }
+    if (gl < ng) {
+      const float acc = dot_row(rsm + c * rst, qs[gl], d);
+      a.qbuf[((static_cast<int64_t>(bp) * a.Tq + t) * G + g0 + gl) * d + CW * cs + c] = acc * a.scale_log2;
     }
-#pragma unroll
-    for (int g = 0; g < kHeadChunk; ++g)
-      if (g < ng) a.qbuf[((static_cast<int64_t>(bp) * a.Tq + t) * G + g0 + g) * d + c] = acc[g] * a.scale_log2;
   }
 }
 
 // Merge of the split-K partials and un-rotation in one launch.  Grid
-// (B * H_kv, Tq): the block takes the G query heads of one (sequence, KV
-// head, query position), kHeadChunk at a time.  R_apply^T of the head is
-// staged in LDS first (its loads in flight during the merge).  Thread (row,
-// 4-channel chunk) folds the items of the pseudo-sequence into a running
-// (max, sum, O), kMergeU at a time (O_k = l_k times the stored fp16 O_k / l_k):
+// (B * H_kv * (d / CW), Tq): block (b', slice) merges every query head of one
+// (sequence, KV head, query position) over all d channels and forms output
+// channels [CW slice, +CW).  Thread (row, 4-channel chunk) folds the items of
+// the pseudo-sequence into a running (max, sum, O), kMergeU at a time (O_k =
+// l_k times the stored fp16 O_k / l_k):
 //   o_z = sum_k 2^(m_k - m) O_k / sum_k 2^(m_k - m) l_k,
 //   lse = ln 2 (m + log2 sum_k 2^(m_k - m) l_k);
-// then thread v forms out[v] = sum_c R_v,apply[v][c] o_z[c] for every row.
+// the columns [CW slice, +CW) of R_v,apply^T are staged transposed (row v of
+// the rotation, all c) and thread (g, v) forms out[g][v] = sum_c R_v,apply[v][c] o_z[g][c].
 constexpr int kMergeU = 16;
+constexpr int kRotPieces = 4;  // 16-byte pieces of the rotation slice per thread: 256 * 32 / 8 / 256
 
-template <int GC>  // query heads per pass: min(G, kHeadChunk) rounded up to a power of two
+template <int CW>
 __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeArgs a, DecodeArgs sa) {
-  extern __shared__ uint16_t rs[];  // [d][d] R_apply^T of head h, then zs [kHeadChunk][256]
-  const int bp = blockIdx.x, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv, tid = threadIdx.x;
-  const int G = a.H_q / a.H_kv, d = a.d, M = G * a.Tq, nch = d / 4;
-  float(*zs)[256] = reinterpret_cast<float(*)[256]>(rs + d * d);
-  {
-    const uint4 *src = reinterpret_cast<const uint4 *>(a.rv_t + static_cast<int64_t>(h) * d * d);
-    uint4 *dst = reinterpret_cast<uint4 *>(rs);
-    for (int e0 = 0; e0 < d * d / 8; e0 += 8 * kThreads) {  // eight loads in flight per thread
-      uint4 v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = src[min(e0 + j * kThreads + tid, d * d / 8 - 1)];  // clamped: always defined
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int e = e0 + j * kThreads + tid;
-        if (e < d * d / 8) dst[e] = v[j];
-      }
-    }
-  }
+  __shared__ __align__(16) uint16_t rsm[CW * (256 + 8)];
+  __shared__ __align__(16) float zs[kThreads / CW][256];
+  const int d = a.d, G = a.H_q / a.H_kv, M = G * a.Tq, nch = d / 4, ncs = d / CW, rst = d + 8;
+  const int bp = blockIdx.x / ncs, cs = blockIdx.x % ncs, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv;
+  const int tid = threadIdx.x;
   const int ib = sa.item_begin[bp], ie = sa.item_begin[bp + 1];
   const f16 *po = reinterpret_cast<const f16 *>(sa.part_o);
   const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G;  // first output row
-  for (int g0 = 0; g0 < G; g0 += GC) {
-    const int ng = min(GC, G - g0);
+  const int v = tid % CW, gl = tid / CW;
+  // the rotation slice is requested first, so its loads are in flight with
+  // the merge's: rows c of R_v,apply^T, columns [CW cs, +CW), 16 bytes at a
+  // time (d * CW / 8 pieces, at most kRotPieces per thread)
+  u32x4 rw[kRotPieces];
+#pragma unroll
+  for (int k = 0; k < kRotPieces; ++k) {
+    const int e = min(tid + k * kThreads, d * (CW / 8) - 1);  // clamped: always defined
+    const int cc = e / (CW / 8), p8 = e % (CW / 8);
+    rw[k] = *reinterpret_cast<const u32x4 *>(a.rv_t + static_cast<int64_t>(h) * d * d + static_cast<int64_t>(cc) * d +
+                                             CW * cs + 8 * p8);
+  }
+  constexpr int GP = kThreads / CW;  // query heads per pass
+  for (int g0 = 0; g0 < G; g0 += GP) {
+    const int ng = min(GP, G - g0);
     __syncthreads();  // zs is rewritten
-    for (int pr = tid; pr < ng * nch; pr += blockDim.x) {
+    for (int pr = tid; pr < ng * nch; pr += kThreads) {
       const int g = pr / nch, c = pr % nch, m = t * G + g0 + g;
       const float *ml = sa.part_ml + static_cast<int64_t>(m) * 2;
       const f16 *pp = po + static_cast<int64_t>(m) * d + 4 * c;
@@ -233,12 +242,12 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeA
       float mrun = -INFINITY, lrun = 0.0f;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int k0 = ib; k0 < ie; k0 += kMergeU) {
-        f16x4 v[kMergeU];
+        f16x4 vv[kMergeU];
         float2 st[kMergeU];
 #pragma unroll
         for (int e = 0; e < kMergeU; ++e) {
           const int k = min(k0 + e, ie - 1);
-          v[e] = *reinterpret_cast<const f16x4 *>(pp + k * po_stride);
+          vv[e] = *reinterpret_cast<const f16x4 *>(pp + k * po_stride);
           st[e] = *reinterpret_cast<const float2 *>(ml + k * ml_stride);
           if (k0 + e >= ie) st[e].x = -INFINITY;
         }
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeA
 #pragma unroll
           for (int e = 0; e < kMergeU; ++e) {
             const float wgt = st[e].x == -INFINITY ? 0.0f : exp2f(st[e].x - rm);
-            acc += (wgt * st[e].y) * __builtin_convertvector(v[e], f32x4);
+            acc += (wgt * st[e].y) * __builtin_convertvector(vv[e], f32x4);
             lrun += wgt * st[e].y;
           }
           mrun = rm;
@@ -260,28 +269,26 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeA
       }
       const float inv = lrun > 0.0f ? 1.0f / lrun : 0.0f;
       *reinterpret_cast<f32x4 *>(&zs[g][4 * c]) = acc * inv;
-      if (c == 0 && a.lse != nullptr) a.lse[row + g0 + g] = lrun > 0.0f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
+      if (c == 0 && cs == 0 && a.lse != nullptr)
+        a.lse[row + g0 + g] = lrun > 0.0f ? (mrun + log2f(lrun)) * kLn2 : -INFINITY;
     }
-    __syncthreads();
-    const int v = tid;
-    if (v >= d) continue;
-    float acc[GC];
+    if (g0 == 0) {
+      // the rotation slice, stored transposed (row v, column c)
 #pragma unroll
-    for (int g = 0; g < GC; ++g) acc[g] = 0.0f;
-    for (int c = 0; c < d; c += 4) {  // four channels per step: 16-byte reads of the merged rows
-      float r[4];
+      for (int k = 0; k < kRotPieces; ++k) {
+        const int e = tid + k * kThreads;
+        if (e < d * (CW / 8)) {
+          const int cc = e / (CW / 8), p8 = e % (CW / 8);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = bf16_to_f32(rs[(c + j) * d + v]);  // R_v,apply[v][c + j]
-#pragma unroll
-      for (int g = 0; g < GC; ++g) {
-        const f32x4 z = *reinterpret_cast<const f32x4 *>(&zs[g][c]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[g] = fmaf(r[j], z[j], acc[g]);
+          for (int j = 0; j < 4; ++j) {
+            rsm[(8 * p8 + 2 * j) * rst + cc] = static_cast<uint16_t>(rw[k][j] & 0xffffu);
+            rsm[(8 * p8 + 2 * j + 1) * rst + cc] = static_cast<uint16_t>(rw[k][j] >> 16);
+          }
+        }
       }
     }
-#pragma unroll
-    for (int g = 0; g < GC; ++g)
-      if (g < ng) a.out[(row + g0 + g) * d + v] = acc[g];
+    __syncthreads();
+    if (gl < ng) a.out[(row + g0 + gl) * d + CW * cs + v] = dot_row(rsm + v * rst, zs[gl], d);
   }
 }
 
@@ -299,33 +306,27 @@ hipError_t launch_gqa_calib_stats(const uint16_t *q, const uint16_t *k, const ui
 }
 
 hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, const DecodeArgs &sa, hipStream_t s) {
-  if (a.d > 256) return hipErrorInvalidValue;
+  if (a.d > 256 || a.d % 16 != 0) return hipErrorInvalidValue;
   TimedLaunch tl("gqa_rotate_q", s);
   // 256 threads: the planner block needs all of them
-  const dim3 grid(a.B * a.H_kv + 1, a.Tq);
-  if (a.d <= 64)
-    gqa_rotate_q_kernel<64><<<grid, kThreads, 0, s>>>(a, sa);
-  else if (a.d <= 128)
-    gqa_rotate_q_kernel<128><<<grid, kThreads, 0, s>>>(a, sa);
+  const int cw = rot_cw(a.d);
+  const dim3 grid(a.B * a.H_kv * (a.d / cw) + 1, a.Tq);
+  if (cw == 32)
+    gqa_rotate_q_kernel<32><<<grid, kThreads, 0, s>>>(a, sa);
   else
-    gqa_rotate_q_kernel<256><<<grid, kThreads, 0, s>>>(a, sa);
+    gqa_rotate_q_kernel<16><<<grid, kThreads, 0, s>>>(a, sa);
   return hipGetLastError();
 }
 
 hipError_t launch_gqa_merge_unrotate(const GqaDecodeArgs &a, const DecodeArgs &sa, hipStream_t s) {
-  if (a.d > 256 || a.d % 4 != 0) return hipErrorInvalidValue;
+  if (a.d > 256 || a.d % 16 != 0) return hipErrorInvalidValue;
   TimedLaunch tl("gqa_merge_unrotate", s);
-  const size_t lds = static_cast<size_t>(a.d) * a.d * sizeof(uint16_t) + kHeadChunk * 256 * sizeof(float);
-  const dim3 grid(a.B * a.H_kv, a.Tq);
-  const int G = a.H_q / a.H_kv;
-  if (G >= 8)
-    gqa_merge_unrotate_kernel<8><<<grid, kThreads, lds, s>>>(a, sa);
-  else if (G >= 4)
-    gqa_merge_unrotate_kernel<4><<<grid, kThreads, lds, s>>>(a, sa);
-  else if (G >= 2)
-    gqa_merge_unrotate_kernel<2><<<grid, kThreads, lds, s>>>(a, sa);
+  const int cw = rot_cw(a.d);
+  const dim3 grid(a.B * a.H_kv * (a.d / cw), a.Tq);
+  if (cw == 32)
+    gqa_merge_unrotate_kernel<32><<<grid, kThreads, 0, s>>>(a, sa);
   else
-    gqa_merge_unrotate_kernel<1><<<grid, kThreads, lds, s>>>(a, sa);
+    gqa_merge_unrotate_kernel<16><<<grid, kThreads, 0, s>>>(a, sa);
   return hipGetLastError();
 }
 
