@@ -463,9 +463,8 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
         const f32x4 x = *reinterpret_cast<const f32x4 *>(st + stage_pos(row, 4 * q));
         const f16x4 y = __builtin_convertvector(x * sm.inv_l[32 * mt + row], f16x4);
         const int m = rb * ROWS + 32 * mt + row;
-        if (m < M)  // streamed out (read once, by the combine kernel)
-          __builtin_nontemporal_store(
-              y, reinterpret_cast<f16x4 *>(a.part_o + (static_cast<int64_t>(item) * M + m) * R + 128 * w + 32 * nt + 4 * q));
+        if (m < M)  // ordinary stores: the combine kernel reads the rows next, often from the L2
+          *reinterpret_cast<f16x4 *>(a.part_o + (static_cast<int64_t>(item) * M + m) * R + 128 * w + 32 * nt + 4 * q) = y;
       }
     }
   if (s_k8 == 0 && s_m < M) {

@@ -124,6 +124,9 @@ APPEND_CASES = [
     ("w1-bf16-large-1500", 1, dict(), 1500),
     ("w1-bf16-large-g16-1100", 1, dict(group_size=16), 1100),
     ("w4-bf16-idx-large-1300", 4, dict(), 1300),
+    ("w1-r128-large-1100", 1, dict(kv_lora_rank=128), 1100),
+    ("w1-r256-large-g16-2100", 1, dict(kv_lora_rank=256, group_size=16), 2100),
+    ("w1-r384-large-1030", 1, dict(kv_lora_rank=384), 1030),
     # at most 1024 tokens: the small-append kernel
     ("w1-bf16-small-8", 1, dict(), 8),
     ("w1-bf16-small-g16-37", 1, dict(group_size=16), 37),
