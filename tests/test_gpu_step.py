@@ -79,3 +79,61 @@ def test_decode_step_equals_separate_calls(name, wid, over, lens, tq, causal, ne
         assert torch.equal(out0, out1), rep
         assert torch.equal(lse0, lse1), rep
         C.say(f"  rep {rep}: cache and outputs identical")
+
+
+def test_decode_step_edge_cases():
+    """No new tokens (decode only), no sequences (append only), and a fused
+    append whose slot list skips tokens (negative and out-of-range slots)."""
+    w = S.WORKLOADS[1].with_(num_heads=16)
+    C.say("decode_step edge cases")
+    layer = C.Layer(w)
+    d = layer.dims
+    rng = np.random.default_rng(29)
+    lens = [90, 41]
+    base, cap = S.contiguous_layout(lens, 5)
+    lat = C.latent_tensor(layer.model.sample(rng, 6), w.latent_dtype)
+    kr = C.t_bf16(S.rope_keys(rng, 6, w.qk_rope_head_dim))
+    slots = torch.tensor([int(base[0]) + 89, -1, int(base[1]) + 40, cap + 7, int(base[1]) + 39, int(base[0]) + 88],
+                         dtype=torch.int64, device=C.DEV)
+    st = S.streams(w.wid, 9)
+    qn, qr = S.queries(w, st, batch=2, tq=1)
+    qn_d, qr_d = C.t_bf16(qn), C.t_bf16(qr)
+    seq_base = torch.from_numpy(base).to(C.DEV)
+    seq_len = torch.from_numpy(np.asarray(lens, np.int32)).to(C.DEV)
+    scale = 1.0 / float(np.sqrt(w.qk_nope_head_dim + w.qk_rope_head_dim))
+    fill = lambda: [M.Cache(d, cap, C.DEV) for _ in range(2)]
+
+    # skipped slots in a fused append
+    c0, c1 = fill()
+    M.mla_append_quant(d, lat, kr, None, slots, layer.Rt_d, layer.alpha_d, c0)
+    out0, lse0 = M.mla_decode_absorbed(d, qn_d, qr_d, layer.w_uk_f, layer.w_uv_f, c0, seq_base, seq_len, 1, True, scale)
+    out1, lse1 = M.mla_decode_step(d, lat, kr, None, slots, layer.Rt_d, layer.alpha_d, qn_d, qr_d, layer.w_uk_f,
+                                   layer.w_uv_f, c1, seq_base, seq_len, 1, True, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(c0.codes, c1.codes) and torch.equal(c0.scale_zero.view(torch.int16),
+                                                           c1.scale_zero.view(torch.int16))
+    assert torch.equal(c0.k_rope.view(torch.int16), c1.k_rope.view(torch.int16))
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+
+    # no new tokens: the decode alone
+    empty_lat = torch.empty((0, w.kv_lora_rank), dtype=torch.bfloat16, device=C.DEV)
+    empty_kr = torch.empty((0, w.qk_rope_head_dim), dtype=torch.bfloat16, device=C.DEV)
+    empty_slots = torch.empty((0,), dtype=torch.int64, device=C.DEV)
+    before = c1.codes.clone()
+    out2, lse2 = M.mla_decode_step(d, empty_lat, empty_kr, None, empty_slots, layer.Rt_d, layer.alpha_d, qn_d, qr_d,
+                                   layer.w_uk_f, layer.w_uv_f, c1, seq_base, seq_len, 1, True, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(before, c1.codes)
+    assert torch.equal(out2, out0) and torch.equal(lse2, lse0)
+
+    # no sequences: the append alone
+    c2, _ = fill()
+    no_b = torch.empty((0,), dtype=torch.int64, device=C.DEV)
+    no_l = torch.empty((0,), dtype=torch.int32, device=C.DEV)
+    qn0 = torch.empty((0, 1, w.num_heads, w.qk_nope_head_dim), dtype=torch.bfloat16, device=C.DEV)
+    qr0 = torch.empty((0, 1, w.num_heads, w.qk_rope_head_dim), dtype=torch.bfloat16, device=C.DEV)
+    M.mla_decode_step(d, lat, kr, None, slots, layer.Rt_d, layer.alpha_d, qn0, qr0, layer.w_uk_f, layer.w_uv_f, c2,
+                      no_b, no_l, 1, True, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(c0.codes, c2.codes) and torch.equal(c0.k_rope.view(torch.int16), c2.k_rope.view(torch.int16))
+    C.say("  skipped slots, decode only, append only: identical to the separate calls")
