@@ -24,6 +24,8 @@
 //    operands straight from memory, the same MFMA sequence per accumulator.
 //  * append_valu_kernel: any other shape and fp32 latents; the dot products
 //    run in fp64 (exact products, fp64 sum) and are rounded once to fp32.
+#include <atomic>
+
 #include "append_tile.hpp"
 
 namespace mla {
@@ -369,11 +371,18 @@ hipError_t launch_staged(const AppendParams &p, hipStream_t s) {
   using C = StagedCfg<R, WAVES, NT>;
   constexpr int PFC = PF < C::NCH ? PF : C::NCH;
   const void *fn = reinterpret_cast<const void *>(&append_staged_kernel<R, G, WAVES, NT, PFC>);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(C::LDS));
+  // the dynamic LDS limit is a per-device attribute of the function: set it
+  // once on each device this instantiation launches on (devices past 63 set
+  // it on every launch)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t{1} << dev : 0;
+  if (bit == 0 || (attr_set.load(std::memory_order_acquire) & bit) == 0) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(C::LDS));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   const int64_t blocks = ((p.n + kTokPerBlock - 1) / kTokPerBlock) * (R / kSlice);
   if (blocks > (int64_t{1} << 30)) return hipErrorInvalidValue;
