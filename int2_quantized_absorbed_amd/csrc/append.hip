@@ -170,6 +170,17 @@ __global__ __launch_bounds__(64 * WAVES) void append_staged_kernel(AppendParams 
   const int64_t wave_tok0 = static_cast<int64_t>(tb) * kTokPerBlock + w * TOKW;
   const uint16_t *lat = static_cast<const uint16_t *>(p.latent);
 
+  // this thread's pieces of the R_apply^T slice (rows [cs*128, +128)) are
+  // requested first: the products need them before anything else
+  constexpr int CPR = R / 8;  // 16-byte pieces per row
+  constexpr int RPT = kSlice * CPR / C::THREADS;  // pieces per thread
+  static_assert(kSlice * CPR % C::THREADS == 0, "the slice splits evenly over the threads");
+  u32x4 rv[RPT];
+  {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(p.Rt + static_cast<int64_t>(cs) * kSlice * R);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) rv[j] = src[tid + C::THREADS * j];
+  }
   // chunk loads: load i of a chunk brings 16 bytes (piece l & 7) of the
   // chunk's 128 bytes of token wave_tok0 + 8i + (l >> 3); tokens past the end
   // read the last token's row (their outputs are never stored)
@@ -203,42 +214,55 @@ __global__ __launch_bounds__(64 * WAVES) void append_staged_kernel(AppendParams 
       for (int g = 0; g < NGT; ++g) alpha_of[mt][g] = p.alpha[(cs * kSlice + mt * 32) / G + g];
   }
 
-  // side keys first (their loads and stores overlap the prologue):
-  // channel-slice block cs copies its share of this token tile
-  // (ceil(kTokPerBlock / NSLICE) tokens), split over the waves, every lane
-  // moving 16-byte pieces
+  // side keys: channel-slice block cs copies its share of this token tile
+  // (ceil(kTokPerBlock / NSLICE) tokens), split over the waves.  When the
+  // wave's share is at most one 16-byte piece per lane (the usual shapes),
+  // the pieces are loaded here, in flight with the rotation staging below,
+  // and stored after it; otherwise they are copied here.
+  bool keys_deferred = false;
+  uint4 kr_v = {}, ix_v = {};
+  int64_t kr_sl = -1, ix_sl = -1;  // cache slots of the pieces (checked at store time)
+  int kr_pc = 0, ix_pc = 0;        // piece index within the key
   if (p.z_out == nullptr) {
     constexpr int PB = (kTokPerBlock + NSLICE - 1) / NSLICE, PW = (PB + WAVES - 1) / WAVES;
     const int64_t tile_end = min<int64_t>(static_cast<int64_t>(tb + 1) * kTokPerBlock, p.n);
     const int64_t t0 = static_cast<int64_t>(tb) * kTokPerBlock + cs * PB + w * PW;
     const int64_t t1 = min<int64_t>(min<int64_t>(t0 + PW, static_cast<int64_t>(tb) * kTokPerBlock + (cs + 1) * PB), tile_end);
     const int cnt = static_cast<int>(t1 - t0);
-    if (cnt > 0) {
+    const int pr = p.d_r / 8, pi = p.d_idx / 8;  // 16-byte pieces per token
+    keys_deferred = (p.d_r & 7) == 0 && (p.d_idx & 7) == 0 && cnt * pr <= 64 && cnt * pi <= 64;
+    if (cnt > 0 && keys_deferred) {
+      if (l < cnt * pr) {
+        const int64_t t = t0 + l / pr;
+        kr_sl = p.slots[t];
+        kr_pc = l % pr;
+        kr_v = reinterpret_cast<const uint4 *>(p.k_rope + t * p.d_r)[kr_pc];
+      }
+      if (pi > 0 && l < cnt * pi) {
+        const int64_t t = t0 + l / pi;
+        ix_sl = p.slots[t];
+        ix_pc = l % pi;
+        ix_v = reinterpret_cast<const uint4 *>(p.idx_key + t * p.d_idx)[ix_pc];
+      }
+    } else if (cnt > 0) {
       copy_side_keys(p.cache.k_rope, p.k_rope, p.d_r, p.slots, t0, cnt, p.cache.capacity, l);
       if (p.d_idx > 0) copy_side_keys(p.cache.idx_key, p.idx_key, p.d_idx, p.slots, t0, cnt, p.cache.capacity, l);
     }
   }
 
-  // stage R_apply^T rows [cs*128, +128) into LDS, 16 loads in flight per thread
-  {
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.Rt + static_cast<int64_t>(cs) * kSlice * R);
-    constexpr int CPR = R / 8;  // 16-byte chunks per row
-    constexpr int TOTAL = kSlice * CPR;
-    constexpr int PER = TOTAL / C::THREADS;  // chunks per thread
-    constexpr int SU = PER % 16 == 0 ? 16 : (PER % 8 == 0 ? 8 : (PER % 4 == 0 ? 4 : 1));
-    static_assert(TOTAL % (C::THREADS * SU) == 0, "staging loop has no tail");
-    for (int e0 = tid; e0 < TOTAL; e0 += C::THREADS * SU) {
-      uint4 v[SU];
+  // the R_apply^T slice into LDS
 #pragma unroll
-      for (int j = 0; j < SU; ++j) v[j] = src[e0 + C::THREADS * j];
-#pragma unroll
-      for (int j = 0; j < SU; ++j) {
-        const int e = e0 + C::THREADS * j;
-        *reinterpret_cast<uint4 *>(rt_s + rt_off<R>(e / CPR, e % CPR)) = v[j];
-      }
-    }
+  for (int j = 0; j < RPT; ++j) {
+    const int e = tid + C::THREADS * j;
+    *reinterpret_cast<u32x4 *>(rt_s + rt_off<R>(e / CPR, e % CPR)) = rv[j];
   }
   __syncthreads();
+  if (keys_deferred) {
+    if (kr_sl >= 0 && kr_sl < p.cache.capacity)
+      reinterpret_cast<uint4 *>(p.cache.k_rope + kr_sl * p.d_r)[kr_pc] = kr_v;
+    if (ix_sl >= 0 && ix_sl < p.cache.capacity)
+      reinterpret_cast<uint4 *>(p.cache.idx_key + ix_sl * p.d_idx)[ix_pc] = ix_v;
+  }
 
   f32x16 acc[2][4][NT];
 #pragma unroll
