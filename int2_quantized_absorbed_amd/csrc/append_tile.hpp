@@ -100,28 +100,35 @@ __device__ __forceinline__ void tile_epilogue(const AppendParams &p, const f32x1
   // quotient estimates u for all 16 values and their nearest integers; the
   // exact division runs only where some estimate of this lane lies within
   // 2e-6 of a half-integer (a code boundary, or one the clamp makes
-  // harmless).  A NaN or infinite estimate gives the same code either way.
+  // harmless); NaN and infinite estimates take that path too.
   float xs[16], rs[16];
-  float dmin = 1.0f;
+  bool near = false;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const QuantParams &qq = qp[v / VPG];
     xs[v] = __fsub_rn(z[v], qq.zero_f);
     const float u = quant_u_estimate(xs[v], qq);
     rs[v] = rintf(u);
-    dmin = fminf(dmin, 0.5f - fabsf(u - rs[v]));
+    near |= !(fabsf(u - rs[v]) < 0.5f - 2e-6f);  // (NaN: near)
   }
-  if (!(dmin > 2e-6f)) {
+  if (near) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const QuantParams &qq = qp[v / VPG];
       const float u = quant_u_estimate(xs[v], qq);
-      if (!(0.5f - fabsf(u - rs[v]) > 2e-6f)) rs[v] = rintf(__fdiv_rn(xs[v], qq.scale_f));
+      if (!(fabsf(u - rs[v]) < 0.5f - 2e-6f)) rs[v] = rintf(__fdiv_rn(xs[v], qq.scale_f));
     }
   }
+  // four clamped codes c0..c3 make the byte c0 + 4 c1 + 16 c2 + 64 c3, an
+  // integer that fp32 holds exactly; the conversion places it in the dword
   uint32_t dword = 0;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) dword |= static_cast<uint32_t>(fminf(fmaxf(rs[v], 0.0f), 3.0f)) << (2 * v);
+  for (int k = 0; k < 4; ++k) {
+    float b = fminf(fmaxf(rs[4 * k + 3], 0.0f), 3.0f);
+#pragma unroll
+    for (int j = 2; j >= 0; --j) b = fmaf(b, 4.0f, fminf(fmaxf(rs[4 * k + j], 0.0f), 3.0f));
+    dword = __builtin_amdgcn_cvt_pk_u8_f32(b, k, dword);
+  }
   // a group with scale 0 (all values equal) gets code 0 throughout
 #pragma unroll
   for (int g = 0; g < NGT; ++g)
