@@ -219,15 +219,17 @@ def main():
     pre_cache = M.Cache(d, n_pre, dev)
     for _ in range(3):
         M.mla_append_quant(d, pre_lat, pre_kr, pre_idx, pre_slots, Rt, alpha, pre_cache)
+    # 20 appends back to back between two events on the launch stream (the
+    # library launches on torch's current stream), so host launch latency
+    # does not enter the per-append time
     torch.cuda.synchronize()
-    M.mla_timing_enable(True)
-    M.mla_timing_reset()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
     for _ in range(20):
         M.mla_append_quant(d, pre_lat, pre_kr, pre_idx, pre_slots, Rt, alpha, pre_cache)
+    ev1.record()
     torch.cuda.synchronize()
-    ms, n = M.mla_timing_query("append_quant")
-    M.mla_timing_enable(False)
-    pre_us = ms / n * 1e3
+    pre_us = ev0.elapsed_time(ev1) / 20 * 1e3
     pre_bytes = n_pre * append_bytes_per_token(w)
     pre_flops = 2.0 * n_pre * w.kv_lora_rank * w.kv_lora_rank
     append_prefill = {
