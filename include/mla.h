@@ -245,6 +245,14 @@ size_t mla_decode_workspace_size(const mla_dims *dims, int32_t batch,
  * Requirements: 1 <= tq <= 64; batch >= 0 (0 = nothing to do);
  * kv_lora_rank <= 512 (UNSUPPORTED otherwise); the caller keeps
  * seq_base[b] + seq_len[b] <= capacity (not checkable on the host).
+ * Operand range: the MFMA path (H*tq >= 16) multiplies fp16 operands with
+ * fp32 accumulation, so |q_nope|, |q~ * softmax_scale * log2(e)|,
+ * |q_rope * softmax_scale * log2(e)|, |k_rope| and |z_hat| must stay below
+ * 65504 (the fp16 maximum); beyond it an operand overflows to infinity and
+ * the rows it touches come out undefined.  No range check is made.  Each
+ * operand carries one fp16 rounding (relative 2^-11; z_hat = zero + scale *
+ * code is rounded once, so where |zero| >> scale that rounding can exceed
+ * the code step).  The vector-ALU path works in fp32.
  * Asynchronous; no host synchronisation.
  * ---------------------------------------------------------------------- */
 mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope,
@@ -448,7 +456,10 @@ size_t gqa_decode_workspace_size(const gqa_dims *dims, int32_t batch,
  * An empty sequence gives out = 0, lse = -inf.  Runs as: query rotation,
  * split-K attention over each (sequence, KV head) (MFMA for head_dim 128
  * with at most 32 query rows per KV head, G * tq; vector ALU otherwise),
- * then the log-sum-exp merge and the un-rotation in one launch.
+ * then the log-sum-exp merge and the un-rotation in one launch.  The MFMA
+ * kernel takes q R_k * softmax_scale * log2(e) and the dequantised K and V
+ * entries as fp16 operands: they must stay below 65504 in magnitude (no
+ * range check is made).
  * Asynchronous; no host synchronisation.
  * Errors: INVALID_ARG (dims, batch < 0, tq outside 1..64, causal not 0/1,
  * NULL or unaligned pointers), WORKSPACE, HIP. */

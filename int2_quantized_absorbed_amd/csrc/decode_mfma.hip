@@ -457,6 +457,10 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
       const int col = slot_channel(sl >> 6, (sl & 63) >> 3, sl & 7) - 32 * nt;
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[stage_pos(8 * (v >> 2) + 4 * hf + (v & 3), col)] = o[mt][nt][v];
+      // the staged values cross lanes: keep the stores above the reads (and,
+      // below, the reads above the stores of the tile two steps on, which
+      // reuses this buffer)
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 8 * j + (l >> 3), q = l & 7;
@@ -466,6 +470,7 @@ __global__ __launch_bounds__(256, 1) void splitk_mfma_kernel(DecodeArgs a, int r
         if (m < M)  // ordinary stores: the combine kernel reads the rows next, often from the L2
           *reinterpret_cast<f16x4 *>(a.part_o + (static_cast<int64_t>(item) * M + m) * R + 128 * w + 32 * nt + 4 * q) = y;
       }
+      __builtin_amdgcn_wave_barrier();
     }
   if (s_k8 == 0 && s_m < M) {
     a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 0] = m_run;
@@ -701,6 +706,9 @@ __global__ __launch_bounds__(64) void gqa_splitk_mfma_kernel(DecodeArgs a) {
   RawTile rk = gqa_load<G>(a.cache, tile_slot(0), hf);
   RawTile rv = gqa_load<G>(a.vcache, tile_slot(0), hf);
   for (int i = 0; i < n_tiles; ++i) {
+    // LDS is handed between lanes of this one wave: the previous tile's
+    // reads of P and the V tile stay above this tile's stores
+    __builtin_amdgcn_wave_barrier();
     // K operands, the next K tile in flight, the scores; then V into the
     // same registers, the next V tile in flight, V to LDS (short live ranges
     // keep two waves per SIMD)
@@ -751,6 +759,7 @@ __global__ __launch_bounds__(64) void gqa_splitk_mfma_kernel(DecodeArgs a) {
     psum += __shfl_xor(psum, 32);
     l_run = l_run * alpha + psum;
     if (hf == 0) sm.alpha[l32] = alpha;
+    __builtin_amdgcn_wave_barrier();  // V tile, P and alpha stored before other lanes read them
     if (__any(scale_o ? 1 : 0)) {  // in place in the accumulator registers
       gqa_o_settle<true>(o);
 #pragma unroll
@@ -782,6 +791,7 @@ __global__ __launch_bounds__(64) void gqa_splitk_mfma_kernel(DecodeArgs a) {
   }
   // partial: O / l in fp16 (rows 8 (v / 4) + 4 hf + v % 4, slot 32 nt + l32), (m, l)
   if (hf == 0) sm.inv_l[l32] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  __builtin_amdgcn_wave_barrier();
   f16 *po = reinterpret_cast<f16 *>(a.part_o);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {

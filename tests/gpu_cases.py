@@ -44,11 +44,15 @@ class Layer:
     """One calibrated layer: oracle rotation and clip ratios (numpy) plus
     the same values on the device."""
 
-    def __init__(self, w: S.Workload, seed_offset: int = 0):
+    def __init__(self, w: S.Workload, seed_offset: int = 0, mean=None):
+        """mean = (n_dirs, lo, hi): latents with a seeded non-zero mean of
+        lo..hi standard deviations along n_dirs eigen-directions."""
         self.w = w
         self.dims = dims_of(w)
         self.st = S.streams(w.wid, seed_offset)
         self.model = S.latent_model(w, self.st)
+        if mean is not None:
+            self.model = self.model.with_mean(np.random.default_rng(977 + seed_offset), *mean)
         self.c_cal = S.calib_latents(w, self.st, self.model)
         self.R, self.eig, _ = O.calibrate_rotation(self.c_cal)
         self.R_apply = O.rotation_apply(self.R)

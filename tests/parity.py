@@ -3,9 +3,13 @@
 * 2-bit codes: bit-exact, except where the oracle's pre-rounding value u lies
   within BAND = 1e-5 of a quantisation boundary (k + 1/2, k = 0, 1, 2).
 * fp16 scale / zero: exact, except a one-ulp difference where the oracle's
-  fp32 value before rounding lies within 1e-5 (relative) of the midpoint
-  between the two fp16 neighbours; codes of such a group are judged against u
-  recomputed by the oracle from the GPU's own (scale, zero).
+  fp32 value before rounding lies within 1e-5 of the midpoint between the two
+  fp16 neighbours, relative to the largest magnitude the fp32 computation of
+  that value starts from (the group's max |z|: scale and zero come from the
+  group's max and min through differences that can cancel, so an fp32
+  accumulation difference in z carries into them as an absolute error of
+  that size); codes of such a group are judged against u recomputed by the
+  oracle from the GPU's own (scale, zero).
 * attention outputs: per output row (b, t, h),
   max |out - ref| / max |ref| <= 2e-3 with out in fp32;
   log-sum-exp: |lse - ref| <= 1e-3 max(1, |ref|).
@@ -31,9 +35,10 @@ def _near_boundary(u):
     return d < BAND
 
 
-def _f16_midpoint_ok(g16, o16, pre32):
+def _f16_midpoint_ok(g16, o16, pre32, mag):
     """A one-ulp fp16 difference is excused iff the fp32 value before rounding
-    sits within BAND (relative) of the midpoint of the two candidates."""
+    sits within BAND of the midpoint of the two candidates, relative to mag
+    (at least the midpoint's own magnitude)."""
     g = g16.astype(np.float64)
     o = o16.astype(np.float64)
     gb = g16.astype(np.float16).view(np.uint16).astype(np.int32)
@@ -41,7 +46,8 @@ def _f16_midpoint_ok(g16, o16, pre32):
     # neighbours in the fp16 encoding: same sign bit, magnitudes one apart
     one_ulp = ((gb & 0x8000) == (ob & 0x8000)) & (np.abs(gb - ob) == 1)
     mid = 0.5 * (g + o)
-    near = np.abs(pre32.astype(np.float64) - mid) <= BAND * np.maximum(np.abs(mid), 1e-30)
+    ref_mag = np.maximum(np.maximum(np.abs(mid), np.asarray(mag, dtype=np.float64)), 1e-30)
+    near = np.abs(pre32.astype(np.float64) - mid) <= BAND * ref_mag
     return one_ulp & near
 
 
@@ -54,8 +60,10 @@ def compare_append(gpu_packed, gpu_sz, ref: dict, group: int) -> dict:
     os_, oz = ref["scale_h"], ref["zero_h"]
     s_diff = gs.view(np.uint16) != os_.view(np.uint16)
     z_diff = gz.view(np.uint16) != oz.view(np.uint16)
-    sz_bad = (s_diff & ~_f16_midpoint_ok(gs, os_, ref["scale32"])) | \
-             (z_diff & ~_f16_midpoint_ok(gz, oz, ref["lo"]))
+    n = gc.shape[0]
+    gmag = np.max(np.abs(ref["z32"].astype(np.float64)).reshape(n, -1, group), axis=2)
+    sz_bad = (s_diff & ~_f16_midpoint_ok(gs, os_, ref["scale32"], gmag)) | \
+             (z_diff & ~_f16_midpoint_ok(gz, oz, ref["lo"], gmag))
     grp_diff = s_diff | z_diff
     # codes: where the side info differs (excused), judge against u from the
     # GPU's own side info; elsewhere against the oracle's u

@@ -5,12 +5,13 @@ built through the library exactly as ``bench.py`` builds it (same seeded
 latents, rope keys, indexer keys and queries, one append of every token,
 then ``mla_decode_absorbed`` with the default kernel choice).  The oracle
 then re-does one seeded sequence end to end: it quantises the whole
-sequence itself and computes absorbed attention for a seeded sample of
-heads (every query token of that sequence).  Checked:
+sequence itself and computes attention for every head and query token of
+that sequence (rotated-space form; the absorbed form on a seeded sample of
+heads as well).  Checked:
 
 * the sequence's INT2 codes and fp16 side info (bit-exact outside the
   1e-5 boundary band / fp16-midpoint rule), and its rope and indexer keys;
-* the sampled output rows (per-row max relative error <= 2e-3) and lse.
+* every output row of the sequence (per-row max relative error <= 2e-3) and lse.
 """
 from __future__ import annotations
 
@@ -71,17 +72,22 @@ def test_full_size_sampled(wid):
         assert torch.equal(cache.idx_key[a:a + L], idx[a:a + L])
 
     zh = O.dequantize(ref["codes"], ref["scale_h"], ref["zero_h"], w.group_size)
-    qn_b = qn[b][:, heads].float().cpu().numpy()
-    qr_b = qr[b][:, heads].float().cpu().numpy()
-    o_ref, lse_ref = O.absorbed_attention(qn_b, qr_b, layer.w_uk[heads], layer.w_uv[heads], zh, kr_seg,
-                                          layer.R_apply, scale, causal=w.causal)
-    o_gpu = out[b][:, heads].cpu().numpy()
-    lse_gpu = lse[b][:, heads].cpu().numpy()
+    # every head and every query token of the sequence, in the oracle's
+    # rotated-space form (equal to the absorbed form, pinned in fp64)
+    o_ref, lse_ref = O.rotated_attention(qn[b].float().cpu().numpy(), qr[b].float().cpu().numpy(), layer.w_uk,
+                                         layer.w_uv, zh, kr_seg, layer.R_apply, scale, causal=w.causal)
+    o_gpu = out[b].cpu().numpy()
+    lse_gpu = lse[b].cpu().numpy()
     err = row_rel_err(o_gpu, o_ref)
-    C.say(f"  decode, sequence {b}, heads {heads.tolist()}: worst row rel err {float(np.max(err)):.3e}, "
+    C.say(f"  decode, sequence {b}, all {H} heads x {tq} queries: worst row rel err {float(np.max(err)):.3e}, "
           f"lse max abs diff {float(np.max(np.abs(lse_gpu - lse_ref))):.3e}")
     assert np.all(err <= OUT_RTOL), err
     assert np.all(np.abs(lse_gpu - lse_ref) <= LSE_TOL * np.maximum(1, np.abs(lse_ref)))
+    # and the oracle's absorbed form itself on a seeded sample of heads
+    o_abs, _ = O.absorbed_attention(qn[b][:, heads].float().cpu().numpy(), qr[b][:, heads].float().cpu().numpy(),
+                                    layer.w_uk[heads], layer.w_uv[heads], zh, kr_seg, layer.R_apply, scale,
+                                    causal=w.causal)
+    assert np.all(row_rel_err(o_gpu[:, heads], o_abs) <= OUT_RTOL)
 
 
 def test_full_size_sparse():

@@ -113,15 +113,28 @@ def spectrum(w: Workload, st: dict) -> np.ndarray:
 
 @dataclass
 class LatentModel:
-    """The latent distribution of one layer: c = (xi * sqrt(eig)) Q^T."""
+    """The latent distribution of one layer: c = mu + (xi * sqrt(eig)) Q^T
+    (mu = 0 unless a mean is given)."""
     q: np.ndarray
     eig: np.ndarray
     dtype: str
+    mean: np.ndarray | None = None
 
     def sample(self, rng, n: int) -> np.ndarray:
         xi = rng.standard_normal((n, self.q.shape[0]))
-        c = ((xi * np.sqrt(self.eig)[None, :]) @ self.q.T).astype(np.float32)
+        c = (xi * np.sqrt(self.eig)[None, :]) @ self.q.T
+        if self.mean is not None:
+            c = c + self.mean[None, :]
+        c = c.astype(np.float32)
         return to_bf16_values(c) if self.dtype == "bf16" else c
+
+    def with_mean(self, rng, n_dirs: int, lo: float, hi: float) -> "LatentModel":
+        """The same spectrum with a non-zero mean: n_dirs seeded eigen-directions
+        k of the spectrum get mean a_k sqrt(eig_k), a_k uniform in [lo, hi]."""
+        idx = rng.choice(self.q.shape[0], size=n_dirs, replace=False)
+        a = rng.uniform(lo, hi, size=n_dirs)
+        mu = self.q[:, idx] @ (a * np.sqrt(self.eig[idx]))
+        return LatentModel(self.q, self.eig, self.dtype, mu)
 
 
 def latent_model(w: Workload, st: dict) -> LatentModel:
