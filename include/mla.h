@@ -265,6 +265,36 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope,
                                void *stream);
 
 /* ------------------------------------------------------------------------
+ * mla_decode_absorbed_noalloc — mla_decode_absorbed without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operands, outputs, kernels and results as mla_decode_absorbed; the
+ * workspace is instead a static device array of the library (48 MiB, one
+ * copy per GPU, held until the process ends; its address is looked up once
+ * per device on that device's first call).  The call allocates nothing.
+ * Nothing in the array needs to start at zero: every launch writes what the
+ * later launches of the same call read (work list, query operands,
+ * partials).  All calls on one GPU share the array, so calls that overlap
+ * on one GPU (several streams, several host threads) race: serialise them.
+ * Errors: as mla_decode_absorbed; WORKSPACE when this decode needs more
+ * than mla_decode_noalloc_max_workspace() bytes (mla_decode_workspace_size
+ * gives the need), with nothing launched.
+ * ---------------------------------------------------------------------- */
+size_t mla_decode_noalloc_max_workspace(void);
+mla_status mla_decode_absorbed_noalloc(const mla_dims *dims,
+                                       const uint16_t *q_nope,
+                                       const uint16_t *q_rope,
+                                       const uint16_t *w_uk_f,
+                                       const uint16_t *w_uv_f,
+                                       const mla_cache *cache,
+                                       const int64_t *seq_base,
+                                       const int32_t *seq_len, int32_t batch,
+                                       int32_t tq, int32_t causal,
+                                       float softmax_scale, float *out,
+                                       float *lse, void *stream);
+
+/* ------------------------------------------------------------------------
  * mla_decode_step — one decode step: quantise-on-append of the step's new
  * tokens, then absorbed decode over the cache that now holds them
  * [OSCAR-MLA; SHARD-MLA absorb form]

@@ -67,6 +67,10 @@ _SIGS = {
     "mla_decode_absorbed": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, _P, _P, _P, ctypes.POINTER(mla_cache),
                                            _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                            _P, ctypes.c_size_t, _P, _P, _P]),
+    "mla_decode_noalloc_max_workspace": (ctypes.c_size_t, []),
+    "mla_decode_absorbed_noalloc": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, _P, _P, _P,
+                                                   ctypes.POINTER(mla_cache), _P, _P, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
     "mla_decode_step": (ctypes.c_int, [ctypes.POINTER(mla_dims), _P, ctypes.c_int, _P, _P, _P, ctypes.c_int64,
                                        _P, _P, _P, _P, _P, _P, ctypes.POINTER(mla_cache), _P, _P, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, ctypes.c_size_t, _P, _P,
@@ -370,6 +374,33 @@ def mla_decode_absorbed(dims: Dims, q_nope, q_rope, w_uk_f, w_uv_f, cache: Cache
                                    float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
                                    _stream())
     _check(st, "mla_decode_absorbed")
+    return out, lse
+
+
+def mla_decode_noalloc_max_workspace() -> int:
+    return int(lib().mla_decode_noalloc_max_workspace())
+
+
+def mla_decode_absorbed_noalloc(dims: Dims, q_nope, q_rope, w_uk_f, w_uv_f, cache: Cache, seq_base, seq_len,
+                                tq: int, causal: bool, softmax_scale: float, out, lse):
+    """mla_decode_absorbed on the library's static scratch: the caller passes
+    the outputs (out [B, tq, H, d_v] fp32, lse [B, tq, H] fp32)."""
+    H, r = dims.num_heads, dims.kv_lora_rank
+    B = seq_len.shape[0]
+    _need(q_nope, "q_nope", torch.bfloat16, (B, tq, H, dims.qk_nope_head_dim))
+    _need(q_rope, "q_rope", torch.bfloat16, (B, tq, H, dims.qk_rope_head_dim))
+    _need(w_uk_f, "w_uk_f", torch.float16, (H, r, dims.qk_nope_head_dim))
+    _need(w_uv_f, "w_uv_f", torch.float16, (H, dims.v_head_dim, r))
+    _need(seq_base, "seq_base", torch.int64, (B,))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    _need(out, "out", torch.float32, (B, tq, H, dims.v_head_dim))
+    _need(lse, "lse", torch.float32, (B, tq, H))
+    d, c = dims.c(), cache.c()
+    st = lib().mla_decode_absorbed_noalloc(ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk_f),
+                                           _ptr(w_uv_f), ctypes.byref(c), _ptr(seq_base), _ptr(seq_len), B, tq,
+                                           int(bool(causal)), float(softmax_scale), _ptr(out), _ptr(lse),
+                                           _stream())
+    _check(st, "mla_decode_absorbed_noalloc")
     return out, lse
 
 

@@ -606,14 +606,15 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
                        int32_t batch, int32_t tq, int32_t causal, float softmax_scale, void *workspace,
                        size_t workspace_bytes, float *out, float *lse, void *stream,
                        const AppendJob *job = nullptr, mla_dtype job_dtype = MLA_DTYPE_BF16) {
-  const std::string F = std::string(fn) + ": ";
+  // messages are built only on failure (no host allocation on the way)
+  auto F = [fn](const std::string &m) { return std::string(fn) + ": " + m; };
   std::string why;
-  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, F + "" + why);
-  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, F + "batch must be >= 0");
-  if (tq < 1 || tq > 64) return fail(MLA_ERR_INVALID_ARG, F + "tq must be in 1..64");
-  if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, F + "causal must be 0 or 1");
-  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, F + "softmax_scale not finite");
-  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, F + "cache is NULL");
+  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, F(why));
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, F("batch must be >= 0"));
+  if (tq < 1 || tq > 64) return fail(MLA_ERR_INVALID_ARG, F("tq must be in 1..64"));
+  if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, F("causal must be 0 or 1"));
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARG, F("softmax_scale not finite"));
+  if (cache == nullptr) return fail(MLA_ERR_INVALID_ARG, F("cache is NULL"));
   if (batch == 0) {
     if (job != nullptr) {  // the step's append still runs
       const hipError_t e = launch_append(*dims, job->latent, job_dtype, job->k_rope, job->idx_key, job->slots, job->n,
@@ -625,28 +626,28 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
   }
   if (!q_nope || !q_rope || !w_uk_f || !w_uv_f || !seq_base || !seq_len || !workspace || !out ||
       !cache->codes || !cache->scale_zero || !cache->k_rope)
-    return fail(MLA_ERR_INVALID_ARG, F + "NULL device pointer");
+    return fail(MLA_ERR_INVALID_ARG, F("NULL device pointer"));
   const void *ptrs[] = {q_nope, q_rope, w_uk_f, w_uv_f, seq_base, seq_len, workspace, out, lse,
                         cache->codes, cache->scale_zero, cache->k_rope};
   for (const void *p : ptrs)
     if (p != nullptr && !aligned16(p))
-      return fail(MLA_ERR_INVALID_ARG, F + "device pointers must be 16-byte aligned");
+      return fail(MLA_ERR_INVALID_ARG, F("device pointers must be 16-byte aligned"));
   if (dims->kv_lora_rank > 512)
-    return fail(MLA_ERR_UNSUPPORTED, F + "kv_lora_rank > 512");
+    return fail(MLA_ERR_UNSUPPORTED, F("kv_lora_rank > 512"));
   const int M = dims->num_heads * tq;
   bool use_mfma = false;
   if (g_decode_variant == 2) {
     if (!mfma_decode_supported(*dims, M))
-      return fail(MLA_ERR_UNSUPPORTED, F + "no MFMA kernel for this shape");
+      return fail(MLA_ERR_UNSUPPORTED, F("no MFMA kernel for this shape"));
     use_mfma = true;
   } else if (g_decode_variant == 0) {
     use_mfma = M >= 16 && mfma_decode_supported(*dims, M);
   }
   if (use_mfma && !mfma_absorb_supported(*dims))
-    return fail(MLA_ERR_UNSUPPORTED, F + "qk_nope_head_dim must be a multiple of 16 for the MFMA path");
+    return fail(MLA_ERR_UNSUPPORTED, F("qk_nope_head_dim must be a multiple of 16 for the MFMA path"));
   const WsLayout w = layout(*dims, batch, tq);
   if (workspace_bytes < w.total)
-    return fail(MLA_ERR_WORKSPACE, F + "workspace needs " + std::to_string(w.total) + " bytes");
+    return fail(MLA_ERR_WORKSPACE, F("workspace needs ") + std::to_string(w.total) + " bytes");
   DecodeArgs a{};
   a.d = *dims;
   a.q_nope = q_nope;
@@ -705,6 +706,71 @@ mla_status mla_decode_absorbed(const mla_dims *dims, const uint16_t *q_nope, con
                                float *out, float *lse, void *stream) {
   return decode_impl("mla_decode_absorbed", dims, q_nope, q_rope, w_uk_f, w_uv_f, cache, seq_base, seq_len,
                      nullptr, 0, batch, tq, causal, softmax_scale, workspace, workspace_bytes, out, lse, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// decode with the library's own static device scratch (no allocation)
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t{48} << 20;
+constexpr int kMaxDevices = 64;
+
+// The decode workspace of mla_decode_absorbed_noalloc.  Host code never
+// uses this name as an address (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the
+// device's first call and kept.
+mla_status scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_absorbed_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_absorbed_noalloc: device index beyond the supported 64");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "mla_decode_absorbed_noalloc: hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MLA_ERR_HIP, "mla_decode_absorbed_noalloc: scratch has no device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_noalloc_max_workspace(void) { return kScratchBytes; }
+
+mla_status mla_decode_absorbed_noalloc(const mla_dims *dims, const uint16_t *q_nope, const uint16_t *q_rope,
+                                       const uint16_t *w_uk_f, const uint16_t *w_uv_f, const mla_cache *cache,
+                                       const int64_t *seq_base, const int32_t *seq_len, int32_t batch,
+                                       int32_t tq, int32_t causal, float softmax_scale, float *out, float *lse,
+                                       void *stream) {
+  std::string why;
+  if (!dims_valid(dims, &why)) return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed_noalloc: " + why);
+  if (batch < 0 || tq < 1 || tq > 64)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_absorbed_noalloc: batch must be >= 0 and tq in 1..64");
+  const size_t need = layout(*dims, batch, tq).total;
+  if (need > kScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "mla_decode_absorbed_noalloc: this decode needs " + std::to_string(need) +
+                                       " bytes of workspace; the static scratch holds " +
+                                       std::to_string(kScratchBytes) + " (use mla_decode_absorbed)");
+  void *ws = nullptr;
+  const mla_status st = scratch_address(&ws);
+  if (st != MLA_OK) return st;
+  return decode_impl("mla_decode_absorbed_noalloc", dims, q_nope, q_rope, w_uk_f, w_uv_f, cache, seq_base,
+                     seq_len, nullptr, 0, batch, tq, causal, softmax_scale, ws, kScratchBytes, out, lse, stream);
 }
 
 mla_status mla_decode_step(const mla_dims *dims, const void *latent, mla_dtype dtype, const uint16_t *k_rope,

@@ -88,6 +88,28 @@ def test_decode_argument_checks():
                                    1 << 40, P, P, None) == Bd.MLA_ERR_UNSUPPORTED
 
 
+def test_decode_noalloc_argument_checks():
+    """The static-scratch decode checks its arguments and its workspace need
+    on the host: a decode larger than the scratch is refused before anything
+    is launched."""
+    lib = M.lib()
+    d = _dims()
+    P = ctypes.c_void_p(256)
+    cache = Bd.mla_cache(256, 256, 256, 0, 1000)
+    call = lambda **kw: lib.mla_decode_absorbed_noalloc(
+        ctypes.byref(d), kw.get("qn", P), P, P, P, ctypes.byref(cache), P, P, kw.get("B", 2), kw.get("tq", 1),
+        kw.get("causal", 1), 0.07, P, P, None)
+    assert M.mla_decode_noalloc_max_workspace() == 48 << 20
+    assert call(tq=0) == Bd.MLA_ERR_INVALID_ARG
+    assert call(B=-1) == Bd.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_absorbed_noalloc(None, P, P, P, P, ctypes.byref(cache), P, P, 2, 1, 1, 0.07, P, P,
+                                           None) == Bd.MLA_ERR_INVALID_ARG
+    big_b = 256  # 256 sequences of 128 heads x 8 queries: far beyond 48 MiB of workspace
+    assert M.mla_decode_workspace_size(DS, big_b, 8) > M.mla_decode_noalloc_max_workspace()
+    assert call(B=big_b, tq=8) == Bd.MLA_ERR_WORKSPACE
+    assert "static scratch" in M.mla_last_error()
+
+
 def test_index_topk_argument_checks():
     lib = M.lib()
     d = _dims(index_head_dim=64)
