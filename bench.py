@@ -34,7 +34,8 @@ import numpy as np  # noqa: E402
 PEAK_MFMA_F16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "splitk_decode_traffic.json")
-KERNEL_SOURCES = ["int2_quantized_absorbed_amd/csrc/decode_mfma.hip",
+KERNEL_SOURCES = ["int2_quantized_absorbed_amd/csrc/splitk.hip",
+                  "int2_quantized_absorbed_amd/csrc/splitk_tile.hpp",
                   "int2_quantized_absorbed_amd/csrc/kernels.hpp",
                   "int2_quantized_absorbed_amd/csrc/common.hpp"]
 

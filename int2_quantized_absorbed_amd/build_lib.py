@@ -19,7 +19,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 
-SOURCES = ["api.hip", "append.hip", "calib.hip", "decode.hip", "decode_mfma.hip", "gqa.hip", "index.hip"]
+SOURCES = ["api.hip", "append.hip", "calib.hip", "decode.hip", "decode_mfma.hip", "gqa.hip", "index.hip",
+           "splitk.hip"]
+# Per-source flags.  The split-K kernel keeps its MFMA accumulators and
+# operands in ordinary VGPRs (the VGPR form of MFMA): its two wave roles then
+# fit in 256 registers each, two waves per SIMD.
+SOURCE_FLAGS = {"splitk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HOST_SOURCES = ["eigh.cpp"]
 
 ARCH = "gfx950"
@@ -52,7 +57,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmds.append([cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

@@ -1,0 +1,293 @@
+// Split-K flash-decode over the INT2 latent cache (absorbed form) for
+// r = 512, d_r = 64, on gfx950 MFMA.
+//
+// [shard PR #5, TL;DR item 2]: attention runs in latent space over the cached
+// latent plus one shared rope key.  [OSCAR issue #10, maintainer reply, "How
+// the rotation adapts to the latent"]: the cached latent is the rotated INT2
+// latent; the up-projection runs on its dequantised value (after the merge).
+//
+// Built with the VGPR form of MFMA (build flag), so the output accumulators
+// and the query operands live in ordinary VGPRs: both wave roles of the
+// kernel fit in 256 registers, two waves per SIMD.
+#include "splitk_tile.hpp"
+
+namespace mla {
+namespace {
+
+// Warp-specialised split-K kernel: one workgroup = one work item x one block
+// of 64 query rows, eight waves in two roles that share each SIMD.
+//  * Producer w (waves 0..3) owns latent channels [128w, 128w+128) and rope
+//    dims [16w, 16w+16): it loads and dequantises the tiles, stores its part
+//    of each dequantised tile Z to LDS, runs the score MFMAs over its K-slice
+//    and publishes the partial scores.
+//  * Consumer w (waves 4..7) owns 16 rows for the softmax (it sums the four
+//    partial scores, runs the online softmax, writes P and the per-row
+//    rescale factor) and the output block O[64 rows x 128 channels] of slice
+//    w, which it updates with the P Z MFMAs.
+// Producer w and consumer w sit on one SIMD: each runs its MFMAs while the
+// other runs vector-ALU and LDS work.  Per iteration i, two barriers:
+//   X (before A): producer: scores of tile i+1, Z of tile i+1 to LDS;
+//                 consumer: summed scores of tile i, softmax, P of tile i.
+//   Y (A to B):   producer: publish the partial scores of tile i+1,
+//                 dequantise tile i+2, request tile i+3;
+//                 consumer: rescale and O += P Z for tile i.
+// The running max moves only when a tile's max beats it by more than 8 (log2
+// units), as in splitk_mfma_kernel.  The output accumulators live in VGPRs
+// (this translation unit is built with the VGPR form of MFMA), so the
+// rescale is ordinary code and the compiler inserts the MFMA read hazards.
+template <int G>
+__global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_count, int n_logical) {
+  __shared__ Smem sm;
+  const int per_xcd = (n_logical + 7) / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (logical >= n_logical) return;
+  const int item = logical / rb_count;
+  const int rb = logical % rb_count;
+  if (item >= a.meta[0]) return;
+  const WorkItem it = a.items[item];
+
+  const int tid = threadIdx.x;
+  const bool producer = tid < 256;
+  const int w = (tid >> 6) & 3, l = tid & 63, hf = l >> 5, l32 = l & 31;
+  const int H = a.d.num_heads;
+  const int M = H * a.Tq;
+  const int L = a.seq_len[it.b];
+  const int64_t base = a.seq_base[it.b];
+  const int n_tiles = (it.t1 - it.t0 + TT - 1) / TT;
+
+  if (producer) {
+    // ---- Q~ operands (packed by the absorb kernel in exactly this order) ----
+    f16x8 aq[2][KB];
+    {
+      const f16x8 *qp = reinterpret_cast<const f16x8 *>(a.qbuf) +
+                        ((static_cast<int64_t>(it.b) * rb_count + rb) * 4 + w) * (2 * KB * 64);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) aq[mt][kb] = qp[(mt * KB + kb) * 64 + l];
+    }
+    const int32_t *sel = a.sel ? a.sel + static_cast<int64_t>(it.b) * a.sel_stride : nullptr;
+    auto tile_slot = [&](int i) -> int64_t {
+      const int ti = min(i, n_tiles - 1);
+      const int t = min(it.t0 + ti * TT + l32, it.t1 - 1);
+      return base + (sel ? sel[t] : t);
+    };
+    f16x8 bz[KB];
+    f32x16 sacc[2];
+    const int zsw = 8 * ((l32 >> 3) & 1);  // chunk kb goes to kb ^ 1 in rows 8..15, 24..31
+    auto store_z = [&](int zb, const f16x8 (&v)[KB]) {
+      f16 *zt = sm.z[zb][w] + l32 * ZSTRIDE + 64 * hf;
+      f16 *ze = zt + zsw, *zo = zt - zsw;  // even and odd kb
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(((kb & 1) ? zo : ze) + 8 * kb) = v[kb];
+    };
+    // partial scores -> sm.sp[w][mt][l]: four 16-byte stores per
+    // accumulator; quad j of lane l at quad j ^ ((l >> 2) & 3)
+    const int p_sw = (l >> 2) & 3;
+    auto publish = [&]() {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4 *>(&sm.sp[w][mt][l][4 * (j ^ p_sw)]) =
+              f32x4{sacc[mt][4 * j], sacc[mt][4 * j + 1], sacc[mt][4 * j + 2], sacc[mt][4 * j + 3]};
+    };
+    auto scores = [&]() {
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bz[kb], aq[mt][kb], sacc[mt], 0, 0, 0);
+    };
+    RawTile raw;
+    {
+      // prologue: tile 0 scored, published and in Z buffer 0; tile 1
+      // dequantised; tile 2 in flight
+      const RawTile r0 = load_tile<G>(a, tile_slot(0), w, hf);
+      const RawTile r1 = load_tile<G>(a, tile_slot(1), w, hf);
+      raw = load_tile<G>(a, tile_slot(2), w, hf);
+      dequant<G>(r0, bz);
+      scores();
+      store_z(0, bz);
+      publish();
+      dequant<G>(r1, bz);
+    }
+    lds_barrier();  // P0: partial scores and Z of tile 0
+    for (int i = 0; i < n_tiles; ++i) {
+      // X: scores of tile i+1 (harmless recompute past the end), its Z to
+      // the buffer the consumers read at tile i-1 (done by barrier B of i-1)
+      scores();
+      store_z((i & 1) ^ 1, bz);
+      lds_barrier();  // A: P of tile i; the consumers have read the partial scores of tile i
+      // Y: publish tile i+1, dequantise tile i+2, request tile i+3
+      publish();
+      dequant<G>(raw, bz);
+      raw = load_tile<G>(a, tile_slot(i + 3), w, hf);
+      lds_barrier();  // B: partial scores of tile i+1; P and Z of tile i consumed
+    }
+    lds_barrier();  // E: 1 / l of every row
+    return;
+  }
+
+  // ---------------- consumers ----------------
+  // softmax ownership: lane -> (row, 8 consecutive tokens); a row's four lanes
+  // form a quad
+  const int s_row = 16 * w + (l >> 2), s_k8 = l & 3;
+  const int s_m = rb * ROWS + s_row;
+  int s_vis = -1;  // padding rows are never visible
+  if (s_m < M) s_vis = a.causal ? (L - a.Tq + s_m / H + 1) : L;
+  const int s_lim = min(it.t1, s_vis);  // tokens < s_lim are visible to this row
+  float m_run = -INFINITY, l_run = 0.0f;
+  // tiles [0, full_tiles) are visible to every row of this wave: no masking
+  int vmin = s_lim - it.t0;
+  for (int off = 32; off > 0; off >>= 1) vmin = min(vmin, __shfl_xor(vmin, off));
+  const int full_tiles = __builtin_amdgcn_readfirstlane(vmin > 0 ? vmin / TT : 0);
+  // Summed scores of the owned (row, 8 tokens): token 8j + 4h + e of row r
+  // sits in lane (r % 32) + 32h, slot 4j + e, of accumulator r / 32; each
+  // lane's four 16-byte quads are stored XOR-swizzled by bits 2-3 of the lane
+  const int s_lane = s_row & 31, s_mt = s_row >> 5;
+  const int s_q = s_k8 ^ ((s_lane >> 2) & 3);
+
+  f32x16 o[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x16{};
+  const int g16 = l >> 4, s16 = l & 15;
+  const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);    // transposing-load source row
+  const int pv_col = (16 * (g16 & 1) + 4 * (s16 & 3)) ^ (8 * ((g16 >> 1) & 1));
+  lds_barrier();  // P0
+  for (int i = 0; i < n_tiles; ++i) {
+    const int buf = i & 1;
+    // X: the summed scores of tile i, online softmax, P
+    float s[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[0][s_mt][s_lane + 32 * h][4 * s_q]);
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww)
+        acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[ww][s_mt][s_lane + 32 * h][4 * s_q]);
+      s[4 * h] = acc4[0];
+      s[4 * h + 1] = acc4[1];
+      s[4 * h + 2] = acc4[2];
+      s[4 * h + 3] = acc4[3];
+    }
+    if (i >= full_tiles) {
+      const int ncnt = s_lim - (it.t0 + i * TT + 8 * s_k8);  // visible tokens among my 8
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = (e < ncnt) ? s[e] : -INFINITY;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
+    tmax = reduce4<true>(tmax);
+    const bool need = tmax > m_run + kRescaleThreshold;   // true on the first visible tile
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
+    // a row's O is still zero until its first visible tile: no rescale then
+    const bool scale_o = need && m_run != -INFINITY;
+    m_run = need ? tmax : m_run;
+    const float m_sub = (m_run == -INFINITY) ? 0.0f : m_run;
+    float psum = 0.0f;
+    f16x8 pv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(s[e] - m_sub);  // masked: exp2(-inf) = 0
+      psum += p;
+      pv[e] = static_cast<f16>(p);
+    }
+    psum = reduce4<false>(psum);
+    l_run = l_run * alpha + psum;
+    *reinterpret_cast<f16x8 *>(sm.p + s_row * PRSTRIDE + 8 * s_k8) = pv;
+    // every lane stores (a row's lanes store equal values to one address)
+    sm.alpha[s_row] = alpha;
+    sm.resc[w] = __any(scale_o ? 1 : 0);
+    lds_barrier();  // A: P, alpha and the rescale flags of tile i
+    // Y: O = alpha O + P Z for tile i
+    if (sm.resc[0] | sm.resc[1] | sm.resc[2] | sm.resc[3]) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float al = sm.alpha[32 * mt + 8 * (v >> 2) + 4 * hf + (v & 3)];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) o[mt][nt][v] *= al;
+        }
+    }
+    const f16 *zb_base = sm.z[buf][w] + pv_krow * ZSTRIDE + pv_col;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      f16x8 pa[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const f16 *z0 = zb_base + 16 * ks * ZSTRIDE + 32 * nt;
+        const f16x4 lo = ds_read_tr16(z0);
+        const f16x4 hi = ds_read_tr16(z0 + 4 * ZSTRIDE);
+        const f16x8 zb = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[mt], zb, o[mt][nt], 0, 0, 0);
+      }
+    }
+    lds_barrier();  // B
+  }
+  // ---- the partial (O / l in fp16, m, l) of this work item ----
+  if (s_k8 == 0) sm.inv_l[s_row] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  if (s_k8 == 0 && s_m < M) {
+    a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 0] = m_run;
+    a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 1] = l_run;
+  }
+  lds_barrier();  // E
+  // Each 32x32 accumulator tile (rows 32 mt.., the 32 contiguous channels
+  // 128 w + 32 nt..) goes through this slice's Z buffers (the producers are
+  // done with them) so that every lane then stores 4 contiguous channels of
+  // one row.  Staged position of (row, col): rows in pairs of 64 floats, the
+  // half chosen by bit 0 xor bit 2 of the row, so the 4-row-apart halves a
+  // store writes and the adjacent rows a 16-lane read takes fall in disjoint
+  // banks.
+  auto stage_pos = [](int row, int col) { return (row >> 1) * 64 + 32 * ((row ^ (row >> 2)) & 1) + col; };
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float *st = reinterpret_cast<float *>(sm.z[nt & 1][w]);
+      const int sl = 32 * nt + l32;  // slot of the wave's Z tile
+      const int col = slot_channel(sl >> 6, (sl & 63) >> 3, sl & 7) - 32 * nt;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st[stage_pos(8 * (v >> 2) + 4 * hf + (v & 3), col)] = o[mt][nt][v];
+      // the staged values cross lanes: stores above the reads (and the reads
+      // above the stores of the tile two steps on, which reuses this buffer)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 8 * j + (l >> 3), q = l & 7;
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(st + stage_pos(row, 4 * q));
+        const f16x4 y = __builtin_convertvector(x * sm.inv_l[32 * mt + row], f16x4);
+        const int m = rb * ROWS + 32 * mt + row;
+        if (m < M)  // ordinary stores: the combine kernel reads the rows next, often from the L2
+          *reinterpret_cast<f16x4 *>(a.part_o + (static_cast<int64_t>(item) * M + m) * R + 128 * w + 32 * nt + 4 * q) = y;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
+  TimedLaunch tl("splitk_decode", s);
+  const int M = a.d.num_heads * a.Tq;
+  const int rb_count = (M + ROWS - 1) / ROWS;
+  const int n_logical = a.max_items * rb_count;
+  const int grid = ((n_logical + 7) / 8) * 8;
+  if (a.d.group_size == 32)
+    splitk_ws_kernel<32><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+  else
+    splitk_ws_kernel<16><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,161 @@
+// Tile machinery shared by the MFMA decode kernels (r = 512, d_r = 64
+// latent layers; the grouped-query kernel reuses the dequantisation and the
+// Z tile layout): constants, cache-tile loads, the exact INT2 -> fp16
+// dequantisation, LDS layout and small wave-level helpers.
+//
+// [OSCAR issue #10, maintainer reply, "How the rotation adapts to the
+// latent"]: the cached latent is the rotated INT2 latent, dequantised as
+// zero + scale * code with the group's fp16 side information.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mla {
+namespace {
+
+
+constexpr int R = 512;
+constexpr int DR = 64;
+constexpr int ROWS = 64;        // query rows per workgroup
+constexpr int TT = 32;          // tokens per tile
+constexpr int KB = 9;           // K-blocks of 16 per wave: 8 latent + 1 rope
+// Z tile rows: 128 halves + 16 pad, so the four rows a transposing load
+// reads fall in separate banks.  16-byte chunk c of row t is stored at chunk
+// c ^ ((t >> 3) & 1): without it, the 16-byte stores of tokens t and t + 8
+// hit the same banks.
+constexpr int ZSTRIDE = 144;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x4 ds_read_tr16(const f16 *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<s16x4 __attribute__((address_space(3))) *>(
+          reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(f16x4, v);
+}
+
+// Workgroup barrier that only waits for this wave's LDS operations.  HIP's
+// __syncthreads() also waits for every outstanding global load, which would
+// force the next tile's prefetch to land at the first barrier of each tile.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// x *= al for a value the MFMA accumulates in an AGPR.  Written as inline asm
+// with an AGPR operand so the compiler keeps the accumulators in AGPRs and
+// cannot hoist their copies out of the (rarely taken) rescale branch.
+__device__ __forceinline__ void agpr_scale(float &x, float al) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\t"
+      "v_mul_f32 %1, %1, %2\n\t"
+      "v_accvgpr_write_b32 %0, %1"
+      : "+a"(x), "=&v"(t)
+      : "v"(al));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// all-reduce over the 4 lanes of a quad (DPP quad permutations)
+template <bool kMax>
+__device__ __forceinline__ float reduce4(float x) {
+  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
+  x = op(x, dpp_mov<0xB1>(x));  // quad_perm [1,0,3,2]
+  x = op(x, dpp_mov<0x4E>(x));  // quad_perm [2,3,0,1]
+  return x;
+}
+
+// Channel of latent K-slot e (0..7) in K-block kb (0..7) for lane half hf,
+// relative to the wave's first channel.  Matches the dequantisation below:
+// half2 j of block kb comes from byte j of code word kb/2 (channels
+// 16*(kb/2) + 4j .. + 3), taking its channels kb%2 and kb%2 + 2.
+__device__ __forceinline__ int slot_channel(int hf, int kb, int e) {
+  return 64 * hf + 16 * (kb >> 1) + 4 * (e >> 1) + (kb & 1) + 2 * (e & 1);
+}
+
+constexpr int PRSTRIDE = 40;    // halves per row of P (32 tokens + pad)
+
+// Tile state of the split-K kernel:
+//   z   per channel slice, dequantised latent tile [token][slot] (PV B
+//       operand), double-buffered
+//   sp  partial scores [slice][acc slot][lane (+4 for hf = 1)]
+//   p   P [row][token] (PV A operand), alpha per row, per-slice rescale flags
+struct __align__(16) Smem {
+  f16 z[2][4][TT * ZSTRIDE];
+  float sp[4][2][64][16];  // [wave][mt][lane][16 scores, 16-byte quads swizzled]
+  f16 p[ROWS * PRSTRIDE];
+  float alpha[ROWS];
+  float inv_l[ROWS];  // 1 / l of each row, for the normalised partial
+  int resc[4];
+};
+
+struct RawTile {
+  uint4 codes;
+  uint4 sz;     // 2 (G = 32) or 4 (G = 16) scale/zero words
+  uint4 rope;
+};
+
+template <int G>
+__device__ __forceinline__ RawTile load_tile(const DecodeArgs &a, int64_t slot, int w, int hf) {
+  RawTile t;
+  const uint32_t *codes32 = reinterpret_cast<const uint32_t *>(a.cache.codes);
+  t.codes = *reinterpret_cast<const uint4 *>(codes32 + slot * (R / 16) + w * 8 + hf * 4);
+  if (G == 32) {
+    const uint2 s2 = *reinterpret_cast<const uint2 *>(a.cache.scale_zero + (slot * (R / G) + (4 * w + 2 * hf)) * 2);
+    t.sz = uint4{s2.x, s2.y, 0u, 0u};
+  } else {
+    t.sz = *reinterpret_cast<const uint4 *>(a.cache.scale_zero + (slot * (R / G) + (8 * w + 4 * hf)) * 2);
+  }
+  t.rope = *reinterpret_cast<const uint4 *>(a.cache.k_rope + slot * DR + 16 * w + 8 * hf);
+  return t;
+}
+
+// Code byte pair -> exact fp16 pair: with every 2-bit code alone in a
+// nibble (bits 2-3 clear) the nibble is an OCP e2m1 number of value c/2,
+// and gfx950's packed fp4 -> f16 conversion with scale 2 returns (c_lo, c_hi)
+// exactly (low nibble in the low half).
+template <int BYTE>
+__device__ __forceinline__ f16x2 code_pair(uint32_t nibbles) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nibbles, 2.0f, BYTE);
+}
+
+// codes -> fp16 score B operands.  Per code word (16 channels): two masks
+// split the codes of channels (4j, 4j+2) and (4j+1, 4j+3) into nibbles, then
+// per pair one conversion and one fused fp16 multiply-add with the group's
+// (scale, zero): z_hat = zero + scale * c with one rounding.
+template <int G>
+__device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB]) {
+  const uint32_t cws[4] = {t.codes.x, t.codes.y, t.codes.z, t.codes.w};
+  const uint32_t szw[4] = {t.sz.x, t.sz.y, t.sz.z, t.sz.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t sz = szw[(G == 32) ? (q >> 1) : q];
+    const f16x2 sc = __builtin_bit_cast(f16x2, (sz & 0xffffu) * 0x10001u);
+    const f16x2 zr = __builtin_bit_cast(f16x2, (sz >> 16) * 0x10001u);
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      const uint32_t u = (cws[q] >> (2 * odd)) & 0x33333333u;
+      const f16x2 c0 = __builtin_elementwise_fma(code_pair<0>(u), sc, zr);
+      const f16x2 c1 = __builtin_elementwise_fma(code_pair<1>(u), sc, zr);
+      const f16x2 c2 = __builtin_elementwise_fma(code_pair<2>(u), sc, zr);
+      const f16x2 c3 = __builtin_elementwise_fma(code_pair<3>(u), sc, zr);
+      bz[2 * q + odd] = f16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+    }
+  }
+  const uint32_t rws[4] = {t.rope.x, t.rope.y, t.rope.z, t.rope.w};
+  f16x8 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = static_cast<f16>(__uint_as_float(rws[j] << 16));
+    v[2 * j + 1] = static_cast<f16>(__uint_as_float(rws[j] & 0xffff0000u));
+  }
+  bz[8] = v;
+}
+
+}  // namespace
+}  // namespace mla
