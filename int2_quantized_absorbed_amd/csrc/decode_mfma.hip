@@ -241,6 +241,8 @@ __global__ __launch_bounds__(64) void gqa_splitk_mfma_kernel(DecodeArgs a) {
   const int g16 = l >> 4, s16 = l & 15;
   const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);
   const int pv_col = (16 * (g16 & 1) + 4 * (s16 & 3)) ^ (8 * ((g16 >> 1) & 1));
+  // 16-byte chunk c of Z row t at chunk c ^ ((t >> 3) & 1): rows t and t + 8
+  // would otherwise take the same banks in one 16-lane store group
   const int zsw = 8 * ((l32 >> 3) & 1);
   auto tile_slot = [&](int i) -> int64_t {
     const int t = min(it.t0 + min(i, n_tiles - 1) * TT + l32, it.t1 - 1);

@@ -74,7 +74,11 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     };
     f16x8 bz[KB];
     f32x16 sacc[2];
-    const int zsw = 8 * ((l32 >> 3) & 1);  // chunk kb goes to kb ^ 1 in rows 8..15, 24..31
+    // Z tile rows are 288 bytes apart, so rows t and t + 4 fall on the same
+    // banks; 16-byte chunk kb of row t is stored at chunk kb ^ (bit 2 ^ bit 3
+    // of t): the eight rows of an 8-lane store group, and the sixteen of a
+    // 16-lane group, then cover distinct banks
+    const int zsw = 8 * (((l32 >> 2) ^ (l32 >> 3)) & 1);
     auto store_z = [&](int zb, const f16x8 (&v)[KB]) {
       f16 *zt = sm.z[zb][w] + l32 * ZSTRIDE + 64 * hf;
       f16 *ze = zt + zsw, *zo = zt - zsw;  // even and odd kb
@@ -82,8 +86,9 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
       for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f16x8 *>(((kb & 1) ? zo : ze) + 8 * kb) = v[kb];
     };
     // partial scores -> sm.sp[w][mt][l]: four 16-byte stores per
-    // accumulator; quad j of lane l at quad j ^ ((l >> 2) & 3)
-    const int p_sw = (l >> 2) & 3;
+    // accumulator; lanes are 64 bytes apart, so quad j of lane l goes to quad
+    // j ^ ((l >> 1) & 3): any 8 consecutive lanes then store to distinct banks
+    const int p_sw = (l >> 1) & 3;
     auto publish = [&]() {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -146,9 +151,9 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
   const int full_tiles = __builtin_amdgcn_readfirstlane(vmin > 0 ? vmin / TT : 0);
   // Summed scores of the owned (row, 8 tokens): token 8j + 4h + e of row r
   // sits in lane (r % 32) + 32h, slot 4j + e, of accumulator r / 32; each
-  // lane's four 16-byte quads are stored XOR-swizzled by bits 2-3 of the lane
+  // lane's four 16-byte quads are stored XOR-swizzled by bits 1-2 of the lane
   const int s_lane = s_row & 31, s_mt = s_row >> 5;
-  const int s_q = s_k8 ^ ((s_lane >> 2) & 3);
+  const int s_q = s_k8 ^ ((s_lane >> 1) & 3);
 
   f32x16 o[2][4];
 #pragma unroll
@@ -157,7 +162,10 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x16{};
   const int g16 = l >> 4, s16 = l & 15;
   const int pv_krow = 8 * (g16 >> 1) + (s16 >> 2);    // transposing-load source row
+  // and column: rows pv_krow + 16 ks share bit 3 (the chunk swizzle's bit 3
+  // term); the second load's rows are 4 further on, so bit 2 flips too
   const int pv_col = (16 * (g16 & 1) + 4 * (s16 & 3)) ^ (8 * ((g16 >> 1) & 1));
+  const int pv_col_hi = pv_col ^ 8;
   lds_barrier();  // P0
   for (int i = 0; i < n_tiles; ++i) {
     const int buf = i & 1;
@@ -216,6 +224,7 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
         }
     }
     const f16 *zb_base = sm.z[buf][w] + pv_krow * ZSTRIDE + pv_col;
+    const f16 *zb_hi = sm.z[buf][w] + (pv_krow + 4) * ZSTRIDE + pv_col_hi;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       f16x8 pa[2];
@@ -224,9 +233,8 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
         pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const f16 *z0 = zb_base + 16 * ks * ZSTRIDE + 32 * nt;
-        const f16x4 lo = ds_read_tr16(z0);
-        const f16x4 hi = ds_read_tr16(z0 + 4 * ZSTRIDE);
+        const f16x4 lo = ds_read_tr16(zb_base + 16 * ks * ZSTRIDE + 32 * nt);
+        const f16x4 hi = ds_read_tr16(zb_hi + 16 * ks * ZSTRIDE + 32 * nt);
         const f16x8 zb = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)

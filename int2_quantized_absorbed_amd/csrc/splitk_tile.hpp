@@ -21,9 +21,9 @@ constexpr int ROWS = 64;        // query rows per workgroup
 constexpr int TT = 32;          // tokens per tile
 constexpr int KB = 9;           // K-blocks of 16 per wave: 8 latent + 1 rope
 // Z tile rows: 128 halves + 16 pad, so the four rows a transposing load
-// reads fall in separate banks.  16-byte chunk c of row t is stored at chunk
-// c ^ ((t >> 3) & 1): without it, the 16-byte stores of tokens t and t + 8
-// hit the same banks.
+// reads fall in separate banks.  The 16-byte chunks of a row are stored
+// XOR-swizzled by row bits (each kernel states its rule where it stores and
+// reads the tile).
 constexpr int ZSTRIDE = 144;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
