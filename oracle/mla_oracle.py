@@ -39,7 +39,10 @@ against the pages; its reduction to the unweighted rotation, a closed form
 and its invariants are pinned).  The sparse decode functions
 (``index_scores``, ``index_topk``, ``sparse_absorbed_attention``) follow a
 reading of an indexer the pages only name: pinned by brute force, sorting and
-the reduction to dense attention, unpinned against the pages.
+the reduction to dense attention, unpinned against the pages.  The rope-key
+variant (``quantize_rope_key`` and its entry layout) follows a reading of
+designs the pages only name: pinned by brute force, closed forms and
+hand-worked bytes, unpinned against the pages.
 """
 from __future__ import annotations
 
@@ -210,7 +213,7 @@ def rotate(c, r_apply) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-def group_params(z32, alpha, group):
+def group_params(z32, alpha, group, levels=3):
     """Per-(token, group) clip thresholds and fp16 side information, fp32.
 
     z32:   [n, r] float32 rotated latents.
@@ -221,7 +224,7 @@ def group_params(z32, alpha, group):
       mx, mn = max, min of the group
       mid = 0.5 * (mx + mn);  half = 0.5 * (mx - mn)
       lo = mid - (alpha * half);  hi = mid + (alpha * half)
-      scale32 = (hi - lo) / 3
+      scale32 = (hi - lo) / levels   (levels = 3 for INT2 codes 0..3)
       scale_h = fp16(scale32);  zero_h = fp16(lo)
     Returns scale_h, zero_h (float16 [n, r/G]) and scale32, lo (float32, the
     values before the fp16 rounding).
@@ -240,15 +243,16 @@ def group_params(z32, alpha, group):
     ah = a * half
     lo = mid - ah
     hi = mid + ah
-    scale32 = (hi - lo) / F32(3.0)
+    scale32 = (hi - lo) / F32(levels)
     return fp16_round(scale32), fp16_round(lo), scale32, lo
 
 
-def codes_from_params(z32, scale_h, zero_h, group):
-    """INT2 codes of each channel from its group's fp16 scale and zero, fp32.
+def codes_from_params(z32, scale_h, zero_h, group, levels=3):
+    """Codes of each channel from its group's fp16 scale and zero, fp32.
 
       u = (z - zero_h) / scale_h   (u = 0 when scale_h == 0)
-      code = min(3, max(0, rint(u)))   rint: ties to even; NaN -> 0
+      code = min(levels, max(0, rint(u)))   rint: ties to even; NaN -> 0
+    (levels = 3: the INT2 codes of the latent)
     Reading: the stored fp16 scale and zero are the ones used to quantise, so
     the stored side information and the codes agree.
     Returns codes [n, r] uint8 and u [n, r] float32.
@@ -262,7 +266,7 @@ def codes_from_params(z32, scale_h, zero_h, group):
     with np.errstate(divide="ignore", invalid="ignore"):
         u = (zg - z0) / s
     u = np.where(s == 0, F32(0.0), u).astype(F32)
-    code = np.clip(np.rint(u), F32(0.0), F32(3.0))
+    code = np.clip(np.rint(u), F32(0.0), F32(levels))
     code = np.where(np.isnan(code), F32(0.0), code)
     return code.astype(np.uint8).reshape(n, r), u.reshape(n, r)
 
@@ -603,6 +607,78 @@ def sparse_absorbed_attention(q_nope, q_rope, w_uk, w_uv, z_hat, k_rope, r_apply
 
 
 # --------------------------------------------------------------------------
+# Rope-key variant: the shared rope key stored quantised  [OSCAR issue #10,
+# the maintainer's later reply: two designs for the rope and the non-rope
+# parts of MLA are being benchmarked; neither is described]
+# --------------------------------------------------------------------------
+
+ROPE_GROUP = 16
+ROPE_BITS = 4
+
+
+def quantize_rope_key(k_rope, group=ROPE_GROUP, bits=ROPE_BITS):
+    """Quantise the shared rope key of each token, fp32 steps.
+
+    Reading: the rope key is kept out of the rotation (the rotation is fitted
+    on the latent c_kv only, and the rope key carries the positional
+    rotation the scores need as is) and quantised on its own in groups of
+    `group` consecutive dims with `bits`-bit codes, by the latent's
+    quantiser with no clipping (alpha = 1: the pages fit clip thresholds on
+    the rotated latent only) and 2^bits - 1 levels: mid, half, lo = mid -
+    half, hi = mid + half, scale = (hi - lo) / (2^bits - 1), fp16 scale and
+    zero, code = clamp(rint((x - zero) / scale), 0, 2^bits - 1).
+    k_rope [n, d_r] (bf16 values) -> dict with codes [n, d_r], scale_h and
+    zero_h [n, d_r/group] (float16), u, scale32, lo and x32 (the fp32 key).
+    """
+    x32 = np.asarray(k_rope, dtype=F32)
+    n, d = x32.shape
+    if d % group:
+        raise ValueError("qk_rope_head_dim must be a multiple of the rope group")
+    levels = (1 << bits) - 1
+    alpha = np.ones(d // group, dtype=F32)
+    scale_h, zero_h, scale32, lo = group_params(x32, alpha, group, levels)
+    codes, u = codes_from_params(x32, scale_h, zero_h, group, levels)
+    return dict(codes=codes, scale_h=scale_h, zero_h=zero_h, u=u,
+                scale32=scale32, lo=lo, x32=x32)
+
+
+def rope_entry_bytes(d_r, group=ROPE_GROUP, bits=ROPE_BITS):
+    """Bytes of one token's quantised rope key: codes, then (scale, zero)."""
+    return d_r * bits // 8 + 4 * (d_r // group)
+
+
+def pack_rope_entry(codes, scale_h, zero_h):
+    """Byte layout of a quantised rope key (4-bit codes): byte k holds dim
+    2k in bits 0..3 and dim 2k+1 in bits 4..7; then per group its fp16
+    scale and fp16 zero, little-endian.  Returns [n, rope_entry_bytes]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    n, d = c.shape
+    lo_hi = c.reshape(n, d // 2, 2).astype(np.uint16)
+    code_bytes = (lo_hi[:, :, 0] | (lo_hi[:, :, 1] << 4)).astype(np.uint8)
+    sz = np.stack([np.asarray(scale_h, np.float16), np.asarray(zero_h, np.float16)], axis=-1)
+    side = np.ascontiguousarray(sz).view(np.uint8).reshape(n, -1)
+    return np.concatenate([code_bytes, side], axis=1)
+
+
+def unpack_rope_entry(entry, d_r, group=ROPE_GROUP):
+    """Inverse of pack_rope_entry: codes [n, d_r], scale_h, zero_h."""
+    e = np.asarray(entry, dtype=np.uint8)
+    n = e.shape[0]
+    cb = e[:, : d_r // 2]
+    codes = np.empty((n, d_r), dtype=np.uint8)
+    codes[:, 0::2] = cb & 15
+    codes[:, 1::2] = cb >> 4
+    sz = np.ascontiguousarray(e[:, d_r // 2: d_r // 2 + 4 * (d_r // group)]).view(np.float16)
+    sz = sz.reshape(n, d_r // group, 2)
+    return codes, sz[..., 0], sz[..., 1]
+
+
+def dequantize_rope(codes, scale_h, zero_h, group=ROPE_GROUP):
+    """k_hat = zero + scale * code, in fp64 (dequantize with the rope group)."""
+    return dequantize(codes, scale_h, zero_h, group)
+
+
+# --------------------------------------------------------------------------
 # Cache sizing  [LLMH-SIZE; SHARD-MLA]
 # --------------------------------------------------------------------------
 
@@ -619,11 +695,13 @@ def full_head_values_per_token(num_heads, qk_nope_head_dim, qk_rope_head_dim,
 
 
 def int2_cache_bytes_per_token(kv_lora_rank, group, qk_rope_head_dim,
-                               index_head_dim=0):
+                               index_head_dim=0, rope_bits=0):
     """Physical bytes of one token in the INT2 cache (no padding).
 
     2-bit codes (r/4 bytes) + fp16 scale and zero per group (4 r/G bytes) +
-    bf16 rope key (2 d_r) + bf16 indexer key (2 d_idx).
+    the rope key: bf16 (2 d_r), or with rope_bits = 4 its quantised entry
+    (d_r/2 + 4 d_r/16) + bf16 indexer key (2 d_idx).
     """
+    rope = 2 * qk_rope_head_dim if rope_bits == 0 else rope_entry_bytes(qk_rope_head_dim)
     return (kv_lora_rank // 4 + 4 * (kv_lora_rank // group)
-            + 2 * qk_rope_head_dim + 2 * index_head_dim)
+            + rope + 2 * index_head_dim)
