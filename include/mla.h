@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -58,7 +58,22 @@ typedef enum mla_dtype { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype;
  * kv_lora_rank (r) > 0, r % group_size == 0, r % 16 == 0, group_size in
  * {16, 32}; 0 < qk_rope_head_dim (d_r) <= 256 and even; qk_nope_head_dim
  * (d_n), v_head_dim (d_v) in 1..1024; num_heads (H) >= 1;
- * index_head_dim (d_idx) >= 0 (0 = no indexer key). */
+ * index_head_dim (d_idx) >= 0 (0 = no indexer key); rope_bits 0 or 4, and
+ * with 4, d_r a multiple of 16.
+ *
+ * rope_bits selects how the cache stores the shared rope key:
+ *  0  bf16, d_r values (2 d_r bytes);
+ *  4  the rope-key variant [OSCAR issue #10, the maintainer's later reply,
+ *     which names two designs for the rope and non-rope parts without
+ *     describing them].  The reading implemented: the rope key stays out of
+ *     the rotation and is quantised on its own, in groups of 16 dims, with
+ *     4-bit codes by the latent quantiser without clipping (15 levels):
+ *     mid = 0.5(mx+mn), half = 0.5(mx-mn), lo = mid - half, hi = mid + half,
+ *     scale = fp16((hi-lo)/15), zero = fp16(lo), code = min(15, max(0,
+ *     rint((x - zero)/scale))) (0 when scale == 0), in fp32 without fused
+ *     multiply-add.  Entry: d_r/2 code bytes (dim 2k in bits 0..3 of byte k,
+ *     dim 2k+1 in bits 4..7), then per group its fp16 scale and fp16 zero:
+ *     d_r/2 + d_r/4 bytes (48 at d_r = 64, against 128 in bf16). */
 typedef struct mla_dims {
   int32_t kv_lora_rank;
   int32_t qk_rope_head_dim;
@@ -67,6 +82,7 @@ typedef struct mla_dims {
   int32_t num_heads;
   int32_t group_size;
   int32_t index_head_dim;
+  int32_t rope_bits;
 } mla_dims;
 
 /* The INT2 latent cache: structure-of-arrays over token slots
@@ -75,9 +91,12 @@ typedef struct mla_dims {
  *   codes[s*r/4 .. +r/4)        2-bit codes; channel 4k+i at bits 2i..2i+1 of
  *                               byte k (channels of the rotated latent)
  *   scale_zero[s*(r/G)*2 ..]    per group g: [2g] = scale, [2g+1] = zero, fp16
- *   k_rope[s*d_r ..]            shared rope key, bf16, stored unquantised
+ *   k_rope                      shared rope key: rope_bits 0: bf16 at
+ *                               k_rope[s*d_r ..]; rope_bits 4: the quantised
+ *                               entry (see mla_dims) at byte s*(d_r/2 + d_r/4)
  *   idx_key[s*d_idx ..]         indexer key, bf16 (NULL when d_idx == 0)
- * i.e. r/4 + 4r/G + 2d_r (+ 2d_idx) bytes per token, no padding.
+ * i.e. r/4 + 4r/G + rope (2d_r, or d_r/2 + d_r/4) (+ 2d_idx) bytes per
+ * token, no padding.
  * Dequantised value: z_hat = zero + scale * code.  All pointers device. */
 typedef struct mla_cache {
   uint8_t *codes;
@@ -203,7 +222,8 @@ mla_status mla_fold_absorb_weights(const mla_dims *dims, const uint16_t *w_uk,
  *   mid = 0.5(mx+mn); half = 0.5(mx-mn); lo = mid - a*half; hi = mid + a*half
  *   scale = fp16((hi-lo)/3); zero = fp16(lo)
  *   code = min(3, max(0, rint((z - zero)/scale)))   (0 when scale == 0)
- * and write codes, (scale, zero), k_rope[i] and idx_key[i] to the slot.
+ * and write codes, (scale, zero), k_rope[i] (bf16, or with rope_bits = 4
+ * its quantised entry) and idx_key[i] to the slot.
  *   latent        device [n][r] bf16 or fp32
  *   k_rope        device [n][d_r] bf16
  *   idx_key       device [n][d_idx] bf16 (NULL iff d_idx == 0)

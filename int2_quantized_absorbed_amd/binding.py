@@ -33,7 +33,7 @@ class MlaError(RuntimeError):
 class mla_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kv_lora_rank", "qk_rope_head_dim", "qk_nope_head_dim", "v_head_dim",
-        "num_heads", "group_size", "index_head_dim")]
+        "num_heads", "group_size", "index_head_dim", "rope_bits")]
 
 
 class mla_cache(ctypes.Structure):
@@ -178,10 +178,17 @@ class Dims:
     num_heads: int
     group_size: int
     index_head_dim: int = 0
+    rope_bits: int = 0   # 0: bf16 rope key in the cache; 4: the 4-bit rope-key entry
 
     def c(self) -> mla_dims:
         return mla_dims(self.kv_lora_rank, self.qk_rope_head_dim, self.qk_nope_head_dim, self.v_head_dim,
-                        self.num_heads, self.group_size, self.index_head_dim)
+                        self.num_heads, self.group_size, self.index_head_dim, self.rope_bits)
+
+    @property
+    def rope_entry_bytes(self):
+        """Cache bytes of one token's rope key."""
+        d = self.qk_rope_head_dim
+        return 2 * d if self.rope_bits == 0 else d // 2 + d // 4
 
     @property
     def r(self):
@@ -201,7 +208,10 @@ class Cache:
         self.capacity = int(capacity)
         self.codes = torch.zeros((capacity, r // 4), dtype=torch.uint8, device=device)
         self.scale_zero = torch.zeros((capacity, r // g, 2), dtype=torch.float16, device=device)
-        self.k_rope = torch.zeros((capacity, dims.qk_rope_head_dim), dtype=torch.bfloat16, device=device)
+        if dims.rope_bits == 0:
+            self.k_rope = torch.zeros((capacity, dims.qk_rope_head_dim), dtype=torch.bfloat16, device=device)
+        else:  # the 4-bit rope-key entries, bytes
+            self.k_rope = torch.zeros((capacity, dims.rope_entry_bytes), dtype=torch.uint8, device=device)
         self.idx_key = (torch.zeros((capacity, dims.index_head_dim), dtype=torch.bfloat16, device=device)
                         if dims.index_head_dim else None)
 

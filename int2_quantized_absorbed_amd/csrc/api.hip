@@ -50,6 +50,14 @@ bool dims_valid(const mla_dims *d, std::string *why) {
     *why = "qk_rope_head_dim must be even and in 1..256";
     return false;
   }
+  if (d->rope_bits != 0 && d->rope_bits != 4) {
+    *why = "rope_bits must be 0 (bf16 rope key) or 4";
+    return false;
+  }
+  if (d->rope_bits == 4 && d->qk_rope_head_dim % 16 != 0) {
+    *why = "a 4-bit rope key needs qk_rope_head_dim a multiple of 16";
+    return false;
+  }
   if (d->qk_nope_head_dim <= 0 || d->qk_nope_head_dim > 1024 || d->v_head_dim <= 0 ||
       d->v_head_dim > 1024) {
     *why = "qk_nope_head_dim and v_head_dim must be in 1..1024";
@@ -267,6 +275,7 @@ mla_dims gqa_latent_dims(const gqa_dims &g) {
   mla_dims d{};
   d.kv_lora_rank = g.head_dim;
   d.qk_rope_head_dim = 0;
+  d.rope_bits = 0;
   d.qk_nope_head_dim = g.head_dim;
   d.v_head_dim = g.head_dim;
   d.num_heads = g.num_q_heads / g.num_kv_heads;

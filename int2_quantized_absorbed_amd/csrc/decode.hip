@@ -141,7 +141,19 @@ __global__ __launch_bounds__(256) void splitk_valu_kernel(DecodeArgs a, int row_
     for (int e = tid; e < TT * dr; e += 256) {
       const int tk = e / dr, k = e % dr;
       const int tau = t0 + tk;
-      z_s[tk * KP + r + k] = (tau < it.t1) ? bf16_to_f32(a.cache.k_rope[slot_of(tau) * dr + k]) : 0.0f;
+      float v = 0.0f;
+      if (tau < it.t1) {
+        if (a.d.rope_bits == 4) {  // 4-bit rope key: zero + scale * code, one rounding
+          const uint8_t *en = reinterpret_cast<const uint8_t *>(a.cache.k_rope) + slot_of(tau) * (dr / 2 + dr / 4);
+          const uint32_t code = (en[k >> 1] >> (4 * (k & 1))) & 15u;
+          const uint32_t sz = *reinterpret_cast<const uint32_t *>(en + dr / 2 + 4 * (k >> 4));
+          v = fmaf(static_cast<float>(bits_f16(static_cast<uint16_t>(sz & 0xffffu))), static_cast<float>(code),
+                   static_cast<float>(bits_f16(static_cast<uint16_t>(sz >> 16))));
+        } else {
+          v = bf16_to_f32(a.cache.k_rope[slot_of(tau) * dr + k]);
+        }
+      }
+      z_s[tk * KP + r + k] = v;
     }
     __syncthreads();
     if (scorer) {

@@ -35,7 +35,7 @@ namespace {
 // units), as in splitk_mfma_kernel.  The output accumulators live in VGPRs
 // (this translation unit is built with the VGPR form of MFMA), so the
 // rescale is ordinary code and the compiler inserts the MFMA read hazards.
-template <int G>
+template <int G, bool RQ>
 __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_count, int n_logical) {
   __shared__ Smem sm;
   const int per_xcd = (n_logical + 7) / 8;
@@ -110,14 +110,14 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     {
       // prologue: tile 0 scored, published and in Z buffer 0; tile 1
       // dequantised; tile 2 in flight
-      const RawTile r0 = load_tile<G>(a, tile_slot(0), w, hf);
-      const RawTile r1 = load_tile<G>(a, tile_slot(1), w, hf);
-      raw = load_tile<G>(a, tile_slot(2), w, hf);
-      dequant<G>(r0, bz);
+      const RawTile r0 = load_tile<G, RQ>(a, tile_slot(0), w, hf);
+      const RawTile r1 = load_tile<G, RQ>(a, tile_slot(1), w, hf);
+      raw = load_tile<G, RQ>(a, tile_slot(2), w, hf);
+      dequant<G, RQ>(r0, bz);
       scores();
       store_z(0, bz);
       publish();
-      dequant<G>(r1, bz);
+      dequant<G, RQ>(r1, bz);
     }
     lds_barrier();  // P0: partial scores and Z of tile 0
     for (int i = 0; i < n_tiles; ++i) {
@@ -128,8 +128,8 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
       lds_barrier();  // A: P of tile i; the consumers have read the partial scores of tile i
       // Y: publish tile i+1, dequantise tile i+2, request tile i+3
       publish();
-      dequant<G>(raw, bz);
-      raw = load_tile<G>(a, tile_slot(i + 3), w, hf);
+      dequant<G, RQ>(raw, bz);
+      raw = load_tile<G, RQ>(a, tile_slot(i + 3), w, hf);
       lds_barrier();  // B: partial scores of tile i+1; P and Z of tile i consumed
     }
     lds_barrier();  // E: 1 / l of every row
@@ -291,10 +291,18 @@ hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
   const int rb_count = (M + ROWS - 1) / ROWS;
   const int n_logical = a.max_items * rb_count;
   const int grid = ((n_logical + 7) / 8) * 8;
-  if (a.d.group_size == 32)
-    splitk_ws_kernel<32><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
-  else
-    splitk_ws_kernel<16><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+  const bool rq = a.d.rope_bits == 4;
+  if (a.d.group_size == 32) {
+    if (rq)
+      splitk_ws_kernel<32, true><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+    else
+      splitk_ws_kernel<32, false><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+  } else {
+    if (rq)
+      splitk_ws_kernel<16, true><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+    else
+      splitk_ws_kernel<16, false><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+  }
   return hipGetLastError();
 }
 

@@ -97,10 +97,17 @@ struct __align__(16) Smem {
 struct RawTile {
   uint4 codes;
   uint4 sz;     // 2 (G = 32) or 4 (G = 16) scale/zero words
-  uint4 rope;
+  uint4 rope;   // 8 bf16 rope values, or (4-bit rope key) .x 8 codes, .y (scale, zero)
 };
 
-template <int G>
+// Bytes of one token's 4-bit rope-key entry at d_r = 64: 32 code bytes, then
+// the (scale, zero) words of its 4 groups of 16 dims.
+constexpr int kRopeEntry = DR / 2 + DR / 4;
+
+// Tile operands of lane (token, lane half hf) of channel slice w: 64 latent
+// channels' codes, their groups' side information and 8 rope dims (16w +
+// 8hf ..).  RQ: the rope key is stored as 4-bit codes of group w.
+template <int G, bool RQ = false>
 __device__ __forceinline__ RawTile load_tile(const DecodeArgs &a, int64_t slot, int w, int hf) {
   RawTile t;
   const uint32_t *codes32 = reinterpret_cast<const uint32_t *>(a.cache.codes);
@@ -111,7 +118,13 @@ __device__ __forceinline__ RawTile load_tile(const DecodeArgs &a, int64_t slot, 
   } else {
     t.sz = *reinterpret_cast<const uint4 *>(a.cache.scale_zero + (slot * (R / G) + (8 * w + 4 * hf)) * 2);
   }
-  t.rope = *reinterpret_cast<const uint4 *>(a.cache.k_rope + slot * DR + 16 * w + 8 * hf);
+  if (RQ) {
+    const uint8_t *e = reinterpret_cast<const uint8_t *>(a.cache.k_rope) + slot * kRopeEntry;
+    t.rope = uint4{*reinterpret_cast<const uint32_t *>(e + 8 * w + 4 * hf),
+                   *reinterpret_cast<const uint32_t *>(e + DR / 2 + 4 * w), 0u, 0u};
+  } else {
+    t.rope = *reinterpret_cast<const uint4 *>(a.cache.k_rope + slot * DR + 16 * w + 8 * hf);
+  }
   return t;
 }
 
@@ -128,7 +141,7 @@ __device__ __forceinline__ f16x2 code_pair(uint32_t nibbles) {
 // split the codes of channels (4j, 4j+2) and (4j+1, 4j+3) into nibbles, then
 // per pair one conversion and one fused fp16 multiply-add with the group's
 // (scale, zero): z_hat = zero + scale * c with one rounding.
-template <int G>
+template <int G, bool RQ = false>
 __device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB]) {
   const uint32_t cws[4] = {t.codes.x, t.codes.y, t.codes.z, t.codes.w};
   const uint32_t szw[4] = {t.sz.x, t.sz.y, t.sz.z, t.sz.w};
@@ -147,12 +160,30 @@ __device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB]) {
       bz[2 * q + odd] = f16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
     }
   }
-  const uint32_t rws[4] = {t.rope.x, t.rope.y, t.rope.z, t.rope.w};
   f16x8 v;
+  if (RQ) {
+    // 4-bit rope codes: byte j holds dims 2j (low nibble) and 2j+1.  The
+    // fp16 with bits 0x6400 | n is 1024 + n exactly, so subtracting 1024
+    // gives the code; then k_hat = zero + scale * code with one rounding.
+    const uint32_t c = t.rope.x, sz = t.rope.y;
+    const f16x2 sc = __builtin_bit_cast(f16x2, (sz & 0xffffu) * 0x10001u);
+    const f16x2 zr = __builtin_bit_cast(f16x2, (sz >> 16) * 0x10001u);
+    const f16x2 k1024 = f16x2{static_cast<f16>(1024.0f), static_cast<f16>(1024.0f)};
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[2 * j] = static_cast<f16>(__uint_as_float(rws[j] << 16));
-    v[2 * j + 1] = static_cast<f16>(__uint_as_float(rws[j] & 0xffff0000u));
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t b = c >> (8 * j);
+      const uint32_t pair = (b & 0xfu) | (((b >> 4) & 0xfu) << 16) | 0x64006400u;
+      const f16x2 h = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, pair) - k1024, sc, zr);
+      v[2 * j] = h[0];
+      v[2 * j + 1] = h[1];
+    }
+  } else {
+    const uint32_t rws[4] = {t.rope.x, t.rope.y, t.rope.z, t.rope.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = static_cast<f16>(__uint_as_float(rws[j] << 16));
+      v[2 * j + 1] = static_cast<f16>(__uint_as_float(rws[j] & 0xffff0000u));
+    }
   }
   bz[8] = v;
 }

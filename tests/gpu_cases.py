@@ -101,3 +101,23 @@ def oracle_decode(layer: Layer, case: dict, tq: int, causal: bool, scale: float,
                                    layer.R_apply, scale, causal=causal)
         out[b] = (o, l)
     return out
+
+
+def random_rope_entries(rng, n: int, d_r: int):
+    """Random 4-bit rope-key entries (no quantiser involved): codes uniform in
+    0..15, fp16 scales in [1e-3, 0.5], zeros in [-2, 0.5], per group of 16.
+    Returns (entries [n, d_r/2 + d_r/4] uint8, the dequantised keys fp64)."""
+    g = d_r // O.ROPE_GROUP
+    codes = rng.integers(0, 16, size=(n, d_r), dtype=np.uint8)
+    scale = np.exp(rng.uniform(np.log(1e-3), np.log(0.5), size=(n, g))).astype(np.float16)
+    zero = rng.uniform(-2.0, 0.5, size=(n, g)).astype(np.float16)
+    return O.pack_rope_entry(codes, scale, zero), O.dequantize_rope(codes, scale, zero)
+
+
+def upload_cache_rope4(dims: M.Dims, case: dict, entries) -> M.Cache:
+    """A cache with 4-bit rope-key entries (dims.rope_bits == 4)."""
+    c = M.Cache(dims, case["cap"], DEV)
+    c.codes.copy_(torch.from_numpy(case["codes"]))
+    c.scale_zero.copy_(torch.from_numpy(case["sz"]))
+    c.k_rope.copy_(torch.from_numpy(np.ascontiguousarray(entries)))
+    return c

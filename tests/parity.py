@@ -92,3 +92,33 @@ def row_rel_err(out, ref):
     num = np.max(np.abs(out - ref), axis=-1)
     den = np.max(np.abs(ref), axis=-1)
     return num / np.maximum(den, 1e-300)
+
+
+def compare_rope(gpu_entries, ref: dict, d_r: int) -> dict:
+    """4-bit rope-key entries [n, d_r/2 + d_r/4] uint8 against
+    O.quantize_rope_key: codes bit-exact outside the BAND around the
+    boundaries k + 1/2 (k = 0..14); fp16 scale / zero by the side-info rule
+    above (a one-ulp midpoint difference, codes then judged on the GPU's own
+    scale and zero)."""
+    group = O.ROPE_GROUP
+    gc, gs, gz = O.unpack_rope_entry(gpu_entries, d_r)
+    os_, oz = ref["scale_h"], ref["zero_h"]
+    s_diff = gs.view(np.uint16) != os_.view(np.uint16)
+    z_diff = gz.view(np.uint16) != oz.view(np.uint16)
+    n = gc.shape[0]
+    gmag = np.max(np.abs(ref["x32"].astype(np.float64)).reshape(n, -1, group), axis=2)
+    sz_bad = (s_diff & ~_f16_midpoint_ok(gs, os_, ref["scale32"], gmag)) | \
+             (z_diff & ~_f16_midpoint_ok(gz, oz, ref["lo"], gmag))
+    grp_diff = s_diff | z_diff
+    u_ref, codes_ref = ref["u"].copy(), ref["codes"].copy()
+    if grp_diff.any():
+        c2, u2 = O.codes_from_params(ref["x32"], gs, gz, group, levels=15)
+        mask = np.repeat(grp_diff, group, axis=1)
+        u_ref = np.where(mask, u2, u_ref)
+        codes_ref = np.where(mask, c2, codes_ref)
+    bounds = np.arange(15) + 0.5
+    near = np.min(np.abs(u_ref.astype(np.float64)[..., None] - bounds), axis=-1) < BAND
+    mism = gc != codes_ref
+    viol = mism & ~near
+    return dict(n=gc.size, code_mismatch=int(mism.sum()), excused=int((mism & near).sum()),
+                violations=int(viol.sum()), sz_diff=int(grp_diff.sum()), sz_violations=int(sz_bad.sum()))

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
     assert "mla_calibrate_rotation" in names and "mla_fit_clip" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert M.mla_abi_version() == 1
+    assert M.mla_abi_version() == 2
 
 
 def test_status_strings():
@@ -31,7 +31,7 @@ def test_status_strings():
 
 def _dims(**kw):
     base = dict(kv_lora_rank=512, qk_rope_head_dim=64, qk_nope_head_dim=128, v_head_dim=128,
-                num_heads=128, group_size=32, index_head_dim=0)
+                num_heads=128, group_size=32, index_head_dim=0, rope_bits=0)
     base.update(kw)
     return Bd.mla_dims(*base.values())
 
@@ -40,6 +40,7 @@ BAD_DIMS = [
     dict(kv_lora_rank=0), dict(kv_lora_rank=100), dict(group_size=8), dict(group_size=64),
     dict(kv_lora_rank=48, group_size=32), dict(qk_rope_head_dim=0), dict(qk_rope_head_dim=3),
     dict(num_heads=0), dict(index_head_dim=-2), dict(v_head_dim=0),
+    dict(rope_bits=2), dict(rope_bits=8), dict(rope_bits=4, qk_rope_head_dim=40),
 ]
 
 
