@@ -35,8 +35,14 @@ namespace {
 // units), as in splitk_mfma_kernel.  The output accumulators live in VGPRs
 // (this translation unit is built with the VGPR form of MFMA), so the
 // rescale is ordinary code and the compiler inserts the MFMA read hazards.
-template <int G, bool RQ>
-__global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_count, int n_logical) {
+// MT: 32-row MFMA tiles per block (2: 64 query rows; 1: 32 rows, for at most
+// 32 rows in all, which would otherwise be mostly padding).  With MT = 1 the
+// consumers 2 and 3 own no softmax rows.  rb_count counts blocks of 32 MT
+// rows; the query operands are packed in 64-row blocks (rb_count64 of them).
+template <int G, bool RQ, int MT>
+__global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_count, int rb_count64,
+                                                           int n_logical) {
+  constexpr int BROWS = 32 * MT;
   __shared__ Smem sm;
   const int per_xcd = (n_logical + 7) / 8;
   const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -57,14 +63,15 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
 
   if (producer) {
     // ---- Q~ operands (packed by the absorb kernel in exactly this order) ----
-    f16x8 aq[2][KB];
+    f16x8 aq[MT][KB];
     {
+      const int rb64 = (rb * BROWS) / ROWS, mt0 = ((rb * BROWS) % ROWS) / 32;
       const f16x8 *qp = reinterpret_cast<const f16x8 *>(a.qbuf) +
-                        ((static_cast<int64_t>(it.b) * rb_count + rb) * 4 + w) * (2 * KB * 64);
+                        ((static_cast<int64_t>(it.b) * rb_count64 + rb64) * 4 + w) * (2 * KB * 64);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) aq[mt][kb] = qp[(mt * KB + kb) * 64 + l];
+        for (int kb = 0; kb < KB; ++kb) aq[mt][kb] = qp[((mt0 + mt) * KB + kb) * 64 + l];
     }
     const int32_t *sel = a.sel ? a.sel + static_cast<int64_t>(it.b) * a.sel_stride : nullptr;
     auto tile_slot = [&](int i) -> int64_t {
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
       return base + (sel ? sel[t] : t);
     };
     f16x8 bz[KB];
-    f32x16 sacc[2];
+    f32x16 sacc[MT];
     // Z tile rows are 288 bytes apart, so rows t and t + 4 fall on the same
     // banks; 16-byte chunk kb of row t is stored at chunk kb ^ (bit 2 ^ bit 3
     // of t): the eight rows of an 8-lane store group, and the sixteen of a
@@ -91,19 +98,19 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     const int p_sw = (l >> 1) & 3;
     auto publish = [&]() {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           *reinterpret_cast<f32x4 *>(&sm.sp[w][mt][l][4 * (j ^ p_sw)]) =
               f32x4{sacc[mt][4 * j], sacc[mt][4 * j + 1], sacc[mt][4 * j + 2], sacc[mt][4 * j + 3]};
     };
     auto scores = [&]() {
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
           sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bz[kb], aq[mt][kb], sacc[mt], 0, 0, 0);
     };
     RawTile raw;
@@ -140,9 +147,10 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
   // softmax ownership: lane -> (row, 8 consecutive tokens); a row's four lanes
   // form a quad
   const int s_row = 16 * w + (l >> 2), s_k8 = l & 3;
-  const int s_m = rb * ROWS + s_row;
+  const bool s_own = s_row < BROWS;  // false: a consumer with no softmax rows (MT = 1)
+  const int s_m = rb * BROWS + s_row;
   int s_vis = -1;  // padding rows are never visible
-  if (s_m < M) s_vis = a.causal ? (L - a.Tq + s_m / H + 1) : L;
+  if (s_own && s_m < M) s_vis = a.causal ? (L - a.Tq + s_m / H + 1) : L;
   const int s_lim = min(it.t1, s_vis);  // tokens < s_lim are visible to this row
   float m_run = -INFINITY, l_run = 0.0f;
   // tiles [0, full_tiles) are visible to every row of this wave: no masking
@@ -155,9 +163,9 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
   const int s_lane = s_row & 31, s_mt = s_row >> 5;
   const int s_q = s_k8 ^ ((s_lane >> 1) & 3);
 
-  f32x16 o[2][4];
+  f32x16 o[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x16{};
   const int g16 = l >> 4, s16 = l & 15;
@@ -210,12 +218,12 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     *reinterpret_cast<f16x8 *>(sm.p + s_row * PRSTRIDE + 8 * s_k8) = pv;
     // every lane stores (a row's lanes store equal values to one address)
     sm.alpha[s_row] = alpha;
-    sm.resc[w] = __any(scale_o ? 1 : 0);
+    sm.resc[w] = __any((scale_o && s_own) ? 1 : 0);
     lds_barrier();  // A: P, alpha and the rescale flags of tile i
     // Y: O = alpha O + P Z for tile i
     if (sm.resc[0] | sm.resc[1] | sm.resc[2] | sm.resc[3]) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float al = sm.alpha[32 * mt + 8 * (v >> 2) + 4 * hf + (v & 3)];
@@ -227,9 +235,9 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     const f16 *zb_hi = sm.z[buf][w] + (pv_krow + 4) * ZSTRIDE + pv_col_hi;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      f16x8 pa[2];
+      f16x8 pa[MT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
         pa[mt] = *reinterpret_cast<const f16x8 *>(sm.p + (32 * mt + l32) * PRSTRIDE + 16 * ks + 8 * hf);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
         const f16x4 hi = ds_read_tr16(zb_hi + 16 * ks * ZSTRIDE + 32 * nt);
         const f16x8 zb = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
           o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[mt], zb, o[mt][nt], 0, 0, 0);
       }
     }
@@ -245,7 +253,7 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
   }
   // ---- the partial (O / l in fp16, m, l) of this work item ----
   if (s_k8 == 0) sm.inv_l[s_row] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-  if (s_k8 == 0 && s_m < M) {
+  if (s_k8 == 0 && s_own && s_m < M) {
     a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 0] = m_run;
     a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 1] = l_run;
   }
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
   // banks.
   auto stage_pos = [](int row, int col) { return (row >> 1) * 64 + 32 * ((row ^ (row >> 2)) & 1) + col; };
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       float *st = reinterpret_cast<float *>(sm.z[nt & 1][w]);
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
         const int row = 8 * j + (l >> 3), q = l & 7;
         const f32x4 x = *reinterpret_cast<const f32x4 *>(st + stage_pos(row, 4 * q));
         const f16x4 y = __builtin_convertvector(x * sm.inv_l[32 * mt + row], f16x4);
-        const int m = rb * ROWS + 32 * mt + row;
+        const int m = rb * BROWS + 32 * mt + row;
         if (m < M)  // ordinary stores: the combine kernel reads the rows next, often from the L2
           *reinterpret_cast<f16x4 *>(a.part_o + (static_cast<int64_t>(item) * M + m) * R + 128 * w + 32 * nt + 4 * q) = y;
       }
@@ -288,21 +296,32 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
 hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
   TimedLaunch tl("splitk_decode", s);
   const int M = a.d.num_heads * a.Tq;
-  const int rb_count = (M + ROWS - 1) / ROWS;
-  const int n_logical = a.max_items * rb_count;
+  const int mt = M <= 32 ? 1 : 2;  // 32-row blocks when all rows fit one
+  const int rb_count = (M + 32 * mt - 1) / (32 * mt);
+  const int rb_count64 = (M + ROWS - 1) / ROWS;
+  // the plan holds at most max(target, sequences) items: size the grid by
+  // that, not by the workspace's item capacity, or the XCD-ordered block
+  // numbering would hand whole XCDs only blocks past the plan
+  const int n_items = std::min(a.max_items, std::max(a.target_items, a.B));
+  const int n_logical = n_items * rb_count;
   const int grid = ((n_logical + 7) / 8) * 8;
   const bool rq = a.d.rope_bits == 4;
+#define MLA_SPLITK_LAUNCH(G_, RQ_, MT_) \
+  splitk_ws_kernel<G_, RQ_, MT_><<<grid, 512, 0, s>>>(a, rb_count, rb_count64, n_logical)
   if (a.d.group_size == 32) {
-    if (rq)
-      splitk_ws_kernel<32, true><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
-    else
-      splitk_ws_kernel<32, false><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+    if (mt == 1) {
+      if (rq) MLA_SPLITK_LAUNCH(32, true, 1); else MLA_SPLITK_LAUNCH(32, false, 1);
+    } else {
+      if (rq) MLA_SPLITK_LAUNCH(32, true, 2); else MLA_SPLITK_LAUNCH(32, false, 2);
+    }
   } else {
-    if (rq)
-      splitk_ws_kernel<16, true><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
-    else
-      splitk_ws_kernel<16, false><<<grid, 512, 0, s>>>(a, rb_count, n_logical);
+    if (mt == 1) {
+      if (rq) MLA_SPLITK_LAUNCH(16, true, 1); else MLA_SPLITK_LAUNCH(16, false, 1);
+    } else {
+      if (rq) MLA_SPLITK_LAUNCH(16, true, 2); else MLA_SPLITK_LAUNCH(16, false, 2);
+    }
   }
+#undef MLA_SPLITK_LAUNCH
   return hipGetLastError();
 }
 
