@@ -26,11 +26,15 @@ namespace {
 //    w, which it updates with the P Z MFMAs.
 // Producer w and consumer w sit on one SIMD: each runs its MFMAs while the
 // other runs vector-ALU and LDS work.  Per iteration i, two barriers:
-//   X (before A): producer: scores of tile i+1, Z of tile i+1 to LDS;
-//                 consumer: summed scores of tile i, softmax, P of tile i.
-//   Y (A to B):   producer: publish the partial scores of tile i+1,
-//                 dequantise tile i+2, request tile i+3;
-//                 consumer: rescale and O += P Z for tile i.
+//   X (before A): producer: scores of tile i+1, published as soon as the
+//                 MFMAs are done;
+//                 consumer: softmax and P of tile i.
+//   Y (A to B):   producer: Z of tile i+1 to LDS, dequantise tile i+2,
+//                 request tile i+3;
+//                 consumer: rescale and O += P Z for tile i, and the sum of
+//                 the four partial scores of tile i+1.
+// So the exchange of the partial scores overlaps the P Z MFMAs, and the
+// softmax of a tile starts from scores already in registers.
 // The running max moves only when a tile's max beats it by more than 8 (log2
 // units), as in splitk_mfma_kernel.  The output accumulators live in VGPRs
 // (this translation unit is built with the VGPR form of MFMA), so the
@@ -96,22 +100,35 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     // accumulator; lanes are 64 bytes apart, so quad j of lane l goes to quad
     // j ^ ((l >> 1) & 3): any 8 consecutive lanes then store to distinct banks
     const int p_sw = (l >> 1) & 3;
-    auto publish = [&]() {
+    auto publish_tile = [&](int mt) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<f32x4 *>(&sm.sp[w][mt][l][4 * (j ^ p_sw)]) =
-              f32x4{sacc[mt][4 * j], sacc[mt][4 * j + 1], sacc[mt][4 * j + 2], sacc[mt][4 * j + 3]};
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4 *>(&sm.sp[w][mt][l][4 * (j ^ p_sw)]) =
+            f32x4{sacc[mt][4 * j], sacc[mt][4 * j + 1], sacc[mt][4 * j + 2], sacc[mt][4 * j + 3]};
     };
-    auto scores = [&]() {
+    auto mfma_steps = [&](int mt, int kb0, int kb1) {
+#pragma unroll
+      for (int kb = kb0; kb < kb1; ++kb)
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bz[kb], aq[mt][kb], sacc[mt], 0, 0, 0);
+    };
+    // Scores of the tile in bz, published to LDS.  With two row tiles the
+    // first tile's chain runs first, and its stores issue while the second
+    // chain is still in the MFMA pipe.
+    auto scores_publish = [&]() {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bz[kb], aq[mt][kb], sacc[mt], 0, 0, 0);
+      if constexpr (MT == 2) {
+        mfma_steps(0, 0, KB);
+        mfma_steps(1, 0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_tile(0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_steps(1, 2, KB);
+        publish_tile(1);
+      } else {
+        mfma_steps(0, 0, KB);
+        publish_tile(0);
+      }
     };
     RawTile raw;
     {
@@ -121,23 +138,24 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
       const RawTile r1 = load_tile<G, RQ>(a, tile_slot(1), w, hf);
       raw = load_tile<G, RQ>(a, tile_slot(2), w, hf);
       dequant<G, RQ>(r0, bz);
-      scores();
       store_z(0, bz);
-      publish();
+      scores_publish();
       dequant<G, RQ>(r1, bz);
     }
     lds_barrier();  // P0: partial scores and Z of tile 0
+    lds_barrier();  // P1: the consumers have read the partial scores of tile 0
     for (int i = 0; i < n_tiles; ++i) {
-      // X: scores of tile i+1 (harmless recompute past the end), its Z to
-      // the buffer the consumers read at tile i-1 (done by barrier B of i-1)
-      scores();
-      store_z((i & 1) ^ 1, bz);
-      lds_barrier();  // A: P of tile i; the consumers have read the partial scores of tile i
-      // Y: publish tile i+1, dequantise tile i+2, request tile i+3
-      publish();
+      // X: Z of tile i+1 to the buffer the consumers read at tile i-1 (done
+      // by barrier B of i-1); its scores (harmless recompute past the end),
+      // published as soon as the MFMAs are done, while the consumers run the
+      // softmax of tile i
+      store_z((i + 1) & 1, bz);
+      scores_publish();
+      lds_barrier();  // A: partial scores and Z of tile i+1; P of tile i
+      // Y: dequantise tile i+2, request tile i+3
       dequant<G, RQ>(raw, bz);
       raw = load_tile<G, RQ>(a, tile_slot(i + 3), w, hf);
-      lds_barrier();  // B: partial scores of tile i+1; P and Z of tile i consumed
+      lds_barrier();  // B: the consumers have read the partial scores of tile i+1 and P and Z of tile i
     }
     lds_barrier();  // E: 1 / l of every row
     return;
@@ -174,53 +192,66 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
   // term); the second load's rows are 4 further on, so bit 2 flips too
   const int pv_col = (16 * (g16 & 1) + 4 * (s16 & 3)) ^ (8 * ((g16 >> 1) & 1));
   const int pv_col_hi = pv_col ^ 8;
-  lds_barrier();  // P0
-  for (int i = 0; i < n_tiles; ++i) {
-    const int buf = i & 1;
-    // X: the summed scores of tile i, online softmax, P
-    float s[8];
+  // the four partial scores of the owned (row, 8 tokens), summed
+  float s[8];
+  auto read_scores = [&]() {
+    f32x4 part[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww)
+        part[h][ww] = *reinterpret_cast<const f32x4 *>(&sm.sp[ww][s_mt][s_lane + 32 * h][4 * s_q]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f32x4 acc4 = *reinterpret_cast<const f32x4 *>(&sm.sp[0][s_mt][s_lane + 32 * h][4 * s_q]);
+      const f32x4 acc4 = (part[h][0] + part[h][1]) + (part[h][2] + part[h][3]);
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww)
-        acc4 += *reinterpret_cast<const f32x4 *>(&sm.sp[ww][s_mt][s_lane + 32 * h][4 * s_q]);
-      s[4 * h] = acc4[0];
-      s[4 * h + 1] = acc4[1];
-      s[4 * h + 2] = acc4[2];
-      s[4 * h + 3] = acc4[3];
+      for (int e = 0; e < 4; ++e) s[4 * h + e] = acc4[e];
     }
+  };
+  lds_barrier();  // P0
+  read_scores();
+  lds_barrier();  // P1
+  for (int i = 0; i < n_tiles; ++i) {
+    const int buf = i & 1;
+    // X: online softmax and P of tile i (its summed scores are in s)
     if (i >= full_tiles) {
       const int ncnt = s_lim - (it.t0 + i * TT + 8 * s_k8);  // visible tokens among my 8
 #pragma unroll
       for (int e = 0; e < 8; ++e) s[e] = (e < ncnt) ? s[e] : -INFINITY;
     }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
-    tmax = reduce4<true>(tmax);
-    const bool need = tmax > m_run + kRescaleThreshold;   // true on the first visible tile
-    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
-    // a row's O is still zero until its first visible tile: no rescale then
-    const bool scale_o = need && m_run != -INFINITY;
-    m_run = need ? tmax : m_run;
+    float lmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    // The running max of a row moves only when the tile's max beats it by
+    // more than the threshold (always on its first visible tile, m = -inf).
+    // Most tiles move no row of the wave: then the exponentials start from
+    // the running max at once, with no row reduction on the way.
+    float alpha = 1.0f;
+    bool scale_o = false;
+    if (__any(lmax > m_run + kRescaleThreshold ? 1 : 0)) {
+      const float tmax = reduce4<true>(lmax);
+      const bool need = tmax > m_run + kRescaleThreshold;
+      alpha = need ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
+      // a row's O is still zero until its first visible tile: no rescale then
+      scale_o = need && m_run != -INFINITY;
+      m_run = need ? tmax : m_run;
+    }
     const float m_sub = (m_run == -INFINITY) ? 0.0f : m_run;
-    float psum = 0.0f;
+    float pe[8];
     f16x8 pv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(s[e] - m_sub);  // masked: exp2(-inf) = 0
-      psum += p;
-      pv[e] = static_cast<f16>(p);
+      pe[e] = __builtin_amdgcn_exp2f(s[e] - m_sub);  // masked: exp2(-inf) = 0
+      pv[e] = static_cast<f16>(pe[e]);
     }
-    psum = reduce4<false>(psum);
-    l_run = l_run * alpha + psum;
+    // l_run is this lane's share of the row sum (its 8 tokens); the four
+    // lanes of a row are added once, after the last tile
+    l_run = l_run * alpha + (((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7])));
     *reinterpret_cast<f16x8 *>(sm.p + s_row * PRSTRIDE + 8 * s_k8) = pv;
     // every lane stores (a row's lanes store equal values to one address)
     sm.alpha[s_row] = alpha;
     sm.resc[w] = __any((scale_o && s_own) ? 1 : 0);
-    lds_barrier();  // A: P, alpha and the rescale flags of tile i
-    // Y: O = alpha O + P Z for tile i
+    lds_barrier();  // A: P, alpha and the rescale flags of tile i; the partial scores of tile i+1
+    // Y: O = alpha O + P Z for tile i; the summed scores of tile i+1
+    read_scores();
     if (sm.resc[0] | sm.resc[1] | sm.resc[2] | sm.resc[3]) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -252,6 +283,7 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     lds_barrier();  // B
   }
   // ---- the partial (O / l in fp16, m, l) of this work item ----
+  l_run = reduce4<false>(l_run);
   if (s_k8 == 0) sm.inv_l[s_row] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   if (s_k8 == 0 && s_own && s_m < M) {
     a.part_ml[(static_cast<int64_t>(item) * M + s_m) * 2 + 0] = m_run;
