@@ -280,6 +280,10 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
           o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[mt], zb, o[mt][nt], 0, 0, 0);
       }
     }
+    // all P Z MFMAs issue in this phase: the scheduler would sink part of
+    // them past barrier B, where they hold up the softmax of the next tile
+    // behind the producers' score MFMAs on the same SIMD
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // B
   }
   // ---- the partial (O / l in fp16, m, l) of this work item ----
