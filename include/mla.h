@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -409,23 +409,33 @@ mla_status mla_decode_sparse(const mla_dims *dims, const uint16_t *q_nope,
  * implemented:
  *  - the calibration data is one sequence of n_cal tokens under causal
  *    self-attention (query i sees keys 0..i) with the given softmax scale;
- *  - K rotation of head h: eigenvectors, by ascending eigenvalue, of
- *    (M + 1e-8 I)^(-1/2) Sigma_k (M + 1e-8 I)^(-1/2), where Sigma_k is the
- *    uncentred covariance of the head's keys and M the uncentred covariance
- *    of the queries that read it (its G query heads, all positions) scaled
- *    to mean eigenvalue 1: a key error e costs the score error q . e, whose
- *    mean square is e^T M e;
+ *  - K rotation of head h (gqa_dims.k_rotation):
+ *      GQA_K_QUERY_COVARIANCE (0, the default, the plain reading of "a
+ *      query-covariance rotation for K"): eigenvectors, by ascending
+ *      eigenvalue, of Sigma_q, the uncentred covariance of the queries that
+ *      read the head (its G query heads, all positions).  A key error e
+ *      costs the score error q . e, of mean square e^T Sigma_q e, which in
+ *      this basis weights each rotated channel's error by its eigenvalue, so
+ *      channels of equal weight share the INT2 groups;
+ *      GQA_K_QUERY_METRIC (1, a refinement that also follows where the keys
+ *      vary): eigenvectors, by ascending eigenvalue, of
+ *      (M + 1e-8 I)^(-1/2) Sigma_k (M + 1e-8 I)^(-1/2), with Sigma_k the
+ *      uncentred covariance of the head's keys and M = Sigma_q scaled to
+ *      mean eigenvalue 1;
  *  - V rotation of head h: eigenvectors, by ascending eigenvalue, of
  *    sum_t w_t v_t v_t^T / sum_t w_t, with w_t the attention mass key t
  *    receives (summed over the head's query heads and the positions i >= t);
  *  - signs as mla_calibrate_rotation.
  * Layout: query head g reads KV head g / G, G = num_q_heads / num_kv_heads.
  * ---------------------------------------------------------------------- */
+#define GQA_K_QUERY_COVARIANCE 0
+#define GQA_K_QUERY_METRIC 1
 typedef struct gqa_dims {
   int32_t head_dim;     /* d: a multiple of group_size and of 8, 16..256 */
   int32_t num_q_heads;  /* H_q, a multiple of num_kv_heads, <= 4096 */
   int32_t num_kv_heads; /* H_kv >= 1 */
   int32_t group_size;   /* INT2 group along d: 16 or 32 */
+  int32_t k_rotation;   /* GQA_K_QUERY_COVARIANCE or GQA_K_QUERY_METRIC (gqa_calibrate only) */
 } gqa_dims;
 
 /* K and V entries per KV head in the latent entry format (codes packed four

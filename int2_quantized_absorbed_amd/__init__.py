@@ -4,7 +4,7 @@ The compute lives in libmla.so (HIP kernels behind the C ABI in
 include/mla.h); this package is its thin Python binding.
 """
 from .binding import (  # noqa: F401
-    Cache, Dims, GqaCache, GqaDims, MlaError, lib, header_functions,
+    Cache, Dims, GqaCache, GqaDims, MlaError, lib, header_functions, GQA_K_QUERY_COVARIANCE, GQA_K_QUERY_METRIC,
     gqa_append_quant, gqa_calibrate, gqa_decode, gqa_decode_workspace_size, gqa_fit_clip, gqa_prepare_rotation,
     mla_abi_version, mla_append_quant, mla_calibrate_rotation, mla_calibrate_rotation_weighted,
     mla_decode_absorbed, mla_decode_absorbed_noalloc, mla_decode_noalloc_max_workspace, mla_decode_sparse,

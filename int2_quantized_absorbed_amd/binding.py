@@ -42,8 +42,12 @@ class mla_cache(ctypes.Structure):
                 ("capacity", ctypes.c_int64)]
 
 
+GQA_K_QUERY_COVARIANCE = 0   # K rotation: eigenvectors of the query covariance
+GQA_K_QUERY_METRIC = 1       # K rotation: key covariance whitened by the query covariance
+
+
 class gqa_dims(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("head_dim", "num_q_heads", "num_kv_heads", "group_size")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("head_dim", "num_q_heads", "num_kv_heads", "group_size", "k_rotation")]
 
 
 class gqa_cache(ctypes.Structure):
@@ -226,9 +230,10 @@ class GqaDims:
     num_q_heads: int
     num_kv_heads: int
     group_size: int
+    k_rotation: int = GQA_K_QUERY_COVARIANCE   # or GQA_K_QUERY_METRIC (gqa_calibrate only)
 
     def c(self) -> gqa_dims:
-        return gqa_dims(self.head_dim, self.num_q_heads, self.num_kv_heads, self.group_size)
+        return gqa_dims(self.head_dim, self.num_q_heads, self.num_kv_heads, self.group_size, self.k_rotation)
 
     @property
     def n_groups(self):

@@ -266,6 +266,10 @@ bool gqa_dims_valid(const gqa_dims *g, std::string *why) {
     *why = "num_q_heads must be a multiple of num_kv_heads >= 1 and at most 4096";
     return false;
   }
+  if (g->k_rotation != GQA_K_QUERY_COVARIANCE && g->k_rotation != GQA_K_QUERY_METRIC) {
+    *why = "k_rotation must be GQA_K_QUERY_COVARIANCE or GQA_K_QUERY_METRIC";
+    return false;
+  }
   return true;
 }
 
@@ -941,11 +945,15 @@ mla_status gqa_calibrate(const gqa_dims *dims, const uint16_t *q_cal, const uint
   std::vector<double> vals(d), vecs(dd), sw;
   for (int h = 0; h < Hkv; ++h) {
     std::vector<double> sq(hq.begin() + h * dd, hq.begin() + (h + 1) * dd);
-    std::vector<double> sk(hk.begin() + h * dd, hk.begin() + (h + 1) * dd);
-    if (!metric_whitened(d, sq, sk, sw))
-      return fail(MLA_ERR_NUMERIC, "gqa_calibrate: query covariance is zero or not finite, or its eigensolve failed");
+    if (dims->k_rotation == GQA_K_QUERY_METRIC) {
+      std::vector<double> sk(hk.begin() + h * dd, hk.begin() + (h + 1) * dd);
+      if (!metric_whitened(d, sq, sk, sw))
+        return fail(MLA_ERR_NUMERIC, "gqa_calibrate: query covariance is zero or not finite, or its eigensolve failed");
+    } else {
+      sw = sq;
+    }
     if (!eigh_ascending(d, sw.data(), vals.data(), vecs.data()))
-      return fail(MLA_ERR_NUMERIC, "gqa_calibrate: key statistics not finite or eigensolver did not converge");
+      return fail(MLA_ERR_NUMERIC, "gqa_calibrate: key or query statistics not finite or eigensolver did not converge");
     for (size_t i = 0; i < dd; ++i) rk[h * dd + i] = static_cast<float>(vecs[i]);
     if (eig_k != nullptr) std::memcpy(eig_k + static_cast<size_t>(h) * d, vals.data(), sizeof(double) * d);
     if (!eigh_ascending(d, hv.data() + h * dd, vals.data(), vecs.data()))

@@ -118,21 +118,29 @@ def rotation_from_covariance(sigma):
     return vec.astype(np.float32), lam
 
 
-def calibrate(q_cal, k_cal, v_cal, scale):
+K_QUERY_COVARIANCE = 0   # the K rotation's plain reading (the default)
+K_QUERY_METRIC = 1       # the refinement: key covariance in the query metric
+
+
+def calibrate(q_cal, k_cal, v_cal, scale, k_rotation=K_QUERY_COVARIANCE):
     """Both rotations of every KV head.
 
-    Reading of "a query-covariance rotation for K": a key error e costs the
-    score error q . e, of mean square e^T Sigma_q e, so the K rotation is
-    fitted in the metric the query covariance defines: the eigenvectors of
-    Sigma_q^(-1/2) Sigma_k Sigma_q^(-1/2) (Sigma_k the keys' own covariance),
-    ascending - the same construction as the up-projection-aware latent
-    rotation, with the queries in the role of the up-projection.  (The
-    eigenvectors of Sigma_q alone ignore where the keys vary and raised the
-    score error in the directional pin.)  "A score-weighted V-covariance
-    rotation": the eigenvectors of the value covariance weighted by the
-    attention mass each calibration token receives, ascending.
+    "A query-covariance rotation for K", plain reading (K_QUERY_COVARIANCE):
+    the eigenvectors of the query covariance Sigma_q of the KV head's query
+    heads, ascending.  A key error e costs the score error q . e, of mean
+    square e^T Sigma_q e; in this basis that is the eigenvalue-weighted sum of
+    the rotated channels' squared errors, so channels of equal weight share
+    the INT2 groups.  The refinement (K_QUERY_METRIC) also follows where the
+    keys vary: the eigenvectors of Sigma_q^(-1/2) Sigma_k Sigma_q^(-1/2)
+    (Sigma_k the keys' own covariance, Sigma_q scaled to mean eigenvalue 1),
+    ascending - the construction of the up-projection-aware latent rotation,
+    with the queries in the role of the up-projection.
+    "A score-weighted V-covariance rotation": the eigenvectors of the value
+    covariance weighted by the attention mass each calibration token
+    receives, ascending.
     Returns (R_k [H_kv, d, d], eig_k [H_kv, d], R_v, eig_v, w).
     """
+    assert k_rotation in (K_QUERY_COVARIANCE, K_QUERY_METRIC)
     n_kv = np.asarray(k_cal).shape[0]
     sq = query_covariance(q_cal, n_kv)
     sk = key_covariance(k_cal)
@@ -140,7 +148,8 @@ def calibrate(q_cal, k_cal, v_cal, scale):
     sv = value_covariance(v_cal, w)
     rk, ek, rv, ev = [], [], [], []
     for h in range(n_kv):
-        r, e = rotation_from_covariance(metric_weighted(sk[h], sq[h]))
+        sk_h = sq[h] if k_rotation == K_QUERY_COVARIANCE else metric_weighted(sk[h], sq[h])
+        r, e = rotation_from_covariance(sk_h)
         rk.append(r)
         ek.append(e)
         r, e = rotation_from_covariance(sv[h])

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
     assert "mla_calibrate_rotation" in names and "mla_fit_clip" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert M.mla_abi_version() == 2
+    assert M.mla_abi_version() == 3
 
 
 def test_status_strings():
@@ -221,13 +221,14 @@ def test_workspace_size_is_monotone():
 
 
 def _gdims(**kw):
-    a = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, group_size=32)
+    a = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, group_size=32, k_rotation=0)
     a.update(kw)
-    return Bd.gqa_dims(a["head_dim"], a["num_q_heads"], a["num_kv_heads"], a["group_size"])
+    return Bd.gqa_dims(a["head_dim"], a["num_q_heads"], a["num_kv_heads"], a["group_size"], a["k_rotation"])
 
 
 @pytest.mark.parametrize("bad", [dict(head_dim=100), dict(head_dim=512), dict(group_size=8),
-                                 dict(num_q_heads=30), dict(num_kv_heads=0), dict(num_q_heads=4, num_kv_heads=8)])
+                                 dict(num_q_heads=30), dict(num_kv_heads=0), dict(num_q_heads=4, num_kv_heads=8),
+                                 dict(k_rotation=2), dict(k_rotation=-1)])
 def test_gqa_dims_rejected(bad):
     lib = M.lib()
     d = _gdims(**bad)

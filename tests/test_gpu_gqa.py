@@ -49,14 +49,15 @@ def _calib_data(seed, hq, hkv, n, d):
 CAL_CASES = [(64, 8, 2, 256, 16), (128, 4, 4, 200, 32)]
 
 
+@pytest.mark.parametrize("k_rotation", [M.GQA_K_QUERY_COVARIANCE, M.GQA_K_QUERY_METRIC])
 @pytest.mark.parametrize("d,hq,hkv,n,G", CAL_CASES)
-def test_gqa_calibrate_matches_oracle(d, hq, hkv, n, G):
-    C.say(f"gqa calibrate d={d} hq={hq} hkv={hkv} n={n}")
-    dims = M.GqaDims(d, hq, hkv, G)
+def test_gqa_calibrate_matches_oracle(d, hq, hkv, n, G, k_rotation):
+    C.say(f"gqa calibrate d={d} hq={hq} hkv={hkv} n={n} k_rotation={k_rotation}")
+    dims = M.GqaDims(d, hq, hkv, G, k_rotation)
     q, k, v = _calib_data(41, hq, hkv, n, d)
     scale = _scale(d)
     rk, rv, ek, ev = M.gqa_calibrate(dims, C.t_bf16(q), C.t_bf16(k), C.t_bf16(v), scale)
-    ork, oek, orv, oev, _ = Q.calibrate(q, k, v, scale)
+    ork, oek, orv, oev, _ = Q.calibrate(q, k, v, scale, k_rotation=k_rotation)
     assert np.allclose(ek, oek, rtol=1e-9, atol=1e-12)
     assert np.allclose(ev, oev, rtol=1e-9, atol=1e-12)
     assert np.abs(rk.cpu().numpy() - ork).max() <= 1e-5

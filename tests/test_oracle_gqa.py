@@ -8,15 +8,20 @@
   form at scale 0 (uniform causal attention: harmonic sums) and against the
   total mass each (query, head) pair contributes; value_covariance with equal
   weights against the plain uncentred covariance.
-* Rotations: orthogonal, ascending, sign rule; for axis-aligned queries and
-  keys the K rotation is the signed permutation that sorts the axes by
-  ascending key variance over query variance (the closed form of the
-  metric-weighted covariance when both are diagonal); with isotropic
-  queries it is the keys' own covariance basis.
-* Directional (the reason the page gives for a query-aware K rotation, not a
-  strict pin): with anisotropic queries, INT2 keys quantised in the
-  query-covariance basis give a smaller score error than keys quantised in
-  their own covariance basis.
+* K rotation, plain reading (the default, eigenvectors of the query
+  covariance): for queries built with an exactly known covariance Q L Q^T it
+  is Q with its columns ordered by ascending L (signs by the rule) and its
+  eigenvalues are sorted L; it does not depend on the keys; the mean square
+  score error of any key error e over the calibration queries equals the
+  eigenvalue-weighted sum of e's rotated channels squared.
+* K rotation, query-metric refinement: for axis-aligned queries and keys the
+  signed permutation that sorts the axes by ascending key variance over
+  query variance (the closed form of the metric-weighted covariance when
+  both are diagonal); with isotropic queries the keys' own covariance basis.
+* Both: orthogonal, ascending, sign rule.
+* Directional (not a strict pin): with anisotropic queries, INT2 keys
+  quantised in the query-metric basis give a smaller score error than keys
+  quantised in their own covariance basis.
 """
 import numpy as np
 import pytest
@@ -113,7 +118,7 @@ def test_k_rotation_for_axis_aligned_queries():
     kax = np.array([1.0, 2.0, 0.3, 0.2, 3.0, 1.5])      # ratios to the queries all distinct
     q, k, v = _qkv(6, n_q=2, n_kv=1, n=4000, d=6, q_axes=qax)
     k = k * kax
-    rk, ek, rv, ev, _ = Q.calibrate(q, k, v, 0.3)
+    rk, ek, rv, ev, _ = Q.calibrate(q, k, v, 0.3, k_rotation=Q.K_QUERY_METRIC)
     order = np.argsort(kax ** 2 / qax ** 2)                  # ascending key / query variance
     perm = np.abs(rk[0].astype(np.float64))
     assert np.allclose(perm, np.eye(6)[:, order], atol=0.05)
@@ -127,7 +132,7 @@ def test_isotropic_queries_give_key_covariance_basis():
     _, k, v = _qkv(8, n_q=2, n_kv=1, n=48, d=8)
     q = np.stack([np.tile(np.eye(8), (6, 1)) * 2.0 for _ in range(2)])    # Sigma_q = I / 2 exactly
     assert np.allclose(Q.query_covariance(q, 1)[0], 0.5 * np.eye(8))
-    rk, ek, _, _, _ = Q.calibrate(q, k, v, 0.3)
+    rk, ek, _, _, _ = Q.calibrate(q, k, v, 0.3, k_rotation=Q.K_QUERY_METRIC)
     r_self, e_self = Q.rotation_from_covariance(Q.key_covariance(k)[0])
     assert np.allclose(rk[0], r_self, atol=1e-5)
     assert np.allclose(ek[0], e_self / (1 + Q.METRIC_RIDGE), rtol=1e-9)   # M scaled to I
@@ -141,7 +146,7 @@ def test_query_aware_k_rotation_reduces_score_error():
     k = (rng.standard_normal((1, n, d)) * np.exp(np.linspace(0, -3, d))).astype(np.float32)
     k = O.bf16_round(k)[None][0]
     v = rng.standard_normal((1, n, d))
-    rk, _, _, _, _ = Q.calibrate(q, k, v, 0.1)
+    rk, _, _, _, _ = Q.calibrate(q, k, v, 0.1, k_rotation=Q.K_QUERY_METRIC)
     r_self, _, _ = O.calibrate_rotation(k[0])                # K's own covariance basis
 
     def score_err(r):
@@ -152,3 +157,45 @@ def test_query_aware_k_rotation_reduces_score_error():
         return np.mean(((q[0] @ (k[0].astype(np.float64) - k_hat).T)) ** 2)
 
     assert score_err(rk[0]) < score_err(r_self)
+
+
+def _queries_with_covariance(basis, lam, n_q):
+    """Queries [n_q, d, d] whose query covariance is exactly basis diag(lam)
+    basis^T: every query head holds the rows sqrt(d lam_j) basis[:, j]."""
+    d = basis.shape[0]
+    rows = (np.sqrt(d * lam)[:, None] * basis.T)            # row j = sqrt(d lam_j) q_j
+    return np.stack([rows] * n_q)
+
+
+def test_plain_k_rotation_is_the_query_covariance_basis():
+    rng = np.random.default_rng(11)
+    d = 12
+    basis, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    lam = np.exp(rng.uniform(-3, 2, d))
+    q = _queries_with_covariance(basis, lam, 2)
+    assert np.allclose(Q.query_covariance(q, 1)[0], basis @ np.diag(lam) @ basis.T, atol=1e-12)
+    _, k, v = _qkv(12, n_q=2, n_kv=1, n=d, d=d)
+    rk, ek, _, _, _ = Q.calibrate(q, k, v, 0.2)
+    order = np.argsort(lam)
+    assert np.allclose(ek[0], lam[order], rtol=1e-10)
+    expect = O.canonical_signs(basis[:, order])
+    assert np.abs(rk[0].astype(np.float64) - expect).max() <= 1e-6
+    # the keys do not enter the plain reading
+    rk2, ek2, _, _, _ = Q.calibrate(q, 3.0 * k[:, ::-1], v, 0.2)
+    assert np.array_equal(rk2, rk) and np.array_equal(ek2, ek)
+
+
+def test_plain_k_rotation_weights_score_error_by_eigenvalue():
+    q, k, v = _qkv(13, n_q=4, n_kv=2, n=64, d=8, q_axes=np.array([3.0, 0.2, 1.0, 0.5, 2.0, 0.1, 1.5, 0.7]))
+    rk, ek, _, _, _ = Q.calibrate(q, k, v, 0.2)
+    rng = np.random.default_rng(14)
+    for h in range(2):
+        r = rk[h].astype(np.float64)
+        assert np.abs(r.T @ r - np.eye(8)).max() <= 1e-6
+        assert np.all(np.diff(ek[h]) >= 0)
+        assert np.allclose(O.canonical_signs(r), r, atol=1e-7)
+        e = rng.standard_normal(8)
+        qs = q[2 * h:2 * h + 2].reshape(-1, 8)               # the head's two query heads
+        direct = np.mean((qs @ e) ** 2)
+        weighted = np.sum(ek[h] * (r.T @ e) ** 2)
+        assert np.isclose(direct, weighted, rtol=1e-6)
