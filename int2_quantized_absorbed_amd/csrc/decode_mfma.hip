@@ -16,7 +16,7 @@ namespace {
 
 // q~ = W~_UK[h]^T q_nope on MFMA (32x32x16 f16, fp32 acc), and q_rope; both
 // times scale*log2(e), written in fp16 straight into the per-lane operand
-// order of splitk_mfma_kernel: [b][row block][wave][mt][kb][lane][8], zero
+// order of the split-K kernel's producers: [b][row block][wave][mt][kb][lane][8], zero
 // for padding rows.  Block = (head, latent quarter = split-K wave slot,
 // 32 query rows (b, t)); wave w computes 32 channels.  The results are staged
 // in LDS so every operand unit (8 halves) is written with one 16-byte store.

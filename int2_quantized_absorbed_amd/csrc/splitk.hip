@@ -36,7 +36,7 @@ namespace {
 // So the exchange of the partial scores overlaps the P Z MFMAs, and the
 // softmax of a tile starts from scores already in registers.
 // The running max moves only when a tile's max beats it by more than 8 (log2
-// units), as in splitk_mfma_kernel.  The output accumulators live in VGPRs
+// units).  The output accumulators live in VGPRs
 // (this translation unit is built with the VGPR form of MFMA), so the
 // rescale is ordinary code and the compiler inserts the MFMA read hazards.
 // MT: 32-row MFMA tiles per block (2: 64 query rows; 1: 32 rows, for at most
