@@ -327,6 +327,281 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Split-K for at most 16 query rows (one GPU's 16-head share of a layer, or
+// fewer heads): every wave of the workgroup is an independent worker over
+// its own 16-token chunks of the work item (chunks v, v + 8, ...), with the
+// whole 576-wide contraction in its own instructions, so the tile loop has
+// no workgroup barrier and no partial-score exchange:
+//   scores  S^T[16 tokens x 16 rows] = Z Q^T: 18 v_mfma_f32_16x16x32_f16
+//           (Z the dequantised tokens, one per lane row, as the A operand;
+//           the queries, shared by the eight waves, from LDS);
+//   softmax its own running max and sum per row (lazy rescale as above);
+//           the score lanes already hold P^T in the layout of the next
+//           product's B operand;
+//   PV      O^T[512 x 16] += Z^T P^T: 32 v_mfma_f32_16x16x16_f16, Z^T read
+//           with ds_read_b64_tr_b16 from a wave-private LDS copy of the tile.
+// At the end each wave leaves its (m, l) and its O / l (fp16) in LDS, and
+// one pass over the eight waves merges them into the usual normalised fp16
+// partial of the work item.  Dense decode only (sparse decode keeps the
+// kernel above).
+// LDS: the query operands (18 K-steps x 64 lanes x 16 B) and per wave a Z
+// tile of 16 tokens x 512 channels (rows padded by 32 B: the four rows of a
+// transposing read fall in separate banks), which the wave's partial reuses
+// (rows padded by 16 B: a row's 16 lanes of a merge read fall in separate
+// banks).
+constexpr int R16_ZS = R + 16;  // halves per Z tile row
+constexpr int R16_OS = R + 8;   // halves per partial row
+constexpr int R16_KS = 2 * KB;  // K-steps: per lane half 8 latent + 1 rope
+static_assert(R16_OS <= R16_ZS, "a wave's partial must fit its Z region");
+
+struct __align__(16) SmemR16 {
+  f16x8 q[R16_KS * 64];
+  f16 z[8][16 * R16_ZS];
+  float m[8][16], l[8][16];
+};
+
+// ds_read_b64_tr_b16 at an LDS byte address
+__device__ __forceinline__ f16x4 ds_read_tr16_lds(uint32_t addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<s16x4 __attribute__((address_space(3))) *>(static_cast<uintptr_t>(addr)));
+  return __builtin_bit_cast(f16x4, v);
+}
+
+template <int G, bool RQ>
+__global__ __launch_bounds__(512, 1) void splitk_rows16_kernel(DecodeArgs a, int n_logical) {
+  __shared__ SmemR16 sm;
+  const int per_xcd = (n_logical + 7) / 8;
+  const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (item >= n_logical || item >= a.meta[0]) return;
+  const WorkItem it = a.items[item];
+  const int tid = threadIdx.x, l = tid & 63, n = l & 15, g = l >> 4;
+  const int v = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar chunk loop
+  const int H = a.d.num_heads, M = H * a.Tq;
+  const int L = a.seq_len[it.b];
+  const int64_t base = a.seq_base[it.b];
+  const int n_chunks = (it.t1 - it.t0 + 15) / 16;
+
+  // ---- query operands of the block's rows into LDS: unit (step s = 9 hf +
+  // kb, lane n + 16 q) = the producer-order unit (quarter q, half hf, kb) of
+  // row n; rows past M are zero ----
+  {
+    const f16x8 *qb = reinterpret_cast<const f16x8 *>(a.qbuf);
+    for (int u = tid; u < R16_KS * 64; u += 512) {
+      const int s = u >> 6, ln = u & 63, rn = ln & 15, qq = ln >> 4, hf = s / KB, kb = s % KB;
+      f16x8 val = f16x8{};
+      if (rn < M) val = qb[((static_cast<int64_t>(it.b) * 4 + qq) * 2 * KB + kb) * 64 + rn + 32 * hf];
+      sm.q[u] = val;
+    }
+  }
+  // rows of this lane: visible tokens < s_lim (padding rows see none)
+  int s_vis = -1;
+  if (n < M) s_vis = a.causal ? (L - a.Tq + n / H + 1) : L;
+  const int s_lim = min(it.t1, s_vis);
+  // lane (token n of the chunk, quarter g): its cache slot (dense decode
+  // only: a slot indirection would put a dependent load, and with it a wait
+  // for every load in flight, in front of each chunk's requests)
+  auto chunk_slot = [&](int c) -> int64_t { return base + min(it.t0 + 16 * c + n, it.t1 - 1); };
+  f16 *zt = sm.z[v];
+  f32x4 o[32];
+#pragma unroll
+  for (int ct = 0; ct < 32; ++ct) o[ct] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  // transposing-read position of lane l: rows (tokens) 4g + (l & 15) / 4,
+  // columns 4 (l & 3) of each 16-column block
+  const uint32_t ztr =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(zt + (4 * g + ((l & 15) >> 2)) * R16_ZS + 4 * (l & 3)));
+  // two register sets for the chunk tiles, used in turn (two chunks per
+  // trip), so the next chunk's loads stay in flight while one is processed:
+  // copying a tile between registers would wait for its loads
+  RawTile ta0, ta1, tb0, tb1;
+  if (v < n_chunks) {
+    const int64_t s0 = chunk_slot(v);
+    ta0 = load_tile<G, RQ>(a, s0, g, 0);
+    ta1 = load_tile<G, RQ>(a, s0, g, 1);
+  }
+  lds_barrier();  // the query operands (the chunk loads in flight stay in flight)
+  // one chunk: request the wave's next chunk c + 8 into (rn0, rn1), then
+  // process chunk c from (rc0, rc1)
+  auto chunk = [&](int c, const RawTile &rc0, const RawTile &rc1, RawTile &rn0, RawTile &rn1) {
+    if (c + 8 < n_chunks) {
+      const int64_t sn = chunk_slot(c + 8);
+      rn0 = load_tile<G, RQ>(a, sn, g, 0);
+      rn1 = load_tile<G, RQ>(a, sn, g, 1);
+    }
+    // ---- scores: dequantise one code word (two K-steps) at a time ----
+    f32x4 sacc = f32x4{};
+    f16 *zrow = zt + n * R16_ZS + 128 * g;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const RawTile &t = hf ? rc1 : rc0;
+      const uint32_t cws[4] = {t.codes.x, t.codes.y, t.codes.z, t.codes.w};
+      const uint32_t szw[4] = {t.sz.x, t.sz.y, t.sz.z, t.sz.w};
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const uint32_t szq = szw[(G == 32) ? (qd >> 1) : qd];
+        const f16x2 sc = __builtin_bit_cast(f16x2, (szq & 0xffffu) * 0x10001u);
+        const f16x2 zr = __builtin_bit_cast(f16x2, (szq >> 16) * 0x10001u);
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+          const uint32_t u = (cws[qd] >> (2 * odd)) & 0x33333333u;
+          const f16x2 c0 = __builtin_elementwise_fma(code_pair<0>(u), sc, zr);
+          const f16x2 c1 = __builtin_elementwise_fma(code_pair<1>(u), sc, zr);
+          const f16x2 c2 = __builtin_elementwise_fma(code_pair<2>(u), sc, zr);
+          const f16x2 c3 = __builtin_elementwise_fma(code_pair<3>(u), sc, zr);
+          const f16x8 zv = f16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+          const int kb = 2 * qd + odd;
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(zv, sm.q[(KB * hf + kb) * 64 + l], sacc, 0, 0, 0);
+          *reinterpret_cast<f16x8 *>(zrow + 64 * hf + 8 * kb) = zv;
+        }
+      }
+      // rope dims 16 g + 8 hf ..
+      f16x8 rv;
+      if (RQ) {
+        const uint32_t cr = t.rope.x, szr = t.rope.y;
+        const f16x2 sc = __builtin_bit_cast(f16x2, (szr & 0xffffu) * 0x10001u);
+        const f16x2 zr = __builtin_bit_cast(f16x2, (szr >> 16) * 0x10001u);
+        const f16x2 k1024 = f16x2{static_cast<f16>(1024.0f), static_cast<f16>(1024.0f)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t bb = cr >> (8 * j);
+          const uint32_t pair = (bb & 0xfu) | (((bb >> 4) & 0xfu) << 16) | 0x64006400u;
+          const f16x2 h2 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, pair) - k1024, sc, zr);
+          rv[2 * j] = h2[0];
+          rv[2 * j + 1] = h2[1];
+        }
+      } else {
+        const uint32_t rws[4] = {t.rope.x, t.rope.y, t.rope.z, t.rope.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rv[2 * j] = static_cast<f16>(__uint_as_float(rws[j] << 16));
+          rv[2 * j + 1] = static_cast<f16>(__uint_as_float(rws[j] & 0xffff0000u));
+        }
+      }
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(rv, sm.q[(KB * hf + KB - 1) * 64 + l], sacc, 0, 0, 0);
+    }
+    // ---- online softmax of row n over tokens 4g .. 4g + 3 of the chunk ----
+    float s[4];
+    const int tok0 = it.t0 + 16 * c + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = (tok0 + i < s_lim) ? sacc[i] : -INFINITY;
+    const float lmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__any(lmax > m_run + kRescaleThreshold ? 1 : 0)) {
+      float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (tmax > m_run + kRescaleThreshold) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - tmax);  // 0 on the first visible chunk
+        if (m_run != -INFINITY) {
+#pragma unroll
+          for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
+        }
+        l_run *= alpha;
+        m_run = tmax;
+      }
+    }
+    const float m_sub = (m_run == -INFINITY) ? 0.0f : m_run;
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(s[i] - m_sub);  // masked: 0
+    l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    const f16x4 pb = f16x4{static_cast<f16>(pe[0]), static_cast<f16>(pe[1]), static_cast<f16>(pe[2]),
+                           static_cast<f16>(pe[3])};
+    // the Z tile crosses lanes: its stores above the transposing reads below
+    __builtin_amdgcn_wave_barrier();
+    // ---- O^T += Z^T P^T ----
+    // (an opaque copy of the LDS address: hoisted out of the loop, the 32
+    // read addresses would each hold a register; per chunk they fold into
+    // the instructions' offsets)
+    uint32_t zb = ztr;
+    asm volatile("" : "+v"(zb));
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct) {
+      const f16x4 za = ds_read_tr16_lds(zb + 32 * ct);
+      o[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(za, pb, o[ct], 0, 0, 0);
+    }
+    // the next chunk's Z stores after these reads
+    __builtin_amdgcn_wave_barrier();
+  };
+  for (int c = v; c < n_chunks; c += 16) {
+    chunk(c, ta0, ta1, tb0, tb1);
+    if (c + 8 < n_chunks) chunk(c + 8, tb0, tb1, ta0, ta1);
+  }
+  // ---- merge the eight waves ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  // the wave's O / l in fp16 into its own Z region, free now (one wave's LDS
+  // operations complete in order, so its last transposing reads come first):
+  // column 16 ct + 4 g + i of row n
+  {
+    const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    f16 *ob = zt + n * R16_OS + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct)
+      *reinterpret_cast<f16x4 *>(ob + 16 * ct) =
+          f16x4{static_cast<f16>(o[ct][0] * inv_l), static_cast<f16>(o[ct][1] * inv_l),
+                static_cast<f16>(o[ct][2] * inv_l), static_cast<f16>(o[ct][3] * inv_l)};
+  }
+  if (g == 0) {
+    sm.m[v][n] = m_run;
+    sm.l[v][n] = l_run;
+  }
+  // an LDS-only barrier: __syncthreads would also wait for the partial's
+  // global stores of the other waves
+  lds_barrier();
+  // thread (row rn, 16-column block ct): weights exp2(m_w - mx) l_w / den of
+  // the eight waves, then their weighted sum
+  const int rn = tid & 15, ct = tid >> 4;
+  float mw[8], ew[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    mw[w] = sm.m[w][rn];
+    mx = fmaxf(mx, mw[w]);
+  }
+  float den = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    ew[w] = (mw[w] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - mx) * sm.l[w][rn];
+    den += ew[w];
+  }
+  const float rden = den > 0.0f ? 1.0f / den : 0.0f;
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const float wt = ew[w] * rden;
+    const f16 *src = sm.z[w] + rn * R16_OS + 16 * ct;
+    const f16x8 a0 = *reinterpret_cast<const f16x8 *>(src);
+    const f16x8 a1 = *reinterpret_cast<const f16x8 *>(src + 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[e] = fmaf(static_cast<float>(a0[e]), wt, acc[e]);
+      acc[8 + e] = fmaf(static_cast<float>(a1[e]), wt, acc[8 + e]);
+    }
+  }
+  if (ct == 0 && rn < M) {
+    a.part_ml[(static_cast<int64_t>(item) * M + rn) * 2 + 0] = mx;
+    a.part_ml[(static_cast<int64_t>(item) * M + rn) * 2 + 1] = den;
+  }
+  // column block ct = (quarter q, half hf, K-block pair j) = 8 q + 4 hf + j
+  // covers channels 128 q + 64 hf + 16 j .. + 16; its column 8 (kb & 1) + e
+  // is channel slot_channel(hf, kb, e)
+  if (rn < M) {
+    const int q = ct >> 3, hf = (ct >> 2) & 1, j = ct & 3;
+    f16 outv[16];
+#pragma unroll
+    for (int col = 0; col < 16; ++col) {
+      const int kb = 2 * j + (col >> 3), e = col & 7;
+      outv[slot_channel(hf, kb, e) - 64 * hf - 16 * j] = static_cast<f16>(acc[col]);
+    }
+    f16 *dst = reinterpret_cast<f16 *>(a.part_o) + (static_cast<int64_t>(item) * M + rn) * R + 128 * q + 64 * hf + 16 * j;
+    *reinterpret_cast<f16x8 *>(dst) = f16x8{outv[0], outv[1], outv[2], outv[3], outv[4], outv[5], outv[6], outv[7]};
+    *reinterpret_cast<f16x8 *>(dst + 8) =
+        f16x8{outv[8], outv[9], outv[10], outv[11], outv[12], outv[13], outv[14], outv[15]};
+  }
+}
 }  // namespace
 
 hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
@@ -342,6 +617,21 @@ hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
   const int n_logical = n_items * rb_count;
   const int grid = ((n_logical + 7) / 8) * 8;
   const bool rq = a.d.rope_bits == 4;
+#ifndef MLA_SPLITK_ROWS16
+#define MLA_SPLITK_ROWS16 1
+#endif
+  if (MLA_SPLITK_ROWS16 && M <= 16 && a.sel == nullptr) {
+    const int n_items16 = std::min(a.max_items, std::max(a.target_items, a.B));
+    const int grid16 = ((n_items16 + 7) / 8) * 8;
+#define MLA_ROWS16_LAUNCH(G_, RQ_) splitk_rows16_kernel<G_, RQ_><<<grid16, 512, 0, s>>>(a, n_items16)
+    if (a.d.group_size == 32) {
+      if (rq) MLA_ROWS16_LAUNCH(32, true); else MLA_ROWS16_LAUNCH(32, false);
+    } else {
+      if (rq) MLA_ROWS16_LAUNCH(16, true); else MLA_ROWS16_LAUNCH(16, false);
+    }
+#undef MLA_ROWS16_LAUNCH
+    return hipGetLastError();
+  }
 #define MLA_SPLITK_LAUNCH(G_, RQ_, MT_) \
   splitk_ws_kernel<G_, RQ_, MT_><<<grid, 512, 0, s>>>(a, rb_count, rb_count64, n_logical)
   if (a.d.group_size == 32) {

@@ -172,6 +172,8 @@ RISE_CASES = [
     ("ramp-h128-long-items", dict(), [20000], 1, True, "ramp", 0),
     ("ramp-h16-mfma", dict(num_heads=16), [1500, 64, 4000], 1, True, "ramp", 2),
     ("ramp-tq8-causal-mfma", dict(num_heads=16), [900, 129], 8, True, "ramp", 2),
+    ("steps-h16-rows16", dict(num_heads=16), [3000, 515], 1, True, "steps", 0),
+    ("steps-h4-tq4-rows16", dict(num_heads=4), [2500, 300], 4, True, "steps", 0),
     ("ramp-h128-valu", dict(), [2049, 700, 97], 1, True, "ramp", 1),
     ("steps-h128-mfma", dict(), [3000, 515], 1, True, "steps", 2),
     ("steps-h128-long-items", dict(), [24000], 1, True, "steps", 0),

@@ -224,6 +224,11 @@ DECODE_CASES = [
     ("w1-g16", 1, dict(group_size=16, num_heads=32), [129], 1, True, 0),
     ("w1-mfma-forced", 1, dict(), [1, 33, 64, 95], 1, True, 2),
     ("w1-h8-mfma-padrows", 1, dict(num_heads=8), [500], 1, True, 2),
+    # at most 16 query rows: the 16-row kernel (waves over 16-token chunks)
+    ("w1-h16-many-chunks", 1, dict(num_heads=16), [5000, 17, 1, 160], 1, False, 0),
+    ("w1-h4-tq4-causal-mfma", 1, dict(num_heads=4), [700, 33, 4], 4, True, 2),
+    ("w1-h2-tq3-mfma", 1, dict(num_heads=2), [300, 45], 3, True, 2),
+    ("w1-h16-g16", 1, dict(group_size=16, num_heads=16), [777, 2049], 1, True, 0),
     ("w2-ragged-long", 2, dict(), [2049, 1500, 31, 4000], 1, True, 0),
 ]
 

@@ -95,6 +95,7 @@ DECODE_CASES = [
     ("tq8-causal", dict(num_heads=16), [40, 9, 600], 8, True, 0),
     ("h16-mfma", dict(num_heads=16), [300, 1100], 1, True, 2),
     ("g16", dict(group_size=16, num_heads=32), [513], 1, True, 0),
+    ("h8-g16-rows16", dict(group_size=16, num_heads=8), [700, 17], 1, True, 0),
 ]
 
 

@@ -79,7 +79,7 @@ def test_index_topk_matches_oracle(name, lens, top_k, dup, pool):
         assert np.array_equal(sel[b, :len(ref)], ref), (name, b)
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_decode_sparse_matches_oracle(variant):
     w = S.WORKLOADS[4].with_(num_heads=64 if variant == 0 else 16)
     lens = [3000, 700, 0, 2500]
