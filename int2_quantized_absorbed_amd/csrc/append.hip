@@ -436,16 +436,12 @@ hipError_t launch_mfma_r(const AppendParams &p, hipStream_t s) {
 }  // namespace
 
 bool append_fusable(const mla_dims &d, mla_dtype dt, int64_t n) {
-  return dt == MLA_DTYPE_BF16 && d.kv_lora_rank == 512 && d.rope_bits == 0 && n > 0 && n <= kSkinnyMaxTokens;
+  return dt == MLA_DTYPE_BF16 && d.kv_lora_rank == 512 && (d.rope_bits == 0 || d.rope_bits == 4) && n > 0 &&
+         n <= kSkinnyMaxTokens;
 }
 
-// Rope-key variant: quantise each token's rope key in groups of 16 dims to
-// 4-bit codes with fp16 scale and zero [OSCAR issue #10, maintainer's later
-// reply: two designs for the rope and non-rope parts; the reading is the
-// latent quantiser without clipping, 15 levels, rope key unrotated].  One
-// thread per (token, group): 16 bf16 values in (two 16-byte loads), 8 code
-// bytes and one (scale, zero) word out.  Every step in IEEE fp32 with no
-// contraction, the division correctly rounded, as the latent quantiser.
+// Rope-key variant: one thread per (token, group of 16 rope dims), see
+// rope_quant_group.
 __global__ __launch_bounds__(256) void rope_quant_kernel(const uint16_t *__restrict__ k_rope,
                                                          const int64_t *__restrict__ slots, int64_t n, int d_r,
                                                          uint8_t *__restrict__ entries, int64_t capacity) {
@@ -456,43 +452,7 @@ __global__ __launch_bounds__(256) void rope_quant_kernel(const uint16_t *__restr
   if (tok >= n) return;
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= capacity) return;
-  const uint4 *src = reinterpret_cast<const uint4 *>(k_rope + tok * d_r + 16 * g);
-  const uint4 v0 = src[0], v1 = src[1];
-  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  float x[16];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    x[2 * j] = __uint_as_float(w[j] << 16);
-    x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-  }
-  float mx = x[0], mn = x[0];
-#pragma unroll
-  for (int j = 1; j < 16; ++j) {
-    mx = fmaxf(mx, x[j]);
-    mn = fminf(mn, x[j]);
-  }
-  const float mid = __fmul_rn(0.5f, __fadd_rn(mx, mn));
-  const float half = __fmul_rn(0.5f, __fsub_rn(mx, mn));
-  const float lo = __fsub_rn(mid, half);
-  const float hi = __fadd_rn(mid, half);
-  const f16 scale = f32_to_f16(__fdiv_rn(__fsub_rn(hi, lo), 15.0f));
-  const f16 zero = f32_to_f16(lo);
-  const float sf = static_cast<float>(scale), zf = static_cast<float>(zero);
-  uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    uint32_t c = 0u;
-    if (sf != 0.0f) {  // fmaxf/fminf drop a NaN quotient: code 0
-      const float u = __fdiv_rn(__fsub_rn(x[j], zf), sf);
-      c = static_cast<uint32_t>(fminf(fmaxf(rintf(u), 0.0f), 15.0f));
-    }
-    packed[j >> 3] |= c << (4 * (j & 7));
-  }
-  uint8_t *e = entries + slot * (d_r / 2 + d_r / 4);  // entries are 4-byte aligned (12 bytes at d_r = 16)
-  reinterpret_cast<uint32_t *>(e + 8 * g)[0] = packed[0];
-  reinterpret_cast<uint32_t *>(e + 8 * g)[1] = packed[1];
-  *reinterpret_cast<uint32_t *>(e + d_r / 2 + 4 * g) =
-      static_cast<uint32_t>(f16_bits(scale)) | (static_cast<uint32_t>(f16_bits(zero)) << 16);
+  rope_quant_group(k_rope, tok, g, d_r, slot, entries);
 }
 
 bool append_uses_mfma(const mla_dims &d, mla_dtype dt) {
@@ -535,6 +495,7 @@ hipError_t launch_append(const mla_dims &d, const void *latent, mla_dtype dt, co
   p.G = d.group_size;
   p.d_r = d.qk_rope_head_dim;
   p.d_idx = d.index_head_dim;
+  p.rope_bits = 0;
   if (append_uses_mfma(d, dt)) {
     switch (p.r) {
       case 128: return launch_mfma_r<128>(p, s);

@@ -63,7 +63,57 @@ struct AppendParams {
   float *z_out;
   int64_t lat_stride;  // elements from one token's latent row to the next
   int r, G, d_r, d_idx;
+  int rope_bits;       // 0: bf16 rope keys copied; 4: quantised (rope_quant_group)
 };
+
+// Rope-key variant: token tok's rope dims 16 g .. 16 g + 15 to 4-bit codes
+// with an fp16 (scale, zero) [OSCAR issue #10, maintainer's later reply: two
+// designs for the rope and non-rope parts; the reading is the latent
+// quantiser without clipping, 15 levels, rope key unrotated]: 16 bf16 values
+// in (two 16-byte loads), 8 code bytes and one (scale, zero) word out into
+// the slot's entry (d_r / 2 code bytes, then d_r / 16 words; entries are
+// 4-byte aligned).  Every step in IEEE fp32 with no contraction, the division
+// correctly rounded, as the latent quantiser.
+__device__ __forceinline__ void rope_quant_group(const uint16_t *__restrict__ k_rope, int64_t tok, int g, int d_r,
+                                                 int64_t slot, uint8_t *__restrict__ entries) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(k_rope + tok * d_r + 16 * g);
+  const uint4 v0 = src[0], v1 = src[1];
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[2 * j] = __uint_as_float(w[j] << 16);
+    x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+  float mx = x[0], mn = x[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) {
+    mx = fmaxf(mx, x[j]);
+    mn = fminf(mn, x[j]);
+  }
+  const float mid = __fmul_rn(0.5f, __fadd_rn(mx, mn));
+  const float half = __fmul_rn(0.5f, __fsub_rn(mx, mn));
+  const float lo = __fsub_rn(mid, half);
+  const float hi = __fadd_rn(mid, half);
+  const f16 scale = f32_to_f16(__fdiv_rn(__fsub_rn(hi, lo), 15.0f));
+  const f16 zero = f32_to_f16(lo);
+  const float sf = static_cast<float>(scale), zf = static_cast<float>(zero);
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t c = 0u;
+    if (sf != 0.0f) {  // fmaxf/fminf drop a NaN quotient: code 0
+      const float u = __fdiv_rn(__fsub_rn(x[j], zf), sf);
+      c = static_cast<uint32_t>(fminf(fmaxf(rintf(u), 0.0f), 15.0f));
+    }
+    packed[j >> 3] |= c << (4 * (j & 7));
+  }
+  uint8_t *e = entries + slot * (d_r / 2 + d_r / 4);
+  reinterpret_cast<uint32_t *>(e + 8 * g)[0] = packed[0];
+  reinterpret_cast<uint32_t *>(e + 8 * g)[1] = packed[1];
+  *reinterpret_cast<uint32_t *>(e + d_r / 2 + 4 * g) =
+      static_cast<uint32_t>(f16_bits(scale)) | (static_cast<uint32_t>(f16_bits(zero)) << 16);
+}
 
 // Epilogue of one 32-channel x 32-token rotation tile in MFMA C layout (lane
 // l holds channels ch0 + 8q + 4hf + s, v = 4q + s, of token tok): the fp32
@@ -230,6 +280,87 @@ __device__ __forceinline__ void skinny_tile(const AppendParams &p, int ct, int t
     const int cnt = static_cast<int>(min<int64_t>(32, p.n - t0));
     copy_side_keys(p.cache.k_rope, p.k_rope, p.d_r, p.slots, t0, cnt, p.cache.capacity, l);
     if (p.d_idx > 0) copy_side_keys(p.cache.idx_key, p.idx_key, p.d_idx, p.slots, t0, cnt, p.cache.capacity, l);
+  }
+}
+
+// The same tile for a workgroup of four waves that share one 32-token tile
+// (channel tiles ct of its waves): the tile's 32 latent rows are staged once
+// in LDS (`lat`, 32 rows x R / 8 pieces of 16 bytes, piece p of row t at
+// p ^ (t & 15): the 16 lanes of a read hit separate banks) while every wave
+// holds its R_apply^T rows for all K-steps in registers, so all operands
+// arrive in one memory round trip.  The MFMA sequence is the one above, so
+// the codes are the same bytes.  Side keys are not copied here
+// (side_key_block).  Called by all threads of the workgroup.
+template <int R, int G, int NACC>
+__device__ __forceinline__ void staged_skinny_tile(const AppendParams &p, int ct, int ty, int tid,
+                                                   u32x4 *__restrict__ lat) {
+  constexpr int KS = R / 16, PR = R / 8, PER = 32 * PR / 256;
+  constexpr int NGT = 32 / G;
+  static_assert(PER * 256 == 32 * PR, "whole rows per workgroup");
+  const int l = tid & 63, hf = l >> 5, l32 = l & 31;
+  const int64_t t0 = static_cast<int64_t>(ty) * 32, tok = t0 + l32;
+  const bool valid = tok < p.n;
+  // the tile's latent rows, piece tid + 256 j each (row 0 stands in for
+  // tokens past the end: their columns are never stored)
+  u32x4 lv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid + 256 * j, t = e / PR, pc = e % PR;
+    const int64_t row = t0 + t < p.n ? t0 + t : 0;
+    lv[j] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.latent) + row * p.lat_stride + 8 * pc);
+  }
+  const bf16x8 *arow = reinterpret_cast<const bf16x8 *>(p.Rt + static_cast<int64_t>(32 * ct + l32) * R);
+  bf16x8 aq[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aq[ks] = arow[2 * ks + hf];
+  int64_t slot = -1;
+  if (valid) slot = p.slots[tok];
+  float alpha[NGT];
+#pragma unroll
+  for (int g = 0; g < NGT; ++g) alpha[g] = p.alpha[(32 * ct) / G + g];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid + 256 * j, t = e / PR, pc = e % PR;
+    lat[t * PR + (pc ^ (t & 15))] = lv[j];
+  }
+  __syncthreads();
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) acc[a] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 bq = __builtin_bit_cast(bf16x8, lat[l32 * PR + ((2 * ks + hf) ^ (l32 & 15))]);
+    acc[ks % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], bq, acc[ks % NACC], 0, 0, 0);
+  }
+  f32x16 z = acc[0];
+#pragma unroll
+  for (int a = 1; a < NACC; ++a) z += acc[a];
+  const bool write = valid && slot >= 0 && slot < p.cache.capacity;
+  tile_epilogue<R, G>(p, z, tok, write, slot, 32 * ct, alpha, hf);
+}
+
+// Side keys of the 32-token tile ty by a workgroup of four waves: wave 0 the
+// bf16 rope keys (copied) or waves 0-1 the 4-bit rope keys (one thread per
+// token and group of 16 dims, rope_quant_group); waves 2 and 3 the indexer
+// keys of the tile's first and second 16 tokens.
+__device__ __forceinline__ void side_key_block(const AppendParams &p, int ty, int tid) {
+  const int64_t t0 = static_cast<int64_t>(ty) * 32;
+  const int cnt = static_cast<int>(min<int64_t>(32, p.n - t0));
+  const int wv = tid >> 6, lane = tid & 63;
+  if (p.rope_bits == 4) {
+    const int groups = p.d_r / 16;
+    for (int u = tid; tid < 128 && u < cnt * groups; u += 128) {
+      const int64_t tok = t0 + u / groups;
+      const int64_t slot = p.slots[tok];
+      if (slot >= 0 && slot < p.cache.capacity)
+        rope_quant_group(p.k_rope, tok, u % groups, p.d_r, slot, reinterpret_cast<uint8_t *>(p.cache.k_rope));
+    }
+  } else if (wv == 0) {
+    copy_side_keys(p.cache.k_rope, p.k_rope, p.d_r, p.slots, t0, cnt, p.cache.capacity, lane);
+  }
+  if (wv >= 2 && p.d_idx > 0) {
+    const int h0 = 16 * (wv - 2), hc = min(16, cnt - h0);
+    if (hc > 0) copy_side_keys(p.cache.idx_key, p.idx_key, p.d_idx, p.slots, t0 + h0, hc, p.cache.capacity, lane);
   }
 }
 

@@ -132,9 +132,15 @@ def test_decode_rope_int4(name, over, lens, tq, causal, variant):
     assert worst <= OUT_RTOL
 
 
-def test_decode_step_rope_int4_equals_separate_calls():
+@pytest.mark.parametrize("new", [1, 13])
+def test_decode_step_rope_int4_equals_separate_calls(new):
+    """The step's new tokens (1 or 13 per sequence: one or two 32-token
+    tiles) appended inside the query-absorb launch, rope keys quantised there
+    too, against mla_append_quant then mla_decode_absorbed.  The cache holds
+    every earlier token; the step's slots start as a fill pattern, so a
+    missing write shows."""
     w = S.WORKLOADS[1]
-    C.say("decode step with 4-bit rope")
+    C.say(f"decode step with 4-bit rope, {new} new tokens per sequence")
     layer = C.Layer(w)
     d4 = rope4(w)
     lens = [900, 1301, 64]
@@ -142,7 +148,9 @@ def test_decode_step_rope_int4_equals_separate_calls():
     rng = np.random.default_rng(23)
     lat = C.t_bf16(layer.model.sample(rng, cap))
     kr = C.t_bf16(S.rope_keys(rng, cap, w.qk_rope_head_dim))
-    last = torch.tensor([int(base[b]) + L - 1 for b, L in enumerate(lens)], dtype=torch.int64, device=C.DEV)
+    step = np.array([int(base[b]) + L - 1 - j for b, L in enumerate(lens) for j in range(new)], np.int64)
+    old = np.setdiff1d(np.arange(cap, dtype=np.int64), step)
+    step_d, old_d = torch.from_numpy(step).to(C.DEV), torch.from_numpy(old).to(C.DEV)
     qn, qr = S.queries(w, S.streams(w.wid, 5), batch=len(lens), tq=1)
     qn, qr = C.t_bf16(qn), C.t_bf16(qr)
     sb, sl = torch.from_numpy(base).to(C.DEV), torch.from_numpy(np.asarray(lens, np.int32)).to(C.DEV)
@@ -150,21 +158,26 @@ def test_decode_step_rope_int4_equals_separate_calls():
     caches, outs = [], []
     for fused in (True, False):
         cache = M.Cache(d4, cap, C.DEV)
-        M.mla_append_quant(d4, lat, kr, None, torch.arange(cap, dtype=torch.int64, device=C.DEV), layer.Rt_d,
+        cache.codes.fill_(0x5A)
+        cache.k_rope.fill_(0x3C)
+        M.mla_append_quant(d4, lat[old_d].contiguous(), kr[old_d].contiguous(), None, old_d, layer.Rt_d,
                            layer.alpha_d, cache)
         if fused:
-            out, lse = M.mla_decode_step(d4, lat[last].contiguous(), kr[last].contiguous(), None, last, layer.Rt_d,
-                                         layer.alpha_d, qn, qr, layer.w_uk_f, layer.w_uv_f, cache, sb, sl, 1, True,
-                                         scale)
+            out, lse = M.mla_decode_step(d4, lat[step_d].contiguous(), kr[step_d].contiguous(), None, step_d,
+                                         layer.Rt_d, layer.alpha_d, qn, qr, layer.w_uk_f, layer.w_uv_f, cache, sb,
+                                         sl, 1, True, scale)
         else:
-            M.mla_append_quant(d4, lat[last].contiguous(), kr[last].contiguous(), None, last, layer.Rt_d,
+            M.mla_append_quant(d4, lat[step_d].contiguous(), kr[step_d].contiguous(), None, step_d, layer.Rt_d,
                                layer.alpha_d, cache)
             out, lse = M.mla_decode_absorbed(d4, qn, qr, layer.w_uk_f, layer.w_uv_f, cache, sb, sl, 1, True, scale)
         caches.append(cache)
         outs.append((out, lse))
     torch.cuda.synchronize()
     assert torch.equal(caches[0].k_rope, caches[1].k_rope) and torch.equal(caches[0].codes, caches[1].codes)
+    assert torch.equal(caches[0].scale_zero.view(torch.int16), caches[1].scale_zero.view(torch.int16))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # the step's slots were written (the fill pattern is gone)
+    assert not np.any(np.all(caches[0].codes.cpu().numpy()[step] == 0x5A, axis=1))
 
 
 @pytest.mark.parametrize("heads", [128, 32])

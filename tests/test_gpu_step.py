@@ -23,6 +23,8 @@ STEP_CASES = [
     ("g32-fused", 1, dict(num_heads=16), [300, 1, 77, 1024], 1, True, 1),
     ("g16-fused", 1, dict(num_heads=16, group_size=16), [40, 513, 64], 2, True, 2),
     ("idx-fused", 4, dict(num_heads=16), [130, 65], 1, True, 1),
+    ("g32-fused-2tiles", 1, dict(num_heads=16), [300, 500], 1, True, 20),  # 40 tokens: a ragged second tile
+    ("idx-fused-2tiles", 4, dict(num_heads=16), [130, 65, 90], 1, True, 11),  # 33 tokens
     ("large-append", 1, dict(num_heads=16), [700, 600], 1, True, 550),   # 1100 tokens: separate append
     ("valu-decode", 0, dict(), [100, 37], 1, True, 1),                     # r = 64: vector-ALU decode
 ]
