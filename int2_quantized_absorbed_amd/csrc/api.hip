@@ -150,12 +150,12 @@ struct WsLayout {
   int max_items = 0;
 };
 
-// Work items that fill the GPU: one resident block per (item, row block).
-int target_items(int rows, bool mfma) {
+// Work items that fill the GPU: one resident workgroup (or wave) per item and
+// row block of the split-K kernel that runs (sparse: selected-token decode).
+int target_items(int rows, bool mfma, bool sparse) {
   const int ncu = device_cu_count();
-  const int rb = mfma ? (rows + mfma_row_block() - 1) / mfma_row_block() : (rows + 15) / 16;
-  const int slots = mfma ? ncu : 2 * ncu;  // resident blocks per launch
-  const int t = slots / rb;
+  if (mfma) return splitk_target_items(rows, sparse, ncu);
+  const int t = 2 * ncu / ((rows + 15) / 16);  // two 16-row blocks per compute unit
   return t < 1 ? 1 : t;
 }
 
@@ -172,7 +172,9 @@ WsLayout layout(const mla_dims &d, int B, int Tq, int min_items = 0) {
   const int r = d.kv_lora_rank, K = r + d.qk_rope_head_dim;
   const int M = d.num_heads * Tq;
   // the planner emits at most max(target, number of sequences) items
-  const int tgt = std::max(target_items(M, true), target_items(M, false));
+  int tgt = target_items(M, false, false);
+  if (mfma_decode_supported(d, M))
+    tgt = std::max(tgt, std::max(target_items(M, true, false), target_items(M, true, true)));
   w.max_items = std::max(std::max(tgt, B), min_items);
   size_t off = 0;
   w.items = off;
@@ -305,7 +307,7 @@ bool gqa_use_mfma(const gqa_dims &g, int Tq) {
 
 int gqa_target_items(const gqa_dims &g, int Tq) {
   const int rows = g.num_q_heads / g.num_kv_heads * Tq;
-  return gqa_use_mfma(g, Tq) ? kGqaWavesPerCu * device_cu_count() : target_items(rows, false);
+  return gqa_use_mfma(g, Tq) ? kGqaWavesPerCu * device_cu_count() : target_items(rows, false, false);
 }
 
 GqaWs gqa_layout(const gqa_dims &g, int B, int Tq) {
@@ -685,7 +687,7 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
   a.part_o = reinterpret_cast<uint16_t *>(ws + w.part_o);
   a.part_ml = reinterpret_cast<float *>(ws + w.part_ml);
   a.max_items = w.max_items;
-  a.target_items = target_items(M, use_mfma);
+  a.target_items = target_items(M, use_mfma, sel != nullptr);
   a.tile = use_mfma ? 32 : 16;
   a.min_chunk_tiles = min_chunk_tiles(a.tile);
   a.sel = sel;

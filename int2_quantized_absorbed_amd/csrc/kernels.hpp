@@ -141,6 +141,12 @@ struct AppendJob {
 bool append_fusable(const mla_dims &d, mla_dtype dt, int64_t n);
 hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s, const AppendJob *job = nullptr);
 hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s);
+// The split-K kernel of the MFMA path for `rows` query rows per sequence
+// (sparse: selected-token decode), and the work items that fill the GPU
+// with it (one resident workgroup per item and row block).
+enum class SplitK { kRows16, kWarpSpec };
+SplitK splitk_kernel_for(int rows, bool sparse);
+int splitk_target_items(int rows, bool sparse, int ncu);
 // grouped-query layers: head dim 128, at most 32 query rows per KV head,
 // one wave per work item (grid = max_items)
 bool gqa_mfma_supported(const mla_dims &d, int rows);

@@ -362,13 +362,6 @@ struct __align__(16) SmemR16 {
   float m[8][16], l[8][16];
 };
 
-// ds_read_b64_tr_b16 at an LDS byte address
-__device__ __forceinline__ f16x4 ds_read_tr16_lds(uint32_t addr) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<s16x4 __attribute__((address_space(3))) *>(static_cast<uintptr_t>(addr)));
-  return __builtin_bit_cast(f16x4, v);
-}
-
 template <int G, bool RQ>
 __global__ __launch_bounds__(512, 1) void splitk_rows16_kernel(DecodeArgs a, int n_logical) {
   __shared__ SmemR16 sm;
@@ -430,56 +423,21 @@ __global__ __launch_bounds__(512, 1) void splitk_rows16_kernel(DecodeArgs a, int
       rn0 = load_tile<G, RQ>(a, sn, g, 0);
       rn1 = load_tile<G, RQ>(a, sn, g, 1);
     }
-    // ---- scores: dequantise one code word (two K-steps) at a time ----
+    // ---- scores: one K-block (8 channels of the lane's quarter) at a time ----
     f32x4 sacc = f32x4{};
     f16 *zrow = zt + n * R16_ZS + 128 * g;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const RawTile &t = hf ? rc1 : rc0;
-      const uint32_t cws[4] = {t.codes.x, t.codes.y, t.codes.z, t.codes.w};
-      const uint32_t szw[4] = {t.sz.x, t.sz.y, t.sz.z, t.sz.w};
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const uint32_t szq = szw[(G == 32) ? (qd >> 1) : qd];
-        const f16x2 sc = __builtin_bit_cast(f16x2, (szq & 0xffffu) * 0x10001u);
-        const f16x2 zr = __builtin_bit_cast(f16x2, (szq >> 16) * 0x10001u);
-#pragma unroll
-        for (int odd = 0; odd < 2; ++odd) {
-          const uint32_t u = (cws[qd] >> (2 * odd)) & 0x33333333u;
-          const f16x2 c0 = __builtin_elementwise_fma(code_pair<0>(u), sc, zr);
-          const f16x2 c1 = __builtin_elementwise_fma(code_pair<1>(u), sc, zr);
-          const f16x2 c2 = __builtin_elementwise_fma(code_pair<2>(u), sc, zr);
-          const f16x2 c3 = __builtin_elementwise_fma(code_pair<3>(u), sc, zr);
-          const f16x8 zv = f16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-          const int kb = 2 * qd + odd;
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(zv, sm.q[(KB * hf + kb) * 64 + l], sacc, 0, 0, 0);
-          *reinterpret_cast<f16x8 *>(zrow + 64 * hf + 8 * kb) = zv;
-        }
+      for (int kb = 0; kb < 8; ++kb) {
+        const f16x8 zv = dequant_block<G>(t, kb);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(zv, sm.q[(KB * hf + kb) * 64 + l], sacc, 0, 0, 0);
+        *reinterpret_cast<f16x8 *>(zrow + 64 * hf + 8 * kb) = zv;
       }
       // rope dims 16 g + 8 hf ..
-      f16x8 rv;
-      if (RQ) {
-        const uint32_t cr = t.rope.x, szr = t.rope.y;
-        const f16x2 sc = __builtin_bit_cast(f16x2, (szr & 0xffffu) * 0x10001u);
-        const f16x2 zr = __builtin_bit_cast(f16x2, (szr >> 16) * 0x10001u);
-        const f16x2 k1024 = f16x2{static_cast<f16>(1024.0f), static_cast<f16>(1024.0f)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t bb = cr >> (8 * j);
-          const uint32_t pair = (bb & 0xfu) | (((bb >> 4) & 0xfu) << 16) | 0x64006400u;
-          const f16x2 h2 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, pair) - k1024, sc, zr);
-          rv[2 * j] = h2[0];
-          rv[2 * j + 1] = h2[1];
-        }
-      } else {
-        const uint32_t rws[4] = {t.rope.x, t.rope.y, t.rope.z, t.rope.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          rv[2 * j] = static_cast<f16>(__uint_as_float(rws[j] << 16));
-          rv[2 * j + 1] = static_cast<f16>(__uint_as_float(rws[j] & 0xffff0000u));
-        }
-      }
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(rv, sm.q[(KB * hf + KB - 1) * 64 + l], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_rope<RQ>(t), sm.q[(KB * hf + KB - 1) * 64 + l], sacc, 0,
+                                                    0, 0);
     }
     // ---- online softmax of row n over tokens 4g .. 4g + 3 of the chunk ----
     float s[4];
@@ -604,6 +562,17 @@ __global__ __launch_bounds__(512, 1) void splitk_rows16_kernel(DecodeArgs a, int
 }
 }  // namespace
 
+SplitK splitk_kernel_for(int rows, bool sparse) {
+  return (!sparse && rows <= 16) ? SplitK::kRows16 : SplitK::kWarpSpec;
+}
+
+int splitk_target_items(int rows, bool sparse, int ncu) {
+  // one workgroup per compute unit: the 16-row kernel's eight waves, or a
+  // 64-row block of the warp-specialised kernel
+  const int t = splitk_kernel_for(rows, sparse) == SplitK::kRows16 ? ncu : ncu / ((rows + ROWS - 1) / ROWS);
+  return t < 1 ? 1 : t;
+}
+
 hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
   TimedLaunch tl("splitk_decode", s);
   const int M = a.d.num_heads * a.Tq;
@@ -617,10 +586,7 @@ hipError_t launch_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
   const int n_logical = n_items * rb_count;
   const int grid = ((n_logical + 7) / 8) * 8;
   const bool rq = a.d.rope_bits == 4;
-#ifndef MLA_SPLITK_ROWS16
-#define MLA_SPLITK_ROWS16 1
-#endif
-  if (MLA_SPLITK_ROWS16 && M <= 16 && a.sel == nullptr) {
+  if (splitk_kernel_for(M, a.sel != nullptr) == SplitK::kRows16) {
     const int n_items16 = std::min(a.max_items, std::max(a.target_items, a.B));
     const int grid16 = ((n_items16 + 7) / 8) * 8;
 #define MLA_ROWS16_LAUNCH(G_, RQ_) splitk_rows16_kernel<G_, RQ_><<<grid16, 512, 0, s>>>(a, n_items16)

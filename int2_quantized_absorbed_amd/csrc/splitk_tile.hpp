@@ -36,6 +36,13 @@ __device__ __forceinline__ f16x4 ds_read_tr16(const f16 *p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
+// ds_read_b64_tr_b16 at an LDS byte address
+__device__ __forceinline__ f16x4 ds_read_tr16_lds(uint32_t addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<s16x4 __attribute__((address_space(3))) *>(static_cast<uintptr_t>(addr)));
+  return __builtin_bit_cast(f16x4, v);
+}
+
 // Workgroup barrier that only waits for this wave's LDS operations.  HIP's
 // __syncthreads() also waits for every outstanding global load, which would
 // force the next tile's prefetch to land at the first barrier of each tile.
@@ -137,29 +144,31 @@ __device__ __forceinline__ f16x2 code_pair(uint32_t nibbles) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nibbles, 2.0f, BYTE);
 }
 
-// codes -> fp16 score B operands.  Per code word (16 channels): two masks
-// split the codes of channels (4j, 4j+2) and (4j+1, 4j+3) into nibbles, then
-// per pair one conversion and one fused fp16 multiply-add with the group's
-// (scale, zero): z_hat = zero + scale * c with one rounding.
-template <int G, bool RQ = false>
-__device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB]) {
+// codes -> fp16.  Per code word (16 channels): two masks split the codes of
+// channels (4j, 4j+2) and (4j+1, 4j+3) into nibbles, then per pair one
+// conversion and one fused fp16 multiply-add with the group's (scale, zero):
+// z_hat = zero + scale * c with one rounding.  Latent K-block kb (0..7) of
+// the tile is code word kb / 2, pairs kb % 2: the eight channels
+// slot_channel(hf, kb, 0..7) of the lane's slice.
+template <int G>
+__device__ __forceinline__ f16x8 dequant_block(const RawTile &t, int kb) {
   const uint32_t cws[4] = {t.codes.x, t.codes.y, t.codes.z, t.codes.w};
   const uint32_t szw[4] = {t.sz.x, t.sz.y, t.sz.z, t.sz.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t sz = szw[(G == 32) ? (q >> 1) : q];
-    const f16x2 sc = __builtin_bit_cast(f16x2, (sz & 0xffffu) * 0x10001u);
-    const f16x2 zr = __builtin_bit_cast(f16x2, (sz >> 16) * 0x10001u);
-#pragma unroll
-    for (int odd = 0; odd < 2; ++odd) {
-      const uint32_t u = (cws[q] >> (2 * odd)) & 0x33333333u;
-      const f16x2 c0 = __builtin_elementwise_fma(code_pair<0>(u), sc, zr);
-      const f16x2 c1 = __builtin_elementwise_fma(code_pair<1>(u), sc, zr);
-      const f16x2 c2 = __builtin_elementwise_fma(code_pair<2>(u), sc, zr);
-      const f16x2 c3 = __builtin_elementwise_fma(code_pair<3>(u), sc, zr);
-      bz[2 * q + odd] = f16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-    }
-  }
+  const int q = kb >> 1, odd = kb & 1;
+  const uint32_t sz = szw[(G == 32) ? (q >> 1) : q];
+  const f16x2 sc = __builtin_bit_cast(f16x2, (sz & 0xffffu) * 0x10001u);
+  const f16x2 zr = __builtin_bit_cast(f16x2, (sz >> 16) * 0x10001u);
+  const uint32_t u = (cws[q] >> (2 * odd)) & 0x33333333u;
+  const f16x2 c0 = __builtin_elementwise_fma(code_pair<0>(u), sc, zr);
+  const f16x2 c1 = __builtin_elementwise_fma(code_pair<1>(u), sc, zr);
+  const f16x2 c2 = __builtin_elementwise_fma(code_pair<2>(u), sc, zr);
+  const f16x2 c3 = __builtin_elementwise_fma(code_pair<3>(u), sc, zr);
+  return f16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+}
+
+// The rope K-block of the tile (8 rope dims) as fp16.
+template <bool RQ>
+__device__ __forceinline__ f16x8 dequant_rope(const RawTile &t) {
   f16x8 v;
   if (RQ) {
     // 4-bit rope codes: byte j holds dims 2j (low nibble) and 2j+1.  The
@@ -185,7 +194,16 @@ __device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB]) {
       v[2 * j + 1] = static_cast<f16>(__uint_as_float(rws[j] & 0xffff0000u));
     }
   }
-  bz[8] = v;
+  return v;
+}
+
+// The whole tile: the score operands of the lane's slice (8 latent K-blocks
+// and the rope K-block).
+template <int G, bool RQ = false>
+__device__ __forceinline__ void dequant(const RawTile &t, f16x8 (&bz)[KB]) {
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) bz[kb] = dequant_block<G>(t, kb);
+  bz[8] = dequant_rope<RQ>(t);
 }
 
 }  // namespace
