@@ -265,8 +265,9 @@ size_t mla_decode_workspace_size(const mla_dims *dims, int32_t batch,
  * Requirements: 1 <= tq <= 64; batch >= 0 (0 = nothing to do);
  * kv_lora_rank <= 512 (UNSUPPORTED otherwise); the caller keeps
  * seq_base[b] + seq_len[b] <= capacity (not checkable on the host).
- * Operand range: the MFMA path (H*tq >= 16) multiplies fp16 operands with
- * fp32 accumulation, so |q_nope|, |q~ * softmax_scale * log2(e)|,
+ * Operand range: the MFMA path (kv_lora_rank 512, qk_rope_head_dim 64,
+ * group_size 16 or 32, qk_nope_head_dim a multiple of 16) multiplies fp16
+ * operands with fp32 accumulation, so |q_nope|, |q~ * softmax_scale * log2(e)|,
  * |q_rope * softmax_scale * log2(e)|, |k_rope| and |z_hat| must stay below
  * 65504 (the fp16 maximum); beyond it an operand overflows to infinity and
  * the rows it touches come out undefined.  No range check is made.  Each
@@ -540,10 +541,10 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status status);
 int32_t mla_abi_version(void);
 
-/* Decode kernel selection, for tests and measurement: 0 = automatic (MFMA
- * split-K when H*tq >= 16 and the shape has an MFMA kernel, else the
- * vector-ALU split-K kernel), 1 = always the vector-ALU kernel, 2 = always
- * MFMA (MLA_ERR_UNSUPPORTED where no MFMA kernel fits).  Process-wide. */
+/* Decode kernel selection, for tests and measurement: 0 = automatic (the
+ * MFMA kernels wherever the shape has them, at any H*tq; else the vector-ALU
+ * split-K kernel), 1 = always the vector-ALU kernel, 2 = always MFMA
+ * (MLA_ERR_UNSUPPORTED where no MFMA kernel fits).  Process-wide. */
 mla_status mla_set_decode_variant(int32_t variant);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around

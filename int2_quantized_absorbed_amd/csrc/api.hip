@@ -656,7 +656,9 @@ mla_status decode_impl(const char *fn, const mla_dims *dims, const uint16_t *q_n
       return fail(MLA_ERR_UNSUPPORTED, F("no MFMA kernel for this shape"));
     use_mfma = true;
   } else if (g_decode_variant == 0) {
-    use_mfma = M >= 16 && mfma_decode_supported(*dims, M);
+    // the MFMA kernels wherever the shape has them (at most 16 query rows
+    // take the 16-row kernel), else the vector-ALU kernel
+    use_mfma = mfma_decode_supported(*dims, M) && mfma_absorb_supported(*dims);
   }
   if (use_mfma && !mfma_absorb_supported(*dims))
     return fail(MLA_ERR_UNSUPPORTED, F("qk_nope_head_dim must be a multiple of 16 for the MFMA path"));
