@@ -296,9 +296,8 @@ struct GqaWs {
 };
 
 // Work items of the grouped-query split-K: one wave per item on the MFMA
-// kernel, eight resident per CU (two waves per SIMD at its register count);
-// otherwise the vector-ALU kernel's own target.
-constexpr int kGqaWavesPerCu = 8;
+// kernels, as many as are resident per CU (gqa_waves_per_cu); otherwise the
+// vector-ALU kernel's own target.
 
 bool gqa_use_mfma(const gqa_dims &g, int Tq) {
   const int rows = g.num_q_heads / g.num_kv_heads * Tq;
@@ -307,7 +306,7 @@ bool gqa_use_mfma(const gqa_dims &g, int Tq) {
 
 int gqa_target_items(const gqa_dims &g, int Tq) {
   const int rows = g.num_q_heads / g.num_kv_heads * Tq;
-  return gqa_use_mfma(g, Tq) ? kGqaWavesPerCu * device_cu_count() : target_items(rows, false, false);
+  return gqa_use_mfma(g, Tq) ? gqa_waves_per_cu(rows) * device_cu_count() : target_items(rows, false, false);
 }
 
 GqaWs gqa_layout(const gqa_dims &g, int B, int Tq) {

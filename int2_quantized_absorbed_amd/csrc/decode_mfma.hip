@@ -362,6 +362,170 @@ __global__ __launch_bounds__(64) void gqa_splitk_mfma_kernel(DecodeArgs a) {
   }
 }
 
+// ---- grouped-query layers with at most 16 query rows per KV head ----
+// One wave per work item, 16-token chunks, no LDS shared between waves, so
+// a wave needs about 100 registers and several share a SIMD:
+//   lane (token n = l & 15, quarter g = l >> 4) holds dims 32g .. 32g + 31
+//   of token n's K and V entries (8 code bytes and the groups' (scale,
+//   zero) each), the next chunk's in flight;
+//   scores S^T[16 tokens x 16 rows] = K_hat Q^T: 4 v_mfma_f32_16x16x32_f16,
+//   K-step kb taking the eight dims 32g + slot_channel(0, kb, e) of each
+//   lane's quarter (dequant_block's order), the rotated queries gathered
+//   into the same order once per item;
+//   the score lanes hold P^T in the layout of the next product's B operand;
+//   O^T[128 x 16 rows] += V_hat^T P^T: 8 v_mfma_f32_16x16x16_f16, V_hat^T
+//   read with ds_read_b64_tr_b16 from the wave's LDS copy of the chunk.
+// The partial (O / l fp16, m, l) goes out through the same LDS tile.
+constexpr int GQ16_ZS = GQ_D + 16;  // halves per V tile row
+
+template <int G>
+__device__ __forceinline__ RawTile gqa16_load(const mla_cache &c, int64_t slot, int g) {
+  RawTile t;
+  const uint2 cw = *reinterpret_cast<const uint2 *>(c.codes + slot * (GQ_D / 4) + 8 * g);
+  t.codes = uint4{cw.x, cw.y, 0u, 0u};
+  if (G == 32) {
+    t.sz = uint4{*reinterpret_cast<const uint32_t *>(c.scale_zero + (slot * (GQ_D / G) + g) * 2), 0u, 0u, 0u};
+  } else {
+    const uint2 s2 = *reinterpret_cast<const uint2 *>(c.scale_zero + (slot * (GQ_D / G) + 2 * g) * 2);
+    t.sz = uint4{s2.x, s2.y, 0u, 0u};
+  }
+  t.rope = uint4{0u, 0u, 0u, 0u};
+  return t;
+}
+
+template <int G>
+__global__ __launch_bounds__(64, 4) void gqa_rows16_kernel(DecodeArgs a) {  // registers for four waves per SIMD
+  __shared__ __align__(16) f16 zv_s[16 * GQ16_ZS];
+  const int item = blockIdx.x;
+  if (item >= a.meta[0]) return;
+  const WorkItem it = a.items[item];
+  const int l = threadIdx.x, n = l & 15, g = l >> 4;
+  const int Gq = a.d.num_heads;  // query heads per KV head
+  const int M = Gq * a.Tq;
+  const int L = a.seq_len[it.b];
+  const int64_t base = a.seq_base[it.b];
+  const int n_chunks = (it.t1 - it.t0 + 15) / 16;
+
+  // rotated queries of row n as score B operands (rows past M: zero)
+  f16x8 q[4];
+  {
+    const float *qr = static_cast<const float *>(a.qbuf) + (static_cast<int64_t>(it.b) * M + min(n, M - 1)) * GQ_D;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[kb][e] = static_cast<f16>(n < M ? qr[32 * g + slot_channel(0, kb, e)] : 0.0f);
+  }
+  const int vis = n < M ? (a.causal ? (L - a.Tq + n / Gq + 1) : L) : -1;
+  const int lim = min(it.t1, vis);  // tokens < lim are visible to row n
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 o[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{};
+  // lane's token of chunk c (past the item: its last token, masked)
+  auto chunk_slot = [&](int c) -> int64_t { return base + min(it.t0 + 16 * c + n, it.t1 - 1); };
+  const uint32_t ztr = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>(zv_s + (4 * g + ((l & 15) >> 2)) * GQ16_ZS + 4 * (l & 3)));
+
+  // one chunk: request chunk c + 1 into (nk, nv) (a harmless re-read past
+  // the end), then process chunk c from (ck, cv)
+  auto chunk = [&](int c, const RawTile &ck, const RawTile &cv, RawTile &nk, RawTile &nv) {
+    const int64_t sn = chunk_slot(c + 1);
+    nk = gqa16_load<G>(a.cache, sn, g);
+    nv = gqa16_load<G>(a.vcache, sn, g);
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_block<G>(ck, kb), q[kb], sacc, 0, 0, 0);
+    // the V chunk into LDS: row n, columns 32g + 8kb .. (slot order)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      *reinterpret_cast<f16x8 *>(zv_s + n * GQ16_ZS + 32 * g + 8 * kb) = dequant_block<G>(cv, kb);
+    // online softmax of row n over tokens 4g .. 4g + 3 of the chunk
+    float s[4];
+    const int tok0 = it.t0 + 16 * c + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = (tok0 + i < lim) ? sacc[i] : -INFINITY;
+    const float lmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__any(lmax > m_run + kRescaleThreshold ? 1 : 0)) {
+      float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (tmax > m_run + kRescaleThreshold) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - tmax);  // 0 on the row's first visible chunk
+        if (m_run != -INFINITY) {
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct) o[ct] *= alpha;
+        }
+        l_run *= alpha;
+        m_run = tmax;
+      }
+    }
+    const float m_sub = (m_run == -INFINITY) ? 0.0f : m_run;
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(s[i] - m_sub);  // masked: 0
+    l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    const f16x4 pb = f16x4{static_cast<f16>(pe[0]), static_cast<f16>(pe[1]), static_cast<f16>(pe[2]),
+                           static_cast<f16>(pe[3])};
+    // the V tile crosses lanes: its stores above the transposing reads
+    __builtin_amdgcn_wave_barrier();
+    uint32_t zb = ztr;
+    asm volatile("" : "+v"(zb));
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      o[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(ds_read_tr16_lds(zb + 32 * ct), pb, o[ct], 0, 0, 0);
+    // the next chunk's V stores after these reads
+    __builtin_amdgcn_wave_barrier();
+  };
+  RawTile ka, va, kb2, vb;
+  if (n_chunks > 0) {
+    ka = gqa16_load<G>(a.cache, chunk_slot(0), g);
+    va = gqa16_load<G>(a.vcache, chunk_slot(0), g);
+  }
+  // chunks in pairs, the two register sets in turn; an odd count's last pair
+  // ends with a chunk past the item, all of whose tokens are masked (a
+  // branch around it would let the compiler share the sets, and every chunk
+  // would then wait for its own prefetch)
+  for (int c = 0; c < n_chunks; c += 2) {
+    chunk(c, ka, va, kb2, vb);
+    chunk(c + 1, kb2, vb, ka, va);
+  }
+
+  // ---- the partial: (m, l) of row n, O / l through the V tile ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  if (g == 0 && n < M) {
+    a.part_ml[(static_cast<int64_t>(item) * M + n) * 2 + 0] = m_run;
+    a.part_ml[(static_cast<int64_t>(item) * M + n) * 2 + 1] = l_run;
+  }
+  // O tile ct holds LDS column 16 ct + 4 g + i of row n
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+    *reinterpret_cast<f16x4 *>(zv_s + n * GQ16_ZS + 16 * ct + 4 * g) = __builtin_convertvector(o[ct] * inv_l, f16x4);
+  __builtin_amdgcn_wave_barrier();
+  // unit (row, 16-column block ct): LDS column 16 ct + 8 (kb & 1) + e is
+  // channel 16 ct + 4 (e / 2) + (kb & 1) + 2 (e & 1)
+  f16 *po = reinterpret_cast<f16 *>(a.part_o);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = l + 64 * k, row = u >> 3, ct = u & 7;
+    const f16x8 a0 = *reinterpret_cast<const f16x8 *>(zv_s + row * GQ16_ZS + 16 * ct);
+    const f16x8 a1 = *reinterpret_cast<const f16x8 *>(zv_s + row * GQ16_ZS + 16 * ct + 8);
+    if (row < M) {
+      f16 outv[16];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        outv[4 * (e >> 1) + 2 * (e & 1)] = a0[e];
+        outv[4 * (e >> 1) + 1 + 2 * (e & 1)] = a1[e];
+      }
+      f16 *dst = po + (static_cast<int64_t>(item) * M + row) * GQ_D + 16 * ct;
+      *reinterpret_cast<f16x8 *>(dst) = f16x8{outv[0], outv[1], outv[2], outv[3], outv[4], outv[5], outv[6], outv[7]};
+      *reinterpret_cast<f16x8 *>(dst + 8) =
+          f16x8{outv[8], outv[9], outv[10], outv[11], outv[12], outv[13], outv[14], outv[15]};
+    }
+  }
+}
+
 }  // namespace
 
 bool mfma_absorb_supported(const mla_dims &d) { return d.qk_nope_head_dim % 16 == 0; }
@@ -416,8 +580,19 @@ bool gqa_mfma_supported(const mla_dims &d, int rows) {
          (d.group_size == 16 || d.group_size == 32);
 }
 
+// Up to five 16-row waves fit a SIMD, but each more item adds partials to
+// merge: three per SIMD measured fastest for the whole step.
+int gqa_waves_per_cu(int rows) { return rows <= 16 ? 12 : 8; }
+
 hipError_t launch_gqa_splitk_mfma(const DecodeArgs &a, hipStream_t s) {
   TimedLaunch tl("splitk_decode", s);
+  if (a.d.num_heads * a.Tq <= 16) {
+    if (a.d.group_size == 32)
+      gqa_rows16_kernel<32><<<a.max_items, 64, 0, s>>>(a);
+    else
+      gqa_rows16_kernel<16><<<a.max_items, 64, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (a.d.group_size == 32)
     gqa_splitk_mfma_kernel<32><<<a.max_items, 64, 0, s>>>(a);
   else

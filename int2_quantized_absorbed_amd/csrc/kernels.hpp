@@ -150,6 +150,9 @@ int splitk_target_items(int rows, bool sparse, int ncu);
 // grouped-query layers: head dim 128, at most 32 query rows per KV head,
 // one wave per work item (grid = max_items)
 bool gqa_mfma_supported(const mla_dims &d, int rows);
+// resident waves per compute unit of the grouped-query MFMA kernel for
+// `rows` query rows per KV head (its work-item target per compute unit)
+int gqa_waves_per_cu(int rows);
 hipError_t launch_gqa_splitk_mfma(const DecodeArgs &a, hipStream_t s);
 
 }  // namespace mla

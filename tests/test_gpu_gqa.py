@@ -186,6 +186,8 @@ DECODE_CASES = [
     (64, 32, 4, 16, [5, 64, 2049], 2, True),
     (128, 8, 8, 16, [1, 31, 32, 33, 4000], 4, True),
     (128, 32, 2, 32, [900, 77], 2, True),
+    (128, 16, 1, 32, [600, 45, 1], 1, True),    # 16 rows per KV head: the 16-row kernel's largest
+    (128, 8, 4, 16, [2100, 130], 8, True),      # 2 x 8 drafts = 16 rows, G = 16
 ]
 
 
