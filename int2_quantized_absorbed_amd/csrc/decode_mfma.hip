@@ -236,7 +236,10 @@ __global__ __launch_bounds__(64) void gqa_splitk_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) aq[kb][e] = static_cast<f16>(l32 < M ? qr[slot_channel(hf, kb, e)] : 0.0f);
+      for (int e = 0; e < 8; ++e) {  // (row pointer clamped: loads without a branch)
+        const float x = qr[slot_channel(hf, kb, e)];
+        aq[kb][e] = static_cast<f16>(l32 < M ? x : 0.0f);
+      }
   }
   // softmax ownership: row l32, tokens 8 j + 4 hf + i (j, i < 4) of each tile
   const int vis = l32 < M ? (a.causal ? (L - a.Tq + l32 / Gq + 1) : L) : -1;
@@ -410,10 +413,15 @@ __global__ __launch_bounds__(64, 4) void gqa_rows16_kernel(DecodeArgs a) {  // r
   f16x8 q[4];
   {
     const float *qr = static_cast<const float *>(a.qbuf) + (static_cast<int64_t>(it.b) * M + min(n, M - 1)) * GQ_D;
+    // (the row pointer is clamped, so every load is valid and none needs a
+    // branch: all 32 are in flight together)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[kb][e] = static_cast<f16>(n < M ? qr[32 * g + slot_channel(0, kb, e)] : 0.0f);
+      for (int e = 0; e < 8; ++e) {
+        const float x = qr[32 * g + slot_channel(0, kb, e)];
+        q[kb][e] = static_cast<f16>(n < M ? x : 0.0f);
+      }
   }
   const int vis = n < M ? (a.causal ? (L - a.Tq + n / Gq + 1) : L) : -1;
   const int lim = min(it.t1, vis);  // tokens < lim are visible to row n
@@ -432,6 +440,7 @@ __global__ __launch_bounds__(64, 4) void gqa_rows16_kernel(DecodeArgs a) {  // r
     const int64_t sn = chunk_slot(c + 1);
     nk = gqa16_load<G>(a.cache, sn, g);
     nv = gqa16_load<G>(a.vcache, sn, g);
+    if (c >= n_chunks) return;  // a pair's second chunk past the item: its request only
     f32x4 sacc = f32x4{};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -481,10 +490,10 @@ __global__ __launch_bounds__(64, 4) void gqa_rows16_kernel(DecodeArgs a) {  // r
     ka = gqa16_load<G>(a.cache, chunk_slot(0), g);
     va = gqa16_load<G>(a.vcache, chunk_slot(0), g);
   }
-  // chunks in pairs, the two register sets in turn; an odd count's last pair
-  // ends with a chunk past the item, all of whose tokens are masked (a
-  // branch around it would let the compiler share the sets, and every chunk
-  // would then wait for its own prefetch)
+  // chunks in pairs, the two register sets in turn (a branch around a
+  // pair's second chunk would let the compiler share the sets, and every
+  // chunk would then wait for its own prefetch; past the item it issues its
+  // request and stops)
   for (int c = 0; c < n_chunks; c += 2) {
     chunk(c, ka, va, kb2, vb);
     chunk(c + 1, kb2, vb, ka, va);

@@ -395,6 +395,7 @@ __global__ __launch_bounds__(512, 1) void splitk_rows16_kernel(DecodeArgs a, int
   // lane (token n of the chunk, quarter g): its cache slot (dense decode
   // only: a slot indirection would put a dependent load, and with it a wait
   // for every load in flight, in front of each chunk's requests)
+  // (chunks past the item read its last token; their tokens are masked)
   auto chunk_slot = [&](int c) -> int64_t { return base + min(it.t0 + 16 * c + n, it.t1 - 1); };
   f16 *zt = sm.z[v];
   f32x4 o[32];
@@ -416,13 +417,15 @@ __global__ __launch_bounds__(512, 1) void splitk_rows16_kernel(DecodeArgs a, int
   }
   lds_barrier();  // the query operands (the chunk loads in flight stay in flight)
   // one chunk: request the wave's next chunk c + 8 into (rn0, rn1), then
-  // process chunk c from (rc0, rc1)
+  // process chunk c from (rc0, rc1).  The request is unconditional (past
+  // the item it re-reads the item's last token): with a branch around it
+  // the waits for the chunk in hand would also wait for the request.  A
+  // chunk past the item stops after its request.
   auto chunk = [&](int c, const RawTile &rc0, const RawTile &rc1, RawTile &rn0, RawTile &rn1) {
-    if (c + 8 < n_chunks) {
-      const int64_t sn = chunk_slot(c + 8);
-      rn0 = load_tile<G, RQ>(a, sn, g, 0);
-      rn1 = load_tile<G, RQ>(a, sn, g, 1);
-    }
+    const int64_t sn = chunk_slot(c + 8);
+    rn0 = load_tile<G, RQ>(a, sn, g, 0);
+    rn1 = load_tile<G, RQ>(a, sn, g, 1);
+    if (c >= n_chunks) return;  // a pair's second chunk past the item: its request only
     // ---- scores: one K-block (8 channels of the lane's quarter) at a time ----
     f32x4 sacc = f32x4{};
     f16 *zrow = zt + n * R16_ZS + 128 * g;
@@ -481,9 +484,12 @@ __global__ __launch_bounds__(512, 1) void splitk_rows16_kernel(DecodeArgs a, int
     // the next chunk's Z stores after these reads
     __builtin_amdgcn_wave_barrier();
   };
+  // chunks in pairs, the two register sets in turn (a branch around a
+  // pair's second chunk would let the compiler share the sets; past the
+  // item it issues its request and stops)
   for (int c = v; c < n_chunks; c += 16) {
     chunk(c, ta0, ta1, tb0, tb1);
-    if (c + 8 < n_chunks) chunk(c + 8, tb0, tb1, ta0, ta1);
+    chunk(c + 8, tb0, tb1, ta0, ta1);
   }
   // ---- merge the eight waves ----
   l_run += __shfl_xor(l_run, 16);
