@@ -550,16 +550,16 @@ __global__ __launch_bounds__(512, 1) void splitk_rows16_kernel(DecodeArgs a, int
     a.part_ml[(static_cast<int64_t>(item) * M + rn) * 2 + 1] = den;
   }
   // column block ct = (quarter q, half hf, K-block pair j) = 8 q + 4 hf + j
-  // covers channels 128 q + 64 hf + 16 j .. + 16; its column 8 (kb & 1) + e
-  // is channel slot_channel(hf, kb, e)
+  // covers channels 128 q + 64 hf + 16 j .. + 16; its column 8 b + e is
+  // K-block kb = 2 j + b, channel slot_channel(hf, kb, e) = 64 hf + 16 j +
+  // slot_channel(0, b, e): the same permutation in every block, with indices
+  // known at compile time (a register array indexed at run time would be
+  // lowered to a compare and a select per element)
   if (rn < M) {
     const int q = ct >> 3, hf = (ct >> 2) & 1, j = ct & 3;
     f16 outv[16];
 #pragma unroll
-    for (int col = 0; col < 16; ++col) {
-      const int kb = 2 * j + (col >> 3), e = col & 7;
-      outv[slot_channel(hf, kb, e) - 64 * hf - 16 * j] = static_cast<f16>(acc[col]);
-    }
+    for (int col = 0; col < 16; ++col) outv[slot_channel(0, col >> 3, col & 7)] = static_cast<f16>(acc[col]);
     f16 *dst = reinterpret_cast<f16 *>(a.part_o) + (static_cast<int64_t>(item) * M + rn) * R + 128 * q + 64 * hf + 16 * j;
     *reinterpret_cast<f16x8 *>(dst) = f16x8{outv[0], outv[1], outv[2], outv[3], outv[4], outv[5], outv[6], outv[7]};
     *reinterpret_cast<f16x8 *>(dst + 8) =
