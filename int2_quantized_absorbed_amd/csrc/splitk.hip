@@ -111,22 +111,27 @@ __global__ __launch_bounds__(512, 1) void splitk_ws_kernel(DecodeArgs a, int rb_
       for (int kb = kb0; kb < kb1; ++kb)
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bz[kb], aq[mt][kb], sacc[mt], 0, 0, 0);
     };
-    // Scores of the tile in bz, published to LDS.  With two row tiles the
-    // first tile's chain runs first, and its stores issue while the second
-    // chain is still in the MFMA pipe.
+    // Scores of the tile in bz, published to LDS, with the Z stores that
+    // precede the call (eight per lane) spread over the first MFMAs.  With
+    // two row tiles the first tile's chain runs first, and its stores issue
+    // between the second chain's MFMAs.
     auto scores_publish = [&]() {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
       if constexpr (MT == 2) {
         mfma_steps(0, 0, KB);
         mfma_steps(1, 0, 2);
+        interleave_stores<8, false>();
         __builtin_amdgcn_sched_barrier(0);
         publish_tile(0);
-        __builtin_amdgcn_sched_barrier(0);
         mfma_steps(1, 2, KB);
+        interleave_stores<4, true>();
+        __builtin_amdgcn_sched_barrier(0);
         publish_tile(1);
       } else {
         mfma_steps(0, 0, KB);
+        interleave_stores<8, false>();
+        __builtin_amdgcn_sched_barrier(0);
         publish_tile(0);
       }
     };

@@ -26,6 +26,27 @@ constexpr int KB = 9;           // K-blocks of 16 per wave: 8 latent + 1 rope
 // reads the tile).
 constexpr int ZSTRIDE = 144;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;     // MFMA
+constexpr int kSchedDsWrite = 0x200;  // LDS write
+
+// Orders the scheduling region that ends here as N pairs of one MFMA and
+// one LDS store (the store first if STORE_FIRST), the rest after them.
+// Issued in a burst, a wave's LDS stores queue at the LDS and hold up its
+// next instructions; one per MFMA they drain while the MFMAs run.
+template <int N, bool STORE_FIRST>
+__device__ __forceinline__ void interleave_stores() {
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    if constexpr (STORE_FIRST) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+    }
+  }
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
