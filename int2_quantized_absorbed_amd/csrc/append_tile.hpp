@@ -283,17 +283,20 @@ __device__ __forceinline__ void skinny_tile(const AppendParams &p, int ct, int t
   }
 }
 
-// The same tile for a workgroup of four waves that share one 32-token tile
-// (channel tiles ct of its waves): the tile's 32 latent rows are staged once
-// in LDS (`lat`, 32 rows x R / 8 pieces of 16 bytes, piece p of row t at
-// p ^ (t & 15): the 16 lanes of a read hit separate banks) while every wave
-// holds its R_apply^T rows for all K-steps in registers, so all operands
-// arrive in one memory round trip.  The MFMA sequence is the one above, so
-// the codes are the same bytes.  Side keys are not copied here
-// (side_key_block).  Called by all threads of the workgroup.
+// The same tile computed by wave 0 of a workgroup of four waves: all four
+// stage the 32-token tile's latent rows in LDS (`lat`, 32 rows x R / 8
+// pieces of 16 bytes, piece p of row t at p ^ (t & 15): the 16 lanes of a
+// read hit separate banks) while wave 0 holds the R_apply^T rows of channel
+// tile ct for all K-steps in registers, so all operands arrive in one memory
+// round trip; the other waves return after the staging.  One channel tile
+// per workgroup keeps the R_apply^T bytes each CU fetches at 32 rows.  The
+// MFMA sequence is the one above, so the codes are the same bytes.  Side
+// keys are not copied here (side_key_block).  Called by all threads of the
+// workgroup.
 template <int R, int G, int NACC>
 __device__ __forceinline__ void staged_skinny_tile(const AppendParams &p, int ct, int ty, int tid,
                                                    u32x4 *__restrict__ lat) {
+  const bool active = tid < 64;
   constexpr int KS = R / 16, PR = R / 8, PER = 32 * PR / 256;
   constexpr int NGT = 32 / G;
   static_assert(PER * 256 == 32 * PR, "whole rows per workgroup");
@@ -311,8 +314,10 @@ __device__ __forceinline__ void staged_skinny_tile(const AppendParams &p, int ct
   }
   const bf16x8 *arow = reinterpret_cast<const bf16x8 *>(p.Rt + static_cast<int64_t>(32 * ct + l32) * R);
   bf16x8 aq[KS];
+  if (active) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) aq[ks] = arow[2 * ks + hf];
+    for (int ks = 0; ks < KS; ++ks) aq[ks] = arow[2 * ks + hf];
+  }
   int64_t slot = -1;
   if (valid) slot = p.slots[tok];
   float alpha[NGT];
@@ -324,6 +329,7 @@ __device__ __forceinline__ void staged_skinny_tile(const AppendParams &p, int ct
     lat[t * PR + (pc ^ (t & 15))] = lv[j];
   }
   __syncthreads();
+  if (!active) return;
   f32x16 acc[NACC];
 #pragma unroll
   for (int a = 0; a < NACC; ++a) acc[a] = f32x16{};

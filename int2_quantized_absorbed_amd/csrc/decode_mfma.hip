@@ -31,9 +31,9 @@ constexpr int QTSTRIDE = 136;  // halves per staged row (128 channels + pad)
 // Query absorb (q~ = W~_UK^T q_nope per head, in split-K operand order), the
 // split-K planner (block (0, 0)), and optionally a decode step's small append
 // (columns 1 .. x0 - 1, dispatched right after the planner so its memory
-// round trip overlaps the absorb): per 32-token tile four 4-wave blocks of
-// four 32-channel tiles each (staged_skinny_tile, the latent rows shared in
-// LDS; the same MFMA sequence as the stand-alone append kernels, so the cache
+// round trip overlaps the absorb): per 32-token tile one block per 32-channel
+// tile (staged_skinny_tile: the latent rows staged in LDS, wave 0 computes;
+// the same MFMA sequence as the stand-alone append kernels, so the cache
 // bytes are identical), then one block for the tile's side keys (rope keys
 // copied or quantised to 4 bits, indexer keys).  The absorb blocks are the
 // columns from x0 on.
@@ -56,15 +56,14 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(DecodeArgs a, int rb_c
   }
   if constexpr (G != 0) {
     if (static_cast<int>(blockIdx.x) < x0) {
-      // append blocks: tiles (ct = 4 (blk % (R / 128)) + wave, ty = blk / (R / 128)),
-      // then the side-key blocks (token tile blk - n_tiles R / 128)
+      // append blocks: tiles (ct = blk % (R / 32), ty = blk / (R / 32)), then
+      // the side-key blocks (token tile blk - n_tiles R / 32)
       const int blk = (blockIdx.x - 1) * gridDim.y + blockIdx.y;
       const int n_tiles = static_cast<int>((ap.n + 31) / 32);
-      if (blk < n_tiles * (R / 128)) {
-        const int ty = blk / (R / 128), ct = 4 * (blk % (R / 128)) + (threadIdx.x >> 6);
-        staged_skinny_tile<R, G, 2>(ap, ct, ty, threadIdx.x, wk);
-      } else if (blk < n_tiles * (R / 128 + 1)) {
-        side_key_block(ap, blk - n_tiles * (R / 128), threadIdx.x);
+      if (blk < n_tiles * (R / 32)) {
+        staged_skinny_tile<R, G, 2>(ap, blk % (R / 32), blk / (R / 32), threadIdx.x, wk);
+      } else if (blk < n_tiles * (R / 32 + 1)) {
+        side_key_block(ap, blk - n_tiles * (R / 32), threadIdx.x);
       }
       return;
     }
@@ -573,8 +572,8 @@ hipError_t launch_absorb_mfma_layout(const DecodeArgs &a, hipStream_t s, const A
   ap.d_r = a.d.qk_rope_head_dim;
   ap.d_idx = a.d.index_head_dim;
   ap.rope_bits = a.d.rope_bits;
-  // per 32-token tile: four blocks of four 32-channel tiles, one side-key block
-  const int blocks = (R / 128 + 1) * static_cast<int>((job->n + 31) / 32);
+  // per 32-token tile: one block per 32-channel tile, one side-key block
+  const int blocks = (R / 32 + 1) * static_cast<int>((job->n + 31) / 32);
   const int cols = (blocks + gy - 1) / gy;
   const int x0 = 1 + cols;  // first absorb column
   if (a.d.group_size == 32)
