@@ -373,12 +373,18 @@ __global__ __launch_bounds__(256) void upproj_valu_kernel(DecodeArgs a) {
 //     O), kCombU items per round with their loads issued together; the
 //     slices are merged in slice order and o_z[j] = O / l goes to LDS (and
 //     lse out).
-//  2. Product: wave wv owns output columns 16 wv .. 16 wv + 15 and lane l
-//     latent channels 8 l .. 8 l + 7; the lane's slice of W~_UV[h] (16 rows x
-//     8 channels, fp16) is loaded at kernel start, so it is in flight during
-//     the merge.  Each lane forms RT x 16 eight-term fp32 partial sums; a
-//     butterfly reduce-scatter over the 64 lanes adds them up (lane l ends
-//     with the output l >> (6 - log2(16 RT)) in full).
+//  2. Product: wave wv owns output columns 16 wv .. 16 wv + 15; its slice of
+//     W~_UV[h] (fp16) is loaded at kernel start, so it is in flight during
+//     the merge.
+//     RT = 4: on MFMA (v_mfma_f32_16x16x32_f16), the RT rows padded to 16,
+//     K = the 512 latent channels in 16 steps; lane l holds W~_UV rows
+//     16 wv + (l & 15) at channels 32 ks + 8 (l >> 4) ..; o_z is staged in
+//     LDS as two fp16 parts (hi + lo), each its own product chain, so the
+//     result keeps about fp32 precision of o_z.
+//     RT < 4 (the MFMA tile would be mostly padding): lane l holds latent
+//     channels 8 l .. 8 l + 7 of the 16 rows and forms RT x 16 eight-term
+//     fp32 partial sums; a butterfly reduce-scatter over the 64 lanes adds
+//     them up (lane l ends with the output l >> (6 - log2(16 RT)) in full).
 constexpr int kFuseR = 512, kFuseDv = 128, kFuseThreads = 512, kFuseMaxRows = 16, kCombU = 16;
 
 // p[0 .. N) summed over the lanes that differ in bits log2(D) .. log2(D) - log2(N) + 1:
@@ -402,10 +408,16 @@ template <int RT>
 __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs a, int n_rt, int n_logical) {
   constexpr int S = 4 / RT, CH = kFuseR / 4;
   constexpr int V = 16 * RT, LOGV = RT == 1 ? 4 : (RT == 2 ? 5 : 6);
+  constexpr bool kMfma = RT == 4;
+  // o_z: fp32 for the vector-ALU product; fp16 hi and lo parts for the
+  // MFMA one, rows padded 16 bytes so the 16-lane groups of an operand read
+  // (rows 1040 bytes apart) fall on separate banks
+  constexpr int ZST = kFuseR + 8;
   static_assert(S * RT * CH == kFuseThreads, "one (slice, row, chunk) per thread");
   __shared__ f32x4 s_o[S][RT][CH];
   __shared__ float s_m[S][RT], s_l[S][RT];
-  __shared__ __align__(16) float s_z[RT][kFuseR];
+  __shared__ __align__(16) float s_z[kMfma ? 1 : RT][kFuseR];
+  __shared__ __align__(16) f16 s_zh[kMfma ? RT : 1][ZST], s_zl[kMfma ? RT : 1][ZST];
   const int per_xcd = (n_logical + 7) / 8;
   const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (logical >= n_logical) return;
@@ -413,11 +425,15 @@ __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs
   const int H = a.d.num_heads, M = H * a.Tq, nrows = a.B * a.Tq;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
+  // MFMA: wr[ks] = rows 16 wv + (lane & 15), channels 32 ks + 8 (lane >> 4) ..;
+  // vector ALU: wr[i] = row 16 wv + i, channels 8 lane ..
   f16x8 wr[16];
   {
-    const uint16_t *wp = a.w_uv_f + (static_cast<int64_t>(h) * kFuseDv + 16 * wv) * kFuseR + 8 * lane;
+    const uint16_t *wp =
+        kMfma ? a.w_uv_f + (static_cast<int64_t>(h) * kFuseDv + 16 * wv + (lane & 15)) * kFuseR + 8 * (lane >> 4)
+              : a.w_uv_f + (static_cast<int64_t>(h) * kFuseDv + 16 * wv) * kFuseR + 8 * lane;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wr[i] = *reinterpret_cast<const f16x8 *>(wp + i * kFuseR);
+    for (int i = 0; i < 16; ++i) wr[i] = *reinterpret_cast<const f16x8 *>(wp + i * (kMfma ? 32 : kFuseR));
   }
 
   // ---- 1. merge the partials ----
@@ -484,7 +500,15 @@ __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs
       }
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    *reinterpret_cast<f32x4 *>(&s_z[j][4 * c]) = o * inv;
+    const f32x4 z = o * inv;
+    if constexpr (kMfma) {
+      const f16x4 zh = __builtin_convertvector(z, f16x4);
+      *reinterpret_cast<f16x4 *>(&s_zh[j][4 * c]) = zh;
+      *reinterpret_cast<f16x4 *>(&s_zl[j][4 * c]) =
+          __builtin_convertvector(z - __builtin_convertvector(zh, f32x4), f16x4);
+    } else {
+      *reinterpret_cast<f32x4 *>(&s_z[j][4 * c]) = z;
+    }
     const int q = rt * RT + j;
     if (c == 0 && q < nrows && a.lse != nullptr)
       a.lse[static_cast<int64_t>(q) * H + h] = den > 0.0f ? (mx + log2f(den)) * kLn2 : -INFINITY;
@@ -492,6 +516,26 @@ __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs
   __syncthreads();
 
   // ---- 2. out = W~_UV[h] o_z ----
+  if constexpr (kMfma) {
+    // B operand: o_z row (lane & 15) (rows past RT repeat row RT - 1; their
+    // columns of the product are not stored), channels 32 ks + 8 (lane >> 4) ..
+    const f16 *zh = &s_zh[min(lane & 15, RT - 1)][8 * (lane >> 4)];
+    const f16 *zl = &s_zl[min(lane & 15, RT - 1)][8 * (lane >> 4)];
+    f32x4 acc_h = {0.0f, 0.0f, 0.0f, 0.0f}, acc_l = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      acc_h = __builtin_amdgcn_mfma_f32_16x16x32_f16(wr[ks], *reinterpret_cast<const f16x8 *>(zh + 32 * ks), acc_h,
+                                                     0, 0, 0);
+      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(wr[ks], *reinterpret_cast<const f16x8 *>(zl + 32 * ks), acc_l,
+                                                     0, 0, 0);
+    }
+    // lane holds out[row lane & 15][16 wv + 4 (lane >> 4) + i], i = 0..3
+    const int j = lane & 15, q = rt * RT + j;
+    if (j < RT && q < nrows)
+      *reinterpret_cast<f32x4 *>(a.out + (static_cast<int64_t>(q) * H + h) * kFuseDv + 16 * wv + 4 * (lane >> 4)) =
+          acc_h + acc_l;
+    return;
+  }
   float part[V];
 #pragma unroll
   for (int j = 0; j < RT; ++j) {
