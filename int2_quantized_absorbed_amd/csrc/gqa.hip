@@ -173,20 +173,39 @@ __global__ __launch_bounds__(kThreads) void gqa_rotate_q_kernel(GqaDecodeArgs a,
     a.base2[bp] = static_cast<int64_t>(h) * a.capacity + a.seq_base[b];
     a.len2[bp] = a.seq_len[b];
   }
-  // rows [CW cs, +CW) of R_apply^T[h] are CW * d contiguous values
-  {
-    const uint16_t *src = a.rk_t + (static_cast<int64_t>(h) * d + CW * cs) * d;
-    const int np = d / 8, total = CW * np;
-    for (int e = tid; e < total; e += kThreads)
-      *reinterpret_cast<u32x4 *>(rsm + (e / np) * rst + 8 * (e % np)) = reinterpret_cast<const u32x4 *>(src)[e];
-  }
+  // rows [CW cs, +CW) of R_apply^T[h] are CW * d contiguous values (at most
+  // kRotLoads 16-byte pieces per thread), requested together with the first
+  // pass's query values (at most kQLoads per thread): one memory round trip
   const uint16_t *qbase = a.q + ((static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G) * d;
   const int c = tid % CW, gl = tid / CW;
   constexpr int GP = kThreads / CW;  // query heads per pass
+  constexpr int kRotLoads = CW * 256 / 8 / kThreads, kQLoads = GP * 256 / kThreads;
+  const int np = d / 8, total = CW * np, nq0 = min(GP, G) * d;
+  {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.rk_t + (static_cast<int64_t>(h) * d + CW * cs) * d);
+    u32x4 rw[kRotLoads];
+    uint16_t qv[kQLoads];
+#pragma unroll
+    for (int k = 0; k < kRotLoads; ++k) rw[k] = src[min(tid + k * kThreads, total - 1)];  // clamped: always defined
+#pragma unroll
+    for (int k = 0; k < kQLoads; ++k) qv[k] = qbase[min(tid + k * kThreads, nq0 - 1)];
+#pragma unroll
+    for (int k = 0; k < kRotLoads; ++k) {
+      const int e = tid + k * kThreads;
+      if (e < total) *reinterpret_cast<u32x4 *>(rsm + (e / np) * rst + 8 * (e % np)) = rw[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kQLoads; ++k) {
+      const int e = tid + k * kThreads;
+      if (e < nq0) qs[e / d][e % d] = bf16_to_f32(qv[k]);
+    }
+  }
   for (int g0 = 0; g0 < G; g0 += GP) {
     const int ng = min(GP, G - g0);
-    __syncthreads();  // qs is rewritten (and, the first time, the rotation is staged)
-    for (int e = tid; e < ng * d; e += kThreads) qs[e / d][e % d] = bf16_to_f32(qbase[static_cast<int64_t>(g0) * d + e]);
+    if (g0 > 0) {
+      __syncthreads();  // qs is rewritten
+      for (int e = tid; e < ng * d; e += kThreads) qs[e / d][e % d] = bf16_to_f32(qbase[static_cast<int64_t>(g0) * d + e]);
+    }
     __syncthreads();
     if (gl < ng) {
       const float acc = dot_row(rsm + c * rst, qs[gl], d);
@@ -292,6 +311,111 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_unrotate_kernel(GqaDecodeA
   }
 }
 
+// The same merge and un-rotation for d = 128 with one block per query row
+// (pseudo-sequence b', position t, head g of the KV group), so no block
+// repeats another's merge.  Grid (B * H_kv * G, Tq), 256 threads.
+//  * Thread (slice s, 4-channel chunk c) folds items ib + s, ib + s + 8, ...
+//    of the row, kRowU per round with their loads issued together; the
+//    eight slices are merged in slice order into o_z (LDS) and lse.
+//  * Un-rotation out[v] = sum_c R_v,apply^T[c][v] o_z[c]: wave q sums
+//    channels c in [32 q, 32 q + 32), lane l the output pair (2 l, 2 l + 1);
+//    its 32 rotation words are requested at kernel start, so they are in
+//    flight during the merge; the four quarters are added in order.
+constexpr int kRowD = 128, kRowU = 8;
+
+__global__ __launch_bounds__(kThreads) void gqa_merge_row128_kernel(GqaDecodeArgs a, DecodeArgs sa) {
+  constexpr int NCH = kRowD / 4, S = kThreads / NCH;
+  static_assert(S * NCH == kThreads, "one (slice, chunk) per thread");
+  __shared__ f32x4 s_o[S][NCH];
+  __shared__ float s_m[S], s_l[S];
+  __shared__ __align__(16) float s_z[kRowD];
+  __shared__ float s_part[4][kRowD];
+  const int G = a.H_q / a.H_kv, M = G * a.Tq;
+  const int bp = blockIdx.x / G, g = blockIdx.x % G, t = blockIdx.y, b = bp / a.H_kv, h = bp % a.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, q4 = tid >> 6;
+  const int m = t * G + g;
+  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H_q + h * G + g;
+  uint32_t rv[32];
+  {
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(a.rv_t + (static_cast<int64_t>(h) * kRowD + 32 * q4) * kRowD) + lane;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) rv[i] = src[i * (kRowD / 2)];
+  }
+  {
+    const int c = tid % NCH, sl = tid / NCH;
+    const int ib = sa.item_begin[bp], ie = sa.item_begin[bp + 1];
+    const float *ml = sa.part_ml + static_cast<int64_t>(m) * 2;
+    const f16 *po = reinterpret_cast<const f16 *>(sa.part_o) + static_cast<int64_t>(m) * kRowD + 4 * c;
+    const int64_t ml_stride = static_cast<int64_t>(M) * 2, po_stride = static_cast<int64_t>(M) * kRowD;
+    float mrun = -INFINITY, lrun = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = ib + sl; k0 < ie; k0 += kRowU * S) {
+      f16x4 vv[kRowU];
+      float2 st[kRowU];
+#pragma unroll
+      for (int e = 0; e < kRowU; ++e) {
+        const int k = min(k0 + e * S, ie - 1);
+        vv[e] = *reinterpret_cast<const f16x4 *>(po + k * po_stride);
+        st[e] = *reinterpret_cast<const float2 *>(ml + k * ml_stride);
+        if (k0 + e * S >= ie) st[e].x = -INFINITY;
+      }
+      float rm = mrun;
+#pragma unroll
+      for (int e = 0; e < kRowU; ++e) rm = fmaxf(rm, st[e].x);
+      if (rm != -INFINITY) {
+        const float sc = exp2f(mrun - rm);  // 0 while nothing was folded in
+        acc *= sc;
+        lrun *= sc;
+#pragma unroll
+        for (int e = 0; e < kRowU; ++e) {
+          const float wgt = st[e].x == -INFINITY ? 0.0f : exp2f(st[e].x - rm);
+          acc += (wgt * st[e].y) * __builtin_convertvector(vv[e], f32x4);
+          lrun += wgt * st[e].y;
+        }
+        mrun = rm;
+      }
+    }
+    s_o[sl][c] = acc;
+    if (c == 0) {  // every chunk thread of a slice holds the same (max, sum)
+      s_m[sl] = mrun;
+      s_l[sl] = lrun;
+    }
+  }
+  __syncthreads();
+  if (tid < NCH) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sl = 0; sl < S; ++sl) mx = fmaxf(mx, s_m[sl]);
+    float den = 0.0f;
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int sl = 0; sl < S; ++sl) {
+        if (s_m[sl] == -INFINITY) continue;
+        const float wgt = exp2f(s_m[sl] - mx);
+        den += wgt * s_l[sl];
+        o += wgt * s_o[sl][tid];
+      }
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    *reinterpret_cast<f32x4 *>(&s_z[4 * tid]) = o * inv;
+    if (tid == 0 && a.lse != nullptr) a.lse[row] = den > 0.0f ? (mx + log2f(den)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float z = s_z[32 * q4 + i];
+    p0 = fmaf(__uint_as_float(rv[i] << 16), z, p0);
+    p1 = fmaf(__uint_as_float(rv[i] & 0xffff0000u), z, p1);
+  }
+  s_part[q4][2 * lane] = p0;
+  s_part[q4][2 * lane + 1] = p1;
+  __syncthreads();
+  if (tid < kRowD)
+    a.out[row * kRowD + tid] = (s_part[0][tid] + s_part[1][tid]) + (s_part[2][tid] + s_part[3][tid]);
+}
+
 }  // namespace
 
 hipError_t launch_gqa_calib_stats(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n, int d, int H_q,
@@ -321,6 +445,10 @@ hipError_t launch_gqa_rotate_q(const GqaDecodeArgs &a, const DecodeArgs &sa, hip
 hipError_t launch_gqa_merge_unrotate(const GqaDecodeArgs &a, const DecodeArgs &sa, hipStream_t s) {
   if (a.d > 256 || a.d % 16 != 0) return hipErrorInvalidValue;
   TimedLaunch tl("gqa_merge_unrotate", s);
+  if (a.d == kRowD) {
+    gqa_merge_row128_kernel<<<dim3(a.B * a.H_q, a.Tq), kThreads, 0, s>>>(a, sa);
+    return hipGetLastError();
+  }
   const int cw = rot_cw(a.d);
   const dim3 grid(a.B * a.H_kv * (a.d / cw), a.Tq);
   if (cw == 32)
