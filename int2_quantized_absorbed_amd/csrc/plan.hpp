@@ -105,6 +105,14 @@ __device__ inline void plan_block(const int32_t *__restrict__ seq_len, int B, in
     }
   }
   const int C = lo * tile;
+  // Items, 256 sequences at a time: thread b finds its sequence's item count
+  // and first item (a block-wide scan) and leaves them in LDS; then wave wv
+  // writes the items of sequences wv, wv + 4, ... of the group, its 64 lanes
+  // the consecutive items of one sequence (one thread writing a sequence's
+  // items in a loop took most of the planner's time).  Lane l fetches the
+  // values of the wave's sequence l of the group up front; the loop takes
+  // them from the lanes (readlane), not from LDS.
+  __shared__ int32_t s_first[256], s_count[256], s_chunk[256], s_len[256];
   int carry = 0;
   for (int base = 0; base < B; base += 256) {
     const int b = base + tid;
@@ -117,22 +125,32 @@ __device__ inline void plan_block(const int32_t *__restrict__ seq_len, int B, in
     int before = 0;
     for (int j = 0; j < wv; ++j) before += wtot[j];
     const int excl = carry + before + inc - nb;
-    if (b < B) {
-      item_begin[b] = min(excl, max_items);
-      for (int c = 0; c < nb; ++c) {
-        const int idx = excl + c;
+    s_first[tid] = excl;
+    s_count[tid] = nb;
+    s_chunk[tid] = chunk;
+    s_len[tid] = L;
+    if (b < B) item_begin[b] = min(excl, max_items);
+    __syncthreads();
+    const int cnt = min(256, B - base), nw = (cnt - wv + 3) / 4;  // the wave's sequences: wv + 4k, k < nw
+    const int jl = min(wv + 4 * lane, 255);
+    const int f_l = s_first[jl], n_l = s_count[jl], ch_l = s_chunk[jl], len_l = s_len[jl];
+    for (int k = 0; k < nw; ++k) {
+      const int first = __builtin_amdgcn_readlane(f_l, k), n = __builtin_amdgcn_readlane(n_l, k);
+      const int ch = __builtin_amdgcn_readlane(ch_l, k), Lj = __builtin_amdgcn_readlane(len_l, k);
+      for (int c = lane; c < n; c += 64) {
+        const int idx = first + c;
         if (idx < max_items) {
           WorkItem it;
-          it.b = b;
-          it.t0 = c * chunk;
-          it.t1 = min(L, (c + 1) * chunk);
+          it.b = base + wv + 4 * k;
+          it.t0 = c * ch;
+          it.t1 = min(Lj, (c + 1) * ch);
           it.pad = 0;
           items[idx] = it;
         }
       }
     }
     carry += (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
-    __syncthreads();  // wtot is rewritten by the next group
+    __syncthreads();  // wtot and the per-sequence arrays are rewritten by the next group
   }
   if (tid == 0) {
     const int n = min(carry, max_items);
