@@ -369,14 +369,15 @@ __global__ __launch_bounds__(256) void upproj_valu_kernel(DecodeArgs a) {
 // kFuseMaxRows query rows per head.  Block = (head h, tile of RT query rows),
 // 512 threads, blocks of one head on one XCD (they share W~_UV[h] in L2).
 //  1. Merge: thread (slice s, row j, 4-channel chunk c) folds items ib + s,
-//     ib + s + S, ... (S = 4 / RT slices) of row j into a running (max, sum,
+//     ib + s + S, ... (S = 4 / RT slices; with RT = 8 or 16 one slice and
+//     the rows j, j + 4, ... in turn) of row j into a running (max, sum,
 //     O), kCombU items per round with their loads issued together; the
 //     slices are merged in slice order and o_z[j] = O / l goes to LDS (and
 //     lse out).
 //  2. Product: wave wv owns output columns 16 wv .. 16 wv + 15; its slice of
 //     W~_UV[h] (fp16) is loaded at kernel start, so it is in flight during
 //     the merge.
-//     RT = 4: on MFMA (v_mfma_f32_16x16x32_f16), the RT rows padded to 16,
+//     RT >= 4: on MFMA (v_mfma_f32_16x16x32_f16), the RT rows padded to 16,
 //     K = the 512 latent channels in 16 steps; lane l holds W~_UV rows
 //     16 wv + (l & 15) at channels 32 ks + 8 (l >> 4) ..; o_z is staged in
 //     LDS as two fp16 parts (hi + lo), each its own product chain, so the
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(256) void upproj_valu_kernel(DecodeArgs a) {
 //     channels 8 l .. 8 l + 7 of the 16 rows and forms RT x 16 eight-term
 //     fp32 partial sums; a butterfly reduce-scatter over the 64 lanes adds
 //     them up (lane l ends with the output l >> (6 - log2(16 RT)) in full).
-constexpr int kFuseR = 512, kFuseDv = 128, kFuseThreads = 512, kFuseMaxRows = 16, kCombU = 16;
+constexpr int kFuseR = 512, kFuseDv = 128, kFuseThreads = 512, kFuseMaxRows = 32, kCombU = 16;
 
 // p[0 .. N) summed over the lanes that differ in bits log2(D) .. log2(D) - log2(N) + 1:
 // at each step a lane keeps one half (the upper one if its bit D is set), adds the
@@ -406,14 +407,16 @@ __device__ __forceinline__ void lane_reduce_scatter(float *p, int lane) {
 
 template <int RT>
 __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs a, int n_rt, int n_logical) {
-  constexpr int S = 4 / RT, CH = kFuseR / 4;
+  // merge threads: S item slices x min(RT, 4) rows x CH chunks; with RT > 4
+  // a thread merges rows j, j + 4, ... in turn
+  constexpr int RJ = RT < 4 ? RT : 4, S = 4 / RJ, RPT = RT / RJ, CH = kFuseR / 4;
   constexpr int V = 16 * RT, LOGV = RT == 1 ? 4 : (RT == 2 ? 5 : 6);
-  constexpr bool kMfma = RT == 4;
+  constexpr bool kMfma = RT >= 4;
   // o_z: fp32 for the vector-ALU product; fp16 hi and lo parts for the
   // MFMA one, rows padded 16 bytes so the 16-lane groups of an operand read
   // (rows 1040 bytes apart) fall on separate banks
   constexpr int ZST = kFuseR + 8;
-  static_assert(S * RT * CH == kFuseThreads, "one (slice, row, chunk) per thread");
+  static_assert(S * RJ * CH == kFuseThreads, "one (slice, row, chunk) per thread and pass");
   __shared__ f32x4 s_o[S][RT][CH];
   __shared__ float s_m[S][RT], s_l[S][RT];
   __shared__ __align__(16) float s_z[kMfma ? 1 : RT][kFuseR];
@@ -437,8 +440,9 @@ __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs
   }
 
   // ---- 1. merge the partials ----
-  {
-    const int c = tid % CH, j = (tid / CH) % RT, sl = tid / (CH * RT);
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int c = tid % CH, j = (tid / CH) % RJ + RJ * rr, sl = tid / (CH * RJ);
     const int q = rt * RT + j;
     float mrun = -INFINITY, lrun = 0.0f;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -482,8 +486,8 @@ __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs
     }
   }
   __syncthreads();
-  if (tid < RT * CH) {
-    const int j = tid / CH, c = tid % CH;
+  for (int u = tid; u < RT * CH; u += kFuseThreads) {
+    const int j = u / CH, c = u % CH;
     float mx = -INFINITY;
 #pragma unroll
     for (int sl = 0; sl < S; ++sl) mx = fmaxf(mx, s_m[sl][j]);
@@ -534,8 +538,7 @@ __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs
     if (j < RT && q < nrows)
       *reinterpret_cast<f32x4 *>(a.out + (static_cast<int64_t>(q) * H + h) * kFuseDv + 16 * wv + 4 * (lane >> 4)) =
           acc_h + acc_l;
-    return;
-  }
+  } else {
   float part[V];
 #pragma unroll
   for (int j = 0; j < RT; ++j) {
@@ -557,6 +560,7 @@ __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs
   const int idx = lane >> (6 - LOGV), j = idx >> 4, q = rt * RT + j;
   if ((lane & ((1 << (6 - LOGV)) - 1)) == 0 && q < nrows)
     a.out[(static_cast<int64_t>(q) * H + h) * kFuseDv + 16 * wv + (idx & 15)] = part[0];
+  }
 }
 
 }  // namespace
@@ -610,11 +614,15 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
     TimedLaunch tl("combine_up_proj", s);
     // the widest row tile that still gives every compute unit a block
     const int nrows = a.B * a.Tq, H = a.d.num_heads, ncu = device_cu_count();
-    int rt = 4;
+    int rt = 16;
     while (rt > 1 && H * ((nrows + rt - 1) / rt) < ncu) rt >>= 1;
     const int n_rt = (nrows + rt - 1) / rt, n_logical = H * n_rt;
     const unsigned grid = static_cast<unsigned>((n_logical + 7) / 8) * 8;
-    if (rt == 4)
+    if (rt == 16)
+      combine_upproj_kernel<16><<<grid, kFuseThreads, 0, s>>>(a, n_rt, n_logical);
+    else if (rt == 8)
+      combine_upproj_kernel<8><<<grid, kFuseThreads, 0, s>>>(a, n_rt, n_logical);
+    else if (rt == 4)
       combine_upproj_kernel<4><<<grid, kFuseThreads, 0, s>>>(a, n_rt, n_logical);
     else if (rt == 2)
       combine_upproj_kernel<2><<<grid, kFuseThreads, 0, s>>>(a, n_rt, n_logical);
