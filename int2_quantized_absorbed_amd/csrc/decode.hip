@@ -440,9 +440,76 @@ __global__ __launch_bounds__(kFuseThreads) void combine_upproj_kernel(DecodeArgs
   }
 
   // ---- 1. merge the partials ----
+  if constexpr (RPT > 1) {
+    // rows j = jb, jb + 4, ... of the tile (S = 1): their loads of a round,
+    // U items per row, are issued together, so rows with at most U items
+    // take one memory round trip.  A row without items (past the batch or
+    // an empty sequence) reads item 0 of a valid row, masked.
+    constexpr int U = kCombU / RPT;
+    const int c = tid % CH, jb = (tid / CH) % RJ;
+    int ib[RPT], ie[RPT];
+    const float *ml[RPT];
+    const f16 *po[RPT];
+    float mrun[RPT], lrun[RPT];
+    f32x4 acc[RPT];
+    int rounds = 0;
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr) {
-    const int c = tid % CH, j = (tid / CH) % RJ + RJ * rr, sl = tid / (CH * RJ);
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int q = rt * RT + jb + RJ * rr;
+      const int m = q < nrows ? (q % a.Tq) * H + h : 0;
+      ib[rr] = q < nrows ? a.item_begin[q / a.Tq] : 0;
+      ie[rr] = q < nrows ? a.item_begin[q / a.Tq + 1] : 0;
+      ml[rr] = a.part_ml + static_cast<int64_t>(m) * 2;
+      po[rr] = reinterpret_cast<const f16 *>(a.part_o) + static_cast<int64_t>(m) * kFuseR + 4 * c;
+      rounds = max(rounds, (ie[rr] - ib[rr] + U - 1) / U);
+      mrun[rr] = -INFINITY;
+      lrun[rr] = 0.0f;
+      acc[rr] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int64_t ml_stride = static_cast<int64_t>(M) * 2, po_stride = static_cast<int64_t>(M) * kFuseR;
+    for (int r = 0; r < rounds; ++r) {
+      f16x4 v[RPT][U];
+      float2 st[RPT][U];
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr)
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+          const int kk = ib[rr] + r * U + e;
+          const int k = ie[rr] > ib[rr] ? min(kk, ie[rr] - 1) : 0;
+          v[rr][e] = *reinterpret_cast<const f16x4 *>(po[rr] + k * po_stride);
+          st[rr][e] = *reinterpret_cast<const float2 *>(ml[rr] + k * ml_stride);
+          if (kk >= ie[rr]) st[rr][e].x = -INFINITY;
+        }
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) {
+        float rm = mrun[rr];
+#pragma unroll
+        for (int e = 0; e < U; ++e) rm = fmaxf(rm, st[rr][e].x);
+        if (rm != -INFINITY) {
+          const float sc = exp2f(mrun[rr] - rm);  // 0 while nothing was folded in
+          acc[rr] *= sc;
+          lrun[rr] *= sc;
+#pragma unroll
+          for (int e = 0; e < U; ++e) {
+            const float wgt = st[rr][e].x == -INFINITY ? 0.0f : exp2f(st[rr][e].x - rm);
+            acc[rr] += (wgt * st[rr][e].y) * __builtin_convertvector(v[rr][e], f32x4);
+            lrun[rr] += wgt * st[rr][e].y;
+          }
+          mrun[rr] = rm;
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int j = jb + RJ * rr;
+      s_o[0][j][c] = acc[rr];
+      if (c == 0) {  // every chunk thread of a row holds the same (max, sum)
+        s_m[0][j] = mrun[rr];
+        s_l[0][j] = lrun[rr];
+      }
+    }
+  } else {
+    const int c = tid % CH, j = (tid / CH) % RJ, sl = tid / (CH * RJ);
     const int q = rt * RT + j;
     float mrun = -INFINITY, lrun = 0.0f;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
