@@ -188,6 +188,8 @@ DECODE_CASES = [
     (128, 32, 2, 32, [900, 77], 2, True),
     (128, 16, 1, 32, [600, 45, 1], 1, True),    # 16 rows per KV head: the 16-row kernel's largest
     (128, 8, 4, 16, [2100, 130], 8, True),      # 2 x 8 drafts = 16 rows, G = 16
+    # 40 sequences x 8 KV heads = 320 pseudo-sequences: the planner's second group
+    (128, 32, 8, 32, [(53 * i) % 200 for i in range(40)], 1, True),
 ]
 
 

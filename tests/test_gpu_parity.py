@@ -230,6 +230,8 @@ DECODE_CASES = [
     ("w1-h2-tq3-mfma", 1, dict(num_heads=2), [300, 45], 3, True, 2),
     ("w1-h16-g16", 1, dict(group_size=16, num_heads=16), [777, 2049], 1, True, 0),
     ("w2-ragged-long", 2, dict(), [2049, 1500, 31, 4000], 1, True, 0),
+    # more than 256 sequences: the device planner's second group of 256
+    ("w1-h4-300-sequences", 1, dict(num_heads=4), [(37 * i) % 90 for i in range(300)], 1, True, 0),
 ]
 
 
