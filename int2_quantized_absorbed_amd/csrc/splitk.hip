@@ -26,11 +26,11 @@ namespace {
 //    w, which it updates with the P Z MFMAs.
 // Producer w and consumer w sit on one SIMD: each runs its MFMAs while the
 // other runs vector-ALU and LDS work.  Per iteration i, two barriers:
-//   X (before A): producer: scores of tile i+1, published as soon as the
-//                 MFMAs are done;
+//   X (before A): producer: Z of tile i+1 to LDS and the scores of tile
+//                 i+1, the stores placed between the MFMAs, the partial
+//                 scores published as soon as their MFMAs are done;
 //                 consumer: softmax and P of tile i.
-//   Y (A to B):   producer: Z of tile i+1 to LDS, dequantise tile i+2,
-//                 request tile i+3;
+//   Y (A to B):   producer: dequantise tile i+2, request tile i+3;
 //                 consumer: rescale and O += P Z for tile i, and the sum of
 //                 the four partial scores of tile i+1.
 // So the exchange of the partial scores overlaps the P Z MFMAs, and the
