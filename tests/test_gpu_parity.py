@@ -230,6 +230,9 @@ DECODE_CASES = [
     ("w1-h2-tq3-mfma", 1, dict(num_heads=2), [300, 45], 3, True, 2),
     ("w1-h16-g16", 1, dict(group_size=16, num_heads=16), [777, 2049], 1, True, 0),
     ("w2-ragged-long", 2, dict(), [2049, 1500, 31, 4000], 1, True, 0),
+    # 12 query rows per head at 128 heads: the merge + up-projection's 8-row
+    # tiles (two per head; 24 rows, w3-tq8-causal, take its 16-row tiles)
+    ("w1-12-sequences", 1, dict(), [65, 1, 400, 33, 0, 129, 1000, 64, 2, 777, 31, 96], 1, True, 0),
     # more than 256 sequences: the device planner's second group of 256
     ("w1-h4-300-sequences", 1, dict(num_heads=4), [(37 * i) % 90 for i in range(300)], 1, True, 0),
 ]
