@@ -21,6 +21,8 @@
 // keeps, per chunk of the sequence, the count of keys above its prefix and
 // the suffix sums of its own last-digit histogram, from which the write pass
 // knows how many tokens every earlier chunk selects without a count pass.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace mla {
@@ -85,11 +87,22 @@ __device__ __forceinline__ void flush_hist(const uint32_t *h, uint32_t *g) {
 // scores[base + t] = q_idx[b] . idx_key[base + t], t < L_b, and radix pass
 // 0 (digit 0 of every key) when the sequence has more than top_k tokens.
 // D = index_head_dim (compile-time, so each lane's key loads are all in
-// flight together).
+// flight together).  A wave's 64 consecutive keys are read with contiguous
+// 16-byte pieces per instruction (lane l takes piece l of each 1 KB) and
+// passed to the lane of their token through the wave's 4 KB LDS buffer, in
+// D / 32 rounds of 2048 / D tokens (piece p of a round's token r stored at
+// slot p ^ (r & 7) of its row, so both sides spread over the banks); a lane
+// then adds its token's products in channel order.
 template <int D>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(IndexArgs a) {
+  constexpr int PT = D / 8;             // 16-byte pieces per key
+  constexpr int NR = D / 32;            // rounds through the buffer
+  constexpr int TPR = 64 / NR;          // tokens per round
+  constexpr int IPR = PT / NR;          // load instructions per round (4)
+  static_assert(NR * TPR == 64 && IPR * 64 == TPR * PT, "a round is 4 KB of whole keys");
   __shared__ float q[D];
   __shared__ uint32_t h[1 << digit_bits(0)];
+  __shared__ uint4 kbuf[kThreads / 64][TPR * PT];
   const int b = blockIdx.x, tid = threadIdx.x;
   for (int e = tid; e < D; e += kThreads) q[e] = bf16_to_f32(a.q_idx[static_cast<int64_t>(b) * D + e]);
   const int L = a.seq_len[b];
@@ -100,21 +113,49 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(IndexArgs a) {
   }
   __syncthreads();
   const int64_t base = a.seq_base[b];
-  for (int t = blockIdx.y * kThreads + tid; t < L; t += gridDim.y * kThreads) {
-    const uint4 *k = reinterpret_cast<const uint4 *>(a.idx_key + (base + t) * D);
-    uint4 raw[D / 8];
+  const int lane = tid & 63;
+  uint4 *kb = kbuf[tid >> 6];
+  // uniform over the wave: its first token t - lane is below L
+  for (int t = blockIdx.y * kThreads + tid; t - lane < L; t += gridDim.y * kThreads) {
+    const int tw = t - lane;  // the wave's first token
+    uint4 piece[PT];  // piece e = 64 i + lane of the wave's keys: token e / PT, piece e % PT
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) raw[i] = k[i];
-    float acc = 0.0f;
+    for (int i = 0; i < PT; ++i) {
+      const int e = i * 64 + lane;
+      piece[i] = reinterpret_cast<const uint4 *>(a.idx_key + (base + min(tw + e / PT, L - 1)) * D)[e % PT];
+    }
+    // Round rd: the round's keys into the buffer, then every lane reads the
+    // round's token lane % TPR and the lanes whose token is in this round keep
+    // it.  A wave's LDS operations run in order, and a lane's stores and
+    // reads of the buffer may alias, so the compiler keeps their order too.
+    uint32_t kw[PT][4];
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    for (int rd = 0; rd < NR; ++rd) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = __builtin_fmaf(__uint_as_float(w[j] << 16), q[8 * i + 2 * j], acc);
-        acc = __builtin_fmaf(__uint_as_float(w[j] & 0xffff0000u), q[8 * i + 2 * j + 1], acc);
+      for (int ii = 0; ii < IPR; ++ii) {
+        const int e = (rd * IPR + ii) * 64 + lane, r = e / PT - rd * TPR, p = e % PT;
+        kb[r * PT + (p ^ (r & 7))] = piece[rd * IPR + ii];
+      }
+      const int r = lane % TPR;
+      const bool keep = rd == 0 || lane / TPR == rd;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const uint4 v = kb[r * PT + (i ^ (r & 7))];
+        kw[i][0] = keep ? v.x : kw[i][0];
+        kw[i][1] = keep ? v.y : kw[i][1];
+        kw[i][2] = keep ? v.z : kw[i][2];
+        kw[i][3] = keep ? v.w : kw[i][3];
       }
     }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = __builtin_fmaf(__uint_as_float(kw[i][j] << 16), q[8 * i + 2 * j], acc);
+        acc = __builtin_fmaf(__uint_as_float(kw[i][j] & 0xffff0000u), q[8 * i + 2 * j + 1], acc);
+      }
+    if (t >= L) continue;
     a.scores[base + t] = acc;
     if (radix) atomicAdd(&h[ordered_bits(acc) >> digit_shift(0)], 1u);
   }
@@ -340,9 +381,13 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   {
     TimedLaunch tl("index_score", s);
     index_clear_kernel<<<dim3(a.B, kPasses), kThreads, 0, s>>>(a);
+    // the score kernel's blocks stride over their sequence: two per compute
+    // unit over the batch measured fastest (more, at its register use, run
+    // in a second round; fewer hold fewer loads in flight)
+    const dim3 score_grid(a.B, std::min(a.n_chunks, std::max(1, 2 * device_cu_count() / std::max(1, a.B))));
     switch (a.d_idx) {
-      case 64: index_score_kernel<64><<<chunks, kThreads, 0, s>>>(a); break;
-      case 128: index_score_kernel<128><<<chunks, kThreads, 0, s>>>(a); break;
+      case 64: index_score_kernel<64><<<score_grid, kThreads, 0, s>>>(a); break;
+      case 128: index_score_kernel<128><<<score_grid, kThreads, 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }
   }
