@@ -27,10 +27,10 @@ pytestmark = pytest.mark.gpu
 D_IDX = 64
 
 
-def _index_case(lens, seed, dup=0, pool=0):
+def _index_case(lens, seed, dup=0, pool=0, d_idx=D_IDX):
     rng = np.random.default_rng(seed)
     base, cap = S.contiguous_layout(lens, 5)
-    keys = S.bf16_normal(rng, (cap, D_IDX))
+    keys = S.bf16_normal(rng, (cap, d_idx))
     if pool:
         keys = keys[rng.integers(0, pool, size=cap)]
     if dup:
@@ -40,7 +40,7 @@ def _index_case(lens, seed, dup=0, pool=0):
             for _ in range(min(dup, L // 2)):
                 i, j = rng.integers(0, L, size=2)
                 keys[a + j] = keys[a + i]
-    q = S.bf16_normal(rng, (len(lens), D_IDX))
+    q = S.bf16_normal(rng, (len(lens), d_idx))
     return base, cap, keys, q
 
 
@@ -77,6 +77,19 @@ def test_index_topk_matches_oracle(name, lens, top_k, dup, pool):
         ref = O.index_topk(O.index_scores(q[b], keys[a:a + L]), top_k)
         assert n_sel[b] == len(ref), (name, b)
         assert np.array_equal(sel[b, :len(ref)], ref), (name, b)
+
+
+@pytest.mark.parametrize("lens,top_k", [([5000, 63, 1, 0, 2100], 2048), ([300, 64, 65], 7)])
+def test_index_topk_128_dim_key(lens, top_k):
+    # a 128-dim indexer key: four staging rounds of 16 tokens per wave
+    C.say(f"index top-k, 128-dim key, lens={lens} top_k={top_k}")
+    base, cap, keys, q = _index_case(lens, 12, 0, 0, d_idx=128)
+    sel, n_sel = _run_topk(_dims(d_idx=128), lens, base, cap, keys, q, top_k)
+    for b, L in enumerate(lens):
+        a = int(base[b])
+        ref = O.index_topk(O.index_scores(q[b], keys[a:a + L]), top_k)
+        assert n_sel[b] == len(ref), b
+        assert np.array_equal(sel[b, :len(ref)], ref), b
 
 
 @pytest.mark.parametrize("variant", [0, 1, 2])
