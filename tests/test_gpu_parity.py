@@ -235,6 +235,7 @@ DECODE_CASES = [
     ("w1-12-sequences", 1, dict(), [65, 1, 400, 33, 0, 129, 1000, 64, 2, 777, 31, 96], 1, True, 0),
     # more than 256 sequences: the device planner's second group of 256
     ("w1-h4-300-sequences", 1, dict(num_heads=4), [(37 * i) % 90 for i in range(300)], 1, True, 0),
+    ("w1-300-sequences", 1, dict(), [(41 * i) % 70 for i in range(300)], 1, True, 0),
 ]
 
 
