@@ -236,6 +236,11 @@ DECODE_CASES = [
     # more than 256 sequences: the device planner's second group of 256
     ("w1-h4-300-sequences", 1, dict(num_heads=4), [(37 * i) % 90 for i in range(300)], 1, True, 0),
     ("w1-300-sequences", 1, dict(), [(41 * i) % 70 for i in range(300)], 1, True, 0),
+    # row counts that leave padding rows in a 64-row block: 48 rows (one
+    # block, its last 16 rows padding) and 96 (two blocks, the second half
+    # padding), causal across the query tokens
+    ("w1-h16-tq3-causal", 1, dict(num_heads=16), [200, 47], 3, True, 0),
+    ("w1-h32-tq3-causal", 1, dict(num_heads=32), [150, 3, 64], 3, True, 0),
 ]
 
 
