@@ -344,8 +344,8 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this path is built and "
-              "measured on one MI355X; sharding over GPUs is not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the decode path runs on a "
+              "single MI355X and does not shard over GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch
