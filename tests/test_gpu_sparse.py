@@ -92,9 +92,12 @@ def test_index_topk_128_dim_key(lens, top_k):
         assert np.array_equal(sel[b, :len(ref)], ref), b
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
-def test_decode_sparse_matches_oracle(variant):
-    w = S.WORKLOADS[4].with_(num_heads=64 if variant == 0 else 16)
+# (decode kernel variant, heads): 64 heads on one 64-row block, 16 heads on
+# the vector-ALU and on the forced MFMA kernel, 128 heads on two row blocks
+# per work item
+@pytest.mark.parametrize("variant,heads", [(0, 64), (1, 16), (2, 16), (0, 128)])
+def test_decode_sparse_matches_oracle(variant, heads):
+    w = S.WORKLOADS[4].with_(num_heads=heads)
     lens = [3000, 700, 0, 2500]
     top_k = 1024
     C.say(f"sparse decode variant {variant} H={w.num_heads} lens={lens} top_k={top_k}")
